@@ -1,0 +1,186 @@
+"""CPU oracle of the fused KDA decode step (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The product path never
+imports this package, and this package imports nothing from the product.
+
+The arithmetic lives in ``kda_oracle.cpp`` (fp32 and fp64 instances of one
+literal, unfused implementation); this module only marshals numpy arrays.
+Every exported function is pinned by the CPU tests (closed forms, special
+cases that reduce to torch library routines, brute force on tiny shapes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("KDA_ORACLE_LIB") or os.path.join(
+    _HERE, "libkda_oracle.so")
+_lib = None
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("conv_width", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("norm_eps", ctypes.c_float)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load the oracle library, building it with g++ if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build
+            _build.build()
+        _lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        for name in ("kda_oracle_decode_f32", "kda_oracle_decode_f64"):
+            f = getattr(_lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.POINTER(_Dims)] + [P] * 11 + [ctypes.c_int]
+        for suf, flt in (("f64", ctypes.c_double), ("f32", ctypes.c_float)):
+            f = getattr(_lib, "kda_oracle_conv_" + suf)
+            f.restype = None
+            f.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_ssize_t,
+                          P, P]
+            f = getattr(_lib, "kda_oracle_recurrence_" + suf)
+            f.restype = None
+            f.argtypes = [ctypes.c_int, P, P, P, P, P, flt, P]
+            f = getattr(_lib, "kda_oracle_gated_norm_" + suf)
+            f.restype = None
+            f.argtypes = [ctypes.c_int, P, P, P, flt, ctypes.c_int, P]
+        for name in ("kda_oracle_bf16_from_f32", "kda_oracle_f32_from_bf16"):
+            f = getattr(_lib, name)
+            f.restype = None
+            f.argtypes = [P, P, ctypes.c_size_t]
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _f(dtype):
+    return np.float64 if dtype == "f64" else np.float32
+
+
+# ---------------------------------------------------------------- bf16 ----
+
+def bf16_from_f32(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    lib().kda_oracle_bf16_from_f32(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def f32_from_bf16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    y = np.empty(x.shape, dtype=np.float32)
+    lib().kda_oracle_f32_from_bf16(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+# -------------------------------------------------------------- stages ----
+
+def conv_stage(x_bits, w, cs_bits, dtype="f64"):
+    """Causal conv update of ``nch`` channels.
+
+    x_bits: uint16 [nch] current inputs; w: float32 [W, nch] taps (tap W-1
+    multiplies the current input); cs_bits: uint16 [nch, W-1] stored inputs,
+    oldest first.  Returns (y [nch], new cs_bits); inputs are not modified.
+    """
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    cs = np.array(cs_bits, dtype=np.uint16, order="C", copy=True)
+    W, nch = w.shape
+    assert x_bits.shape == (nch,) and cs.shape == (nch, W - 1)
+    y = np.empty(nch, dtype=_f(dtype))
+    getattr(lib(), "kda_oracle_conv_" + dtype)(nch, W, _ptr(x_bits), _ptr(w),
+                                               nch, _ptr(cs), _ptr(y))
+    return y, cs
+
+
+def recurrence_stage(S, q, k, v, g, beta, dtype="f64"):
+    """Gated delta-rule step of one unit.  Returns (S' [D, D], o [D])."""
+    F = _f(dtype)
+    S2 = np.array(S, dtype=F, order="C", copy=True)
+    D = S2.shape[0]
+    arrs = [np.ascontiguousarray(a, dtype=F) for a in (q, k, v, g)]
+    for a in arrs:
+        assert a.shape == (D,)
+    o = np.empty(D, dtype=F)
+    getattr(lib(), "kda_oracle_recurrence_" + dtype)(
+        D, _ptr(S2), *[_ptr(a) for a in arrs], float(beta), _ptr(o))
+    return S2, o
+
+
+def gated_norm_stage(o, gate_bits, norm_w, eps, norm=True, dtype="f64"):
+    """Gated RMSNorm of one unit's D outputs (or identity when norm off)."""
+    F = _f(dtype)
+    o = np.ascontiguousarray(o, dtype=F)
+    D = o.shape[0]
+    gate_bits = np.ascontiguousarray(gate_bits, dtype=np.uint16)
+    norm_w = np.ascontiguousarray(norm_w, dtype=np.float32)
+    y = np.empty(D, dtype=F)
+    getattr(lib(), "kda_oracle_gated_norm_" + dtype)(
+        D, _ptr(o), _ptr(gate_bits), _ptr(norm_w), float(eps), int(norm),
+        _ptr(y))
+    return y
+
+
+# ----------------------------------------------------------- full step ----
+
+def decode(inp: dict, *, heads: int, head_dim: int = 128, conv_width: int = 4,
+           norm: bool = True, eps: float = 1e-5, dtype: str = "f32",
+           nthreads: int | None = None, inplace: bool = False) -> dict:
+    """One fused decode call on host arrays (see ``synth`` for layouts).
+
+    Returns a dict with ``out`` (uint16 bf16 bits [B, C]), ``y`` (the output
+    before bf16 rounding), ``conv_state`` and ``rec_state`` after the call.
+    Unless ``inplace`` the input pools are copied first.  ``dtype="f64"``
+    carries the recurrent state in double.
+    """
+    F = _f(dtype)
+    qkv = np.ascontiguousarray(inp["qkv"], dtype=np.uint16)
+    B = qkv.shape[0]
+    C = heads * head_dim
+    assert qkv.shape == (B, 3 * C)
+    cs = inp["conv_state"]
+    rs = inp["rec_state"]
+    if inplace:
+        assert cs.dtype == np.uint16 and cs.flags["C_CONTIGUOUS"]
+        assert rs.dtype == F and rs.flags["C_CONTIGUOUS"]
+    else:
+        cs = np.array(cs, dtype=np.uint16, order="C", copy=True)
+        rs = np.array(rs, dtype=F, order="C", copy=True)
+    S = cs.shape[0]
+    assert cs.shape == (S, 3 * C, conv_width - 1)
+    assert rs.shape == (S, heads, head_dim, head_dim)
+    conv_w = np.ascontiguousarray(inp["conv_w"], dtype=np.float32)
+    g = np.ascontiguousarray(inp["g"], dtype=np.float32)
+    beta = np.ascontiguousarray(inp["beta"], dtype=np.float32)
+    gate = np.ascontiguousarray(inp["gate"], dtype=np.uint16)
+    norm_w = np.ascontiguousarray(inp["norm_w"], dtype=np.float32)
+    idx = np.ascontiguousarray(inp["state_idx"], dtype=np.int32)
+    assert conv_w.shape == (3, conv_width, C)
+    assert g.shape == (B, heads, head_dim) and beta.shape == (B, heads)
+    assert idx.shape == (B,)
+    out = np.empty((B, C), dtype=np.uint16)
+    y = np.empty((B, C), dtype=F)
+    d = _Dims(B, heads, head_dim, conv_width, S, 1 if norm else 0, eps)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    rc = getattr(lib(), "kda_oracle_decode_" + dtype)(
+        ctypes.byref(d), _ptr(qkv), _ptr(conv_w), _ptr(cs), _ptr(rs), _ptr(g),
+        _ptr(beta), _ptr(gate), _ptr(norm_w), _ptr(idx), _ptr(out), _ptr(y),
+        int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (status {rc})")
+    return {"out": out, "y": y, "conv_state": cs, "rec_state": rs}

@@ -1,0 +1,312 @@
+// CPU oracle of the fused single-token KDA decode step.
+//
+// TEST INFRASTRUCTURE ONLY.  This library is the correctness reference for
+// the HIP path.  Only the test suite, the smoke check and the benchmark's
+// CPU-baseline leg may load it; the product path never calls it and shares
+// no source with it (its own bf16 conversion, its own indexing, its own
+// status codes).
+//
+// What it computes.  The page "PR #50654 完整报告 -- [ROCm][Perf] Kimi-K3
+// Fused kernel for KDA decode" (sections "Feature and motivation" and
+// "Implementation breakdown", item 1) describes one decode token per
+// sequence and, for each (sequence, value head), three steps in order:
+// advance the causal conv1d state, run the gated delta-rule recurrence on a
+// [128, 128] fp32 state, apply a gated RMSNorm.  The page gives neither the
+// equations nor eps; the plainest readings used here are:
+//
+//   conv (per channel c, width W, causal cross-correlation):
+//       window = (cs[c][0], ..., cs[c][W-2], x[c])      oldest first
+//       a      = sum_t w[t][c] * window[t]              tap W-1 = current
+//       y[c]   = a * sigmoid(a)                          SiLU, on q, k and v
+//       cs[c]  = window[1..W-1]                          exact bf16 copy
+//     The weight is the width-major fp32 mirror [3, W, C] of a depthwise
+//     Conv1d weight, as the page's conv weight loader builds it ("Key
+//     source excerpts", kda_decode.py).
+//   recurrence (per unit; S[i][j], i = key index, j = value index):
+//       Sd[i][j] = exp(g[i]) * S[i][j]                  per-key-channel decay
+//       u[j]     = sum_i k[i] * Sd[i][j]
+//       delta[j] = beta * (v[j] - u[j])
+//       S'[i][j] = Sd[i][j] + k[i] * delta[j]            written back
+//       o[j]     = sum_i q[i] * S'[i][j]                 readout from S'
+//   gated RMSNorm (norm on; over the D outputs of one head):
+//       r    = 1 / sqrt(sum_j o[j]^2 / D + eps)
+//       y[j] = o[j] * r * norm_w[j] * sigmoid(gate[j])
+//     norm off: y[j] = o[j].  Output is bf16, round-to-nearest-even.
+//   null rows ("Key source excerpts", the kernel's padding-row branch): a
+//     row whose slot is <= 0 writes +0.0 to its outputs and reads or writes
+//     no state.  A slot >= num_slots is treated the same way (memory safety;
+//     not on the page).
+//
+// Every step is written out literally and unfused, sums run in index order
+// with a separate multiply and add (built with -ffp-contract=off), and the
+// whole step exists in fp32 (the page's state precision) and in fp64 (for
+// the oracle's own self-checks).
+//
+// Parity status of each function: see the test suite's pins; all stage
+// functions are pinned (closed forms, special cases reducing to torch
+// library routines, brute force on tiny shapes).
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+enum : int {
+  ORC_OK = 0,
+  ORC_ERR_INVALID_ARG = 1,
+};
+
+// ---- bf16 from its definition: the top 16 bits of an IEEE binary32 ----
+
+float bf16_to_f32(uint16_t h) {
+  uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+// Round-to-nearest-even to 8 significand bits.  NaN stays a quiet NaN.
+uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u)
+    return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> T sigmoid(T x) { return T(1) / (T(1) + std::exp(-x)); }
+
+// ---- stage 1: causal conv update of one channel -------------------------
+// cs: the channel's W-1 stored inputs (bf16 bits, oldest first), updated in
+// place; x: the current input; w: tap t at w[t * wstride].
+template <typename T>
+T conv_channel(int W, uint16_t* cs, uint16_t x, const float* w,
+               std::ptrdiff_t wstride) {
+  T acc = T(0);
+  for (int t = 0; t < W; ++t) {
+    const uint16_t xt = (t < W - 1) ? cs[t] : x;
+    const T prod = T(w[t * wstride]) * T(bf16_to_f32(xt));
+    acc = acc + prod;
+  }
+  for (int t = 0; t + 1 < W - 1; ++t) cs[t] = cs[t + 1];
+  cs[W - 2] = x;
+  return acc * sigmoid(acc);
+}
+
+// ---- stage 2: gated delta-rule recurrence of one unit --------------------
+template <typename T>
+void recurrence(int D, T* S, const T* q, const T* k, const T* v, const T* g,
+                T beta, T* o) {
+  std::vector<T> delta(D);
+  // decay: row i (key channel) scaled by exp(g[i])
+  for (int i = 0; i < D; ++i) {
+    const T a = std::exp(g[i]);
+    for (int j = 0; j < D; ++j) S[i * D + j] = a * S[i * D + j];
+  }
+  // u = Sd^T k, delta = beta * (v - u)
+  for (int j = 0; j < D; ++j) {
+    T u = T(0);
+    for (int i = 0; i < D; ++i) {
+      const T prod = k[i] * S[i * D + j];
+      u = u + prod;
+    }
+    delta[j] = beta * (v[j] - u);
+  }
+  // S' = Sd + k delta^T
+  for (int i = 0; i < D; ++i)
+    for (int j = 0; j < D; ++j) {
+      const T prod = k[i] * delta[j];
+      S[i * D + j] = S[i * D + j] + prod;
+    }
+  // o = S'^T q
+  for (int j = 0; j < D; ++j) {
+    T acc = T(0);
+    for (int i = 0; i < D; ++i) {
+      const T prod = q[i] * S[i * D + j];
+      acc = acc + prod;
+    }
+    o[j] = acc;
+  }
+}
+
+// ---- stage 3: gated RMSNorm of one unit's D outputs ----------------------
+template <typename T>
+void gated_norm(int D, const T* o, const uint16_t* gate, const float* norm_w,
+                T eps, int norm_on, T* y) {
+  if (!norm_on) {
+    for (int j = 0; j < D; ++j) y[j] = o[j];
+    return;
+  }
+  T ss = T(0);
+  for (int j = 0; j < D; ++j) {
+    const T sq = o[j] * o[j];
+    ss = ss + sq;
+  }
+  const T r = T(1) / std::sqrt(ss / T(D) + eps);
+  for (int j = 0; j < D; ++j) {
+    const T gj = sigmoid(T(bf16_to_f32(gate[j])));
+    y[j] = ((o[j] * r) * T(norm_w[j])) * gj;
+  }
+}
+
+struct Dims {
+  int32_t batch, num_heads, head_dim, conv_width, num_slots;
+  uint32_t flags;  // bit 0: output norm on
+  float norm_eps;
+};
+
+// ---- the whole step --------------------------------------------------------
+template <typename T>
+int decode(const Dims* d, const uint16_t* qkv, const float* conv_w,
+           uint16_t* conv_state, T* rec_state, const float* g,
+           const float* beta, const uint16_t* gate, const float* norm_w,
+           const int32_t* state_idx, uint16_t* out, T* y_out, int nthreads) {
+  if (!d) return ORC_ERR_INVALID_ARG;
+  const int64_t B = d->batch, H = d->num_heads, D = d->head_dim,
+                W = d->conv_width, S = d->num_slots;
+  const int norm_on = (d->flags & 1u) ? 1 : 0;
+  if (B < 0 || H < 1 || D < 1 || W < 2 || S < 1) return ORC_ERR_INVALID_ARG;
+  if (norm_on && !(d->norm_eps > 0.0f && std::isfinite(d->norm_eps)))
+    return ORC_ERR_INVALID_ARG;
+  if (B == 0) return ORC_OK;
+  if (!qkv || !conv_w || !conv_state || !rec_state || !g || !beta ||
+      !state_idx || !out || (norm_on && (!gate || !norm_w)))
+    return ORC_ERR_INVALID_ARG;
+  const int64_t C = H * D;
+  const T eps = T(d->norm_eps);
+  const int64_t units = B * H;
+  if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel num_threads(nthreads)
+  {
+    std::vector<T> q(D), k(D), v(D), gg(D), o(D), y(D);
+#pragma omp for schedule(static)
+    for (int64_t unit = 0; unit < units; ++unit) {
+      const int64_t n = unit / H, h = unit % H;
+      const int64_t s = state_idx[n];
+      uint16_t* out_row = out + n * C + h * D;
+      if (s <= 0 || s >= S) {
+        for (int64_t j = 0; j < D; ++j) out_row[j] = 0;
+        if (y_out)
+          for (int64_t j = 0; j < D; ++j) y_out[n * C + h * D + j] = T(0);
+        continue;
+      }
+      // stage 1: q, k, v for this head
+      T* parts[3] = {q.data(), k.data(), v.data()};
+      for (int64_t p = 0; p < 3; ++p)
+        for (int64_t i = 0; i < D; ++i) {
+          const int64_t c = p * C + h * D + i;
+          uint16_t* cs = conv_state + (s * 3 * C + c) * (W - 1);
+          const float* w = conv_w + p * W * C + h * D + i;
+          parts[p][i] = conv_channel<T>(static_cast<int>(W), cs,
+                                        qkv[n * 3 * C + c], w, C);
+        }
+      // stage 2
+      for (int64_t i = 0; i < D; ++i) gg[i] = T(g[(n * H + h) * D + i]);
+      T* Sst = rec_state + (s * H + h) * D * D;
+      recurrence<T>(static_cast<int>(D), Sst, q.data(), k.data(), v.data(),
+                    gg.data(), T(beta[n * H + h]), o.data());
+      // stage 3
+      gated_norm<T>(static_cast<int>(D), o.data(),
+                    norm_on ? gate + n * C + h * D : nullptr, norm_w, eps,
+                    norm_on, y.data());
+      for (int64_t j = 0; j < D; ++j) {
+        out_row[j] = f32_to_bf16(static_cast<float>(y[j]));
+        if (y_out) y_out[n * C + h * D + j] = y[j];
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+}  // namespace
+
+// ---- exported C entry points (host pointers) -------------------------------
+extern "C" {
+
+struct kda_oracle_dims {
+  int32_t batch, num_heads, head_dim, conv_width, num_slots;
+  uint32_t flags;
+  float norm_eps;
+};
+
+// Whole step, fp32 state and arithmetic.  y_out (optional, [B, H*D]) gets
+// the fp32 output before bf16 rounding.  Returns 0 or 1 (invalid argument).
+int kda_oracle_decode_f32(const kda_oracle_dims* d, const uint16_t* qkv,
+                          const float* conv_w, uint16_t* conv_state,
+                          float* rec_state, const float* g, const float* beta,
+                          const uint16_t* gate, const float* norm_w,
+                          const int32_t* state_idx, uint16_t* out,
+                          float* y_out, int nthreads) {
+  return decode<float>(reinterpret_cast<const Dims*>(d), qkv, conv_w,
+                       conv_state, rec_state, g, beta, gate, norm_w, state_idx,
+                       out, y_out, nthreads);
+}
+
+// Whole step, fp64 state and arithmetic (rec_state is a double pool).  The
+// bf16 output rounds through float, so it may differ from a direct
+// double-to-bf16 rounding on exact ties; y_out carries the double values.
+int kda_oracle_decode_f64(const kda_oracle_dims* d, const uint16_t* qkv,
+                          const float* conv_w, uint16_t* conv_state,
+                          double* rec_state, const float* g, const float* beta,
+                          const uint16_t* gate, const float* norm_w,
+                          const int32_t* state_idx, uint16_t* out,
+                          double* y_out, int nthreads) {
+  return decode<double>(reinterpret_cast<const Dims*>(d), qkv, conv_w,
+                        conv_state, rec_state, g, beta, gate, norm_w,
+                        state_idx, out, y_out, nthreads);
+}
+
+// Stage 1 over nch channels: channel c has W-1 stored inputs at
+// cs[c*(W-1) ...], input x[c] and taps w[t*wstride + c].
+void kda_oracle_conv_f64(int nch, int W, const uint16_t* x, const float* w,
+                         std::ptrdiff_t wstride, uint16_t* cs, double* y) {
+  for (int c = 0; c < nch; ++c)
+    y[c] = conv_channel<double>(W, cs + static_cast<std::ptrdiff_t>(c) * (W - 1),
+                                x[c], w + c, wstride);
+}
+void kda_oracle_conv_f32(int nch, int W, const uint16_t* x, const float* w,
+                         std::ptrdiff_t wstride, uint16_t* cs, float* y) {
+  for (int c = 0; c < nch; ++c)
+    y[c] = conv_channel<float>(W, cs + static_cast<std::ptrdiff_t>(c) * (W - 1),
+                               x[c], w + c, wstride);
+}
+
+// Stage 2 on one [D, D] state (updated in place).
+void kda_oracle_recurrence_f64(int D, double* S, const double* q,
+                               const double* k, const double* v,
+                               const double* g, double beta, double* o) {
+  recurrence<double>(D, S, q, k, v, g, beta, o);
+}
+void kda_oracle_recurrence_f32(int D, float* S, const float* q, const float* k,
+                               const float* v, const float* g, float beta,
+                               float* o) {
+  recurrence<float>(D, S, q, k, v, g, beta, o);
+}
+
+// Stage 3 on one unit's D outputs.
+void kda_oracle_gated_norm_f64(int D, const double* o, const uint16_t* gate,
+                               const float* norm_w, double eps, int norm_on,
+                               double* y) {
+  gated_norm<double>(D, o, gate, norm_w, eps, norm_on, y);
+}
+void kda_oracle_gated_norm_f32(int D, const float* o, const uint16_t* gate,
+                               const float* norm_w, float eps, int norm_on,
+                               float* y) {
+  gated_norm<float>(D, o, gate, norm_w, eps, norm_on, y);
+}
+
+// bf16 conversions, element-wise over n values.
+void kda_oracle_bf16_from_f32(const float* x, uint16_t* y, std::size_t n) {
+  for (std::size_t i = 0; i < n; ++i) y[i] = f32_to_bf16(x[i]);
+}
+void kda_oracle_f32_from_bf16(const uint16_t* x, float* y, std::size_t n) {
+  for (std::size_t i = 0; i < n; ++i) y[i] = bf16_to_f32(x[i]);
+}
+
+}  // extern "C"
