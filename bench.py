@@ -1,0 +1,225 @@
+"""Throughput of the fused KDA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one kda_decode call over one batch of the workload (default: the
+batch-256, 48-head call with a 512-slot pool and 32 null padding rows),
+with every input resident in HBM.  The timed region is K calls between two
+device synchronisations; each call is also bracketed by HIP events on the
+stream it runs on, which give the kernel's average launch duration for the
+roofline.  Prints one JSON line.
+
+The metric counts (sequence, head) state updates per second (rows of the
+null slot count zero) and the achieved HBM bandwidth from the algorithmic
+byte model (state read + write, conv state read + write, inputs, outputs)
+against MI355X's 8 TB/s.  The CPU oracle timed on the host cores of the
+same machine is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA decode (seq*head) updates/sec + achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_02_amd", "csrc",
+                          "kda_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                            "kda_decode_b256_h48_traffic.md")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """Counter-measured HBM bytes per launch, if recorded for this exact
+    kernel source and workload (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    wl = re.search(r"workload:\s*(\S+)", text)
+    if not (m and h and wl) or h.group(1) != kernel_hash() or \
+            wl.group(1) != workload:
+        return None
+    return int(m.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b256_h48_pool512_null32")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU-oracle time for the baseline (0: skip)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay measurement")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the decode step has no "
+              f"cross-GPU exchange); --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_decode_02_amd import kda, synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.layers != 1:
+        sys.exit("use a single-layer workload")
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    t = synth.to_torch(inp, dev)
+    out = torch.empty(w.batch, w.channels, dtype=torch.bfloat16, device=dev)
+    idx = inp["state_idx"]
+    live_rows = int(((idx > 0) & (idx < w.num_slots)).sum())
+    units = live_rows * w.heads
+    alg_bytes = kda.decode_bytes(w.batch, w.heads, live_rows, w.norm)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"], t["rec_state"],
+                       t["g"], t["beta"], t["gate"], t["norm_w"],
+                       t["state_idx"], out, norm=w.norm, eps=w.eps,
+                       stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev0[i].record(stream)
+        step()
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+    kern_avg_s = float(np.mean(kern_ms)) * 1e-3
+    ms_per_step = wall / K * 1e3
+    value = units * K / wall
+    achieved = alg_bytes / kern_avg_s / 1e9
+
+    extra = {
+        "kernel_us": {"mean": round(kern_avg_s * 1e6, 2),
+                      "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                      "p50": round(float(np.percentile(kern_ms, 50)) * 1e3, 2),
+                      "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
+        "alg_bytes_per_launch": alg_bytes,
+        "units_per_launch": units,
+        "wall_GBs": round(alg_bytes * K / wall / 1e9, 1),
+    }
+
+    if not args.no_graph:
+        R = max(10, K // 4)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(R):
+                step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gs = e0.elapsed_time(e1) * 1e-3 / R
+        extra["graph"] = {"calls": R, "us_per_call": round(gs * 1e6, 2),
+                          "updates_per_s": units / gs,
+                          "GBs": round(alg_bytes / gs / 1e9, 1)}
+        del g
+
+    traffic = recorded_traffic(w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, alg_bytes, units)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "updates/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+                   "head_dim": w.head_dim, "conv_width": w.conv_width,
+                   "num_slots": w.num_slots, "null_rows": w.batch - live_rows,
+                   "output_norm": w.norm, "io": "bf16 qkv/conv_state/gate/out",
+                   "state": "fp32", "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, inp, seconds, alg_bytes, units):
+    """The CPU oracle (fp32, OpenMP over units) on the same batch, repeated
+    in place until ``seconds`` have passed."""
+    import numpy as np
+
+    import oracle
+
+    cores = min(os.cpu_count() or 1,
+                int(os.environ.get("OMP_NUM_THREADS", "0")) or 16, 16)
+    oracle.lib()
+    work = dict(inp, conv_state=inp["conv_state"].copy(),
+                rec_state=inp["rec_state"].copy())
+    print(f"[bench] cpu oracle on {cores} threads", file=sys.stderr,
+          flush=True)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(work, heads=w.heads, norm=w.norm, eps=w.eps,
+                      dtype="f32", nthreads=cores, inplace=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    del np
+    return {"value": round(units * reps / el, 1), "unit": "updates/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"full {w.name} batch ({units} updates) x {reps} calls "
+                      f"in place, {el:.1f} s, fp32, {model}",
+            "GBs": round(alg_bytes * reps / el / 1e9, 2)}
+
+
+if __name__ == "__main__":
+    main()

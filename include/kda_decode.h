@@ -1,0 +1,128 @@
+/*
+ * kda_decode.h -- C ABI of the fused single-token KDA decode step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one described on the page "PR #50654 完整报告 --
+ * [ROCm][Perf] Kimi-K3 Fused kernel for KDA decode" (prhub.com.cn report of
+ * vLLM PR #50654):
+ *   - section "Feature and motivation": for every sequence and every value
+ *     head of a decode batch, advance the causal conv1d state, run the gated
+ *     delta-rule recurrence, apply a gated RMSNorm -- in one launch instead
+ *     of three;
+ *   - section "Implementation breakdown", item 1: a [128, 128] fp32
+ *     recurrent state per head, read and written once per token; output norm
+ *     on or off; the fixed head counts; rows of the null padding slot 0
+ *     produce zeros and skip the state;
+ *   - section "Implementation breakdown", item 3 and the kda_decode.py
+ *     excerpt in "Key source excerpts": head counts 12/24/48/96, head dim
+ *     128, conv width 4, bf16 input and conv state, a width-major fp32 conv
+ *     weight [3, width, channels] and an fp32 norm weight;
+ *   - the kda.py excerpt in "Key source excerpts": the argument list of the
+ *     fused op (input, conv weight, conv state, gate terms, state indices,
+ *     recurrent state, output, output gate, norm weight, norm eps).
+ *
+ * Per row n (one token) and head h, with D = 128, C = H*D, W = 4:
+ *   conv (each channel c of the head's q, k and v parts):
+ *       a = sum_{t<W} conv_w[p][t][h*D+i] * window[t],
+ *       window = (conv_state[s][c][0..W-2], qkv[n][c]), oldest first;
+ *       x = a * sigmoid(a);  conv_state[s][c] <- window[1..W-1] (bit copy)
+ *   recurrence on S = rec_state[s][h] (S[i][j]: i key, j value):
+ *       Sd[i][j] = exp(g[n][h][i]) * S[i][j]
+ *       delta[j] = beta[n][h] * (v[j] - sum_i k[i] Sd[i][j])
+ *       S'[i][j] = Sd[i][j] + k[i] * delta[j]    (written back to slot s)
+ *       o[j]     = sum_i q[i] S'[i][j]
+ *   output (KDA_OUTPUT_NORM set):
+ *       y[j] = o[j] / sqrt(mean_j o^2 + norm_eps) * norm_w[j]
+ *              * sigmoid(gate[n][h*D+j])
+ *     (flag clear: y = o);  out[n][h*D+j] = bf16_rne(y[j]).
+ *   A row whose slot s = state_idx[n] is <= 0 (null padding slot) or
+ *   >= num_slots writes +0.0 to its output and reads or writes no state.
+ *
+ * g and beta arrive already activated (log-decay <= 0, beta in (0, 1));
+ * the gate activations of the page's op and the conv bias are not part of
+ * this entry point.  q and k are used as produced by the conv (no extra
+ * normalisation or scale).
+ */
+#ifndef KDA_DECODE_H
+#define KDA_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null/negative sizes, null pointer, bad eps/flags */
+  KDA_ERR_UNSUPPORTED = 2, /* head count not in {12,24,48,96}, D != 128, W != 4 */
+  KDA_ERR_MISALIGNED = 3,  /* a buffer pointer not 16-byte aligned           */
+  KDA_ERR_DEVICE = 4,      /* no HIP device, or the current one is not gfx950 */
+  KDA_ERR_LAUNCH = 5       /* the kernel launch reported an error            */
+} kda_status;
+
+/* flags */
+#define KDA_OUTPUT_NORM 0x1u /* apply the gated RMSNorm epilogue */
+
+typedef struct kda_dims {
+  int32_t batch;      /* B >= 0 rows, one decode token each                 */
+  int32_t num_heads;  /* H in {12, 24, 48, 96} value heads on this device  */
+  int32_t head_dim;   /* D = 128 (key dim = value dim)                     */
+  int32_t conv_width; /* W = 4                                             */
+  int32_t num_slots;  /* state pool size >= 1; slot 0 is the null slot     */
+  uint32_t flags;     /* KDA_OUTPUT_NORM or 0                              */
+  float norm_eps;     /* > 0 and finite when KDA_OUTPUT_NORM is set        */
+} kda_dims;
+
+/*
+ * One fused decode step over B rows and H heads, queued on `hip_stream`
+ * (a hipStream_t; NULL = the null stream).  Every pointer is a device
+ * pointer to a contiguous row-major buffer, 16-byte aligned:
+ *
+ *   qkv        in      bf16 [B, 3C]           q | k | v parts, head-major
+ *   conv_w     in      fp32 [3, W, C]         tap W-1 multiplies the token
+ *   conv_state in/out  bf16 [num_slots, 3C, W-1]   oldest tap first
+ *   rec_state  in/out  fp32 [num_slots, H, D, D]   [slot][head][key][value]
+ *   g          in      fp32 [B, H, D]         log-decay per key channel
+ *   beta       in      fp32 [B, H]
+ *   gate       in      bf16 [B, C]            not read when the norm is off
+ *   norm_w     in      fp32 [D]               not read when the norm is off
+ *   state_idx  in      int32 [B]              slot per row
+ *   out        out     bf16 [B, C]            every element written
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing,
+ * keeps no per-call state and does not synchronise, so the call can be
+ * captured into a HIP graph.  conv_state and rec_state change only in the
+ * slots named by non-null rows; all other bytes, slot 0 included, are left
+ * untouched.  Non-null slots must be distinct within one call (two rows on
+ * one slot race; the result is then unspecified).  `out` must not overlap
+ * an input.  The state_idx values are read on the device only.
+ *
+ * Errors: checked on the host before anything is queued, in this order:
+ * INVALID_ARG, UNSUPPORTED, (B = 0 returns KDA_OK with nothing queued),
+ * INVALID_ARG for null pointers, MISALIGNED, DEVICE; LAUNCH if the launch
+ * itself fails.  A non-OK status means nothing was queued (except LAUNCH).
+ * Thread-safe.
+ */
+kda_status kda_decode(const kda_dims* dims, const void* qkv,
+                      const float* conv_w, void* conv_state, float* rec_state,
+                      const float* g, const float* beta, const void* gate,
+                      const float* norm_w, const int32_t* state_idx, void* out,
+                      void* hip_stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Algorithmic HBM bytes one kda_decode call moves, for bandwidth reports:
+ * per non-null (row, head) 2*D*D*4 state bytes, 2*3*D*(W-1)*2 conv-state
+ * bytes, 3*D*2 input, D*4 + 4 gate-term bytes, plus the D*2 output (and D*2
+ * gate when the norm is on); per null (row, head) the D*2 output; plus
+ * state_idx, conv_w and norm_w once.  `live_rows` = rows with a valid slot.
+ * Returns 0 for invalid dims. */
+uint64_t kda_decode_bytes(const kda_dims* dims, int32_t live_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_DECODE_H */

@@ -27,8 +27,11 @@ Buffers (all contiguous, row-major; C = H*D channels per q/k/v part):
 bf16 tensors are returned as numpy uint16 arrays of raw bits.  The float32
 to bf16 rounding of the drawn samples is done by torch's CPU cast.
 
-Draw order per workload (fixed): qkv, conv_w, conv_state (every slot),
-rec_state (every slot), g, beta, gate, norm_w, state_idx.
+Streams and draw order (fixed): the per-call tensors come from
+default_rng([seed, layer, 0]) in the order qkv, conv_w, g, beta, gate,
+norm_w, state_idx; the two state pools come from default_rng([seed, layer,
+1]) in the order conv_state (every slot), rec_state (every slot).  Further
+tokens (make_token) continue the first stream.
 """
 from __future__ import annotations
 
@@ -69,10 +72,8 @@ class Workload:
     def channels(self) -> int:
         return self.heads * self.head_dim
 
-    def units(self, state_idx: np.ndarray | None = None) -> int:
+    def units(self, state_idx: np.ndarray) -> int:
         """Non-null (row, head) pairs: the count of state updates."""
-        if state_idx is None:
-            state_idx = make_state_idx(self, np.random.default_rng(self.seed))
         valid = (state_idx > 0) & (state_idx < self.num_slots)
         return int(valid.sum()) * self.heads
 
@@ -149,25 +150,29 @@ def make_token(w: Workload, rng: np.random.Generator) -> dict:
     return {"qkv": qkv, "g": g, "beta": beta.astype(np.float32), "gate": gate}
 
 
-def make_inputs(w: Workload, layer: int = 0) -> dict:
+def make_inputs(w: Workload, layer: int = 0, pools: bool = True) -> dict:
     """All buffers of one decode call of workload ``w`` (numpy, host).
 
-    For a multi-layer sweep, ``layer`` selects the per-layer seed of the
-    small tensors; the recurrent pool is drawn with the base seed.
+    ``layer`` selects the per-layer streams of a multi-layer sweep.  With
+    ``pools=False`` the state pools are not drawn (None); the other tensors
+    are unchanged.  The returned dict also holds the generator of the
+    per-call stream under "rng" (for further tokens).
     """
-    seed = w.seed if layer == 0 else (w.seed * 1000 + layer)
-    rng = np.random.default_rng(seed)
+    rng = np.random.default_rng([w.seed, layer, 0])
     B, H, D, W, S, C = (w.batch, w.heads, w.head_dim, w.conv_width,
                         w.num_slots, w.channels)
     qkv = to_bf16_bits(_normal(rng, (B, 3 * C)))
     conv_w = _normal(rng, (3, W, C), w.conv_w_sigma)
-    conv_state = to_bf16_bits(_normal(rng, (S, 3 * C, W - 1)))
-    rec_state = _normal(rng, (S, H, D, D), w.rec_sigma)
     g = draw_g(w, rng, (B, H, D))
     beta = (1.0 / (1.0 + np.exp(-_normal(rng, (B, H)).astype(np.float64))))
     gate = to_bf16_bits(_normal(rng, (B, C)))
     norm_w = (1.0 + _normal(rng, (D,), 0.1)).astype(np.float32)
     state_idx = make_state_idx(w, rng)
+    conv_state = rec_state = None
+    if pools:
+        prng = np.random.default_rng([w.seed, layer, 1])
+        conv_state = to_bf16_bits(_normal(prng, (S, 3 * C, W - 1)))
+        rec_state = _normal(prng, (S, H, D, D), w.rec_sigma)
     return {
         "qkv": qkv, "conv_w": conv_w, "conv_state": conv_state,
         "rec_state": rec_state, "g": g, "beta": beta.astype(np.float32),
@@ -181,3 +186,31 @@ def small(name: str, batch: int, heads: int, num_slots: int, seed: int,
     """A test-sized workload with the reference distributions."""
     return Workload(name, batch=batch, heads=heads, num_slots=num_slots,
                     seed=seed, **kw)
+
+
+_BF16_KEYS = ("qkv", "conv_state", "gate")
+
+
+def to_torch(inp: dict, device="cuda") -> dict:
+    """Copy the numpy buffers of ``inp`` to torch tensors on ``device``.
+
+    bf16 buffers (uint16 raw bits) become torch.bfloat16 tensors with the
+    same bits; everything else keeps its dtype.  Non-array entries are
+    dropped.
+    """
+    out = {}
+    for key, a in inp.items():
+        if not isinstance(a, np.ndarray):
+            continue
+        if key in _BF16_KEYS:
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+            t = t.view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a))
+        out[key] = t.to(device)
+    return out
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bits of a bf16 torch tensor as a host uint16 array."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports what include/*.h declares, and rejects
+bad arguments on the host (no device calls: run without a GPU).
+
+Argument checks use fake, never-dereferenced pointer values, so this module
+is skipped whenever a HIP device is visible: a check that wrongly passed
+must never reach a kernel launch.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+from linear_attention_decode_02_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(kda_\w+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    L = ctypes.CDLL(kda.LIB_PATH)
+    names = declared_functions()
+    assert "kda_decode" in names and "kda_status_string" in names
+    for name in names:
+        assert hasattr(L, name), f"{name} declared but not exported"
+
+
+def test_status_strings():
+    for code in range(6):
+        s = kda.status_string(code)
+        assert s and s != "unknown status"
+    assert kda.status_string(99) == "unknown status"
+
+
+def test_byte_model_matches_per_unit_table():
+    # Per (row, head) with a valid slot: 64 KiB state in + out, 3 x 128 x 3
+    # bf16 conv state in + out, 384 bf16 inputs, 128 fp32 log-decays and one
+    # beta, 128 bf16 gate and 128 bf16 outputs; null rows only write output.
+    per_unit = 2 * 65536 + 2 * 2304 + 768 + 512 + 4 + 256 + 256
+    assert per_unit == 137476
+    B, H, live = 256, 48, 224
+    expect = (live * H * per_unit + (B - live) * H * 256 + 4 * B
+              + 3 * 4 * H * 128 * 4 + 128 * 4)
+    assert kda.decode_bytes(B, H, live, norm=True) == expect
+    assert abs(expect / 1e6 - 1478.8) < 0.05
+    assert kda.decode_bytes(512, 96, 512, norm=False) == (
+        512 * 96 * (per_unit - 256) + 4 * 512 + 3 * 4 * 96 * 128 * 4)
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="fake-pointer checks run only without a GPU")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+
+
+def call(dims, ptrs=None):
+    p = [FAKE] * 10 if ptrs is None else ptrs
+    return kda.decode_raw(dims, *p, None)
+
+
+def dims(**kw):
+    base = dict(batch=4, num_heads=12, head_dim=128, conv_width=4,
+                num_slots=8, flags=1, norm_eps=1e-5)
+    base.update(kw)
+    return kda.Dims(**base)
+
+
+@no_gpu
+def test_null_dims_rejected():
+    assert kda.lib().kda_decode(None, *([FAKE] * 10), None) == 1
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), 1), (dict(num_slots=0), 1), (dict(num_heads=0), 1),
+    (dict(flags=2), 1), (dict(norm_eps=0.0), 1),
+    (dict(norm_eps=float("nan")), 1), (dict(norm_eps=float("inf")), 1),
+    (dict(num_heads=16), 2), (dict(num_heads=8), 2), (dict(head_dim=64), 2),
+    (dict(conv_width=3), 2),
+])
+def test_bad_dims(kw, code):
+    assert call(dims(**kw)) == code
+
+
+@no_gpu
+def test_eps_unchecked_when_norm_off_and_batch_zero_is_noop():
+    # batch 0: nothing is queued, pointers are not looked at
+    assert call(dims(batch=0), [None] * 10) == 0
+    # norm off: eps and the gate/norm pointers are not used; the request
+    # then fails only at the device check (no GPU here)
+    p = [FAKE] * 10
+    p[6] = p[7] = None
+    assert call(dims(flags=0, norm_eps=0.0), p) == 4
+
+
+@no_gpu
+@pytest.mark.parametrize("which", range(10))
+def test_null_pointer_rejected(which):
+    p = [FAKE] * 10
+    p[which] = None
+    assert call(dims(), p) == 1
+
+
+@no_gpu
+@pytest.mark.parametrize("which", range(10))
+def test_misaligned_pointer_rejected(which):
+    p = [FAKE] * 10
+    p[which] = FAKE + 4
+    assert call(dims(), p) == 3
+
+
+@no_gpu
+def test_no_device_reported():
+    assert call(dims()) == 4
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kda, "_lib", None)
+    monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        kda.lib()
