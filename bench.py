@@ -67,6 +67,8 @@ def parse():
                     help="minimum CPU-oracle time for the baseline (0: skip)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay measurement")
+    ap.add_argument("--no-copy-probe", action="store_true",
+                    help="skip the plain-copy reference (1 GiB torch copy)")
     return ap.parse_args()
 
 
@@ -97,11 +99,11 @@ def main():
     alg_bytes = kda.decode_bytes(w.batch, w.heads, live_rows, w.norm)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(on=stream):
+        # on=None: torch's current stream (the capture stream in a graph)
         kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"], t["rec_state"],
                        t["g"], t["beta"], t["gate"], t["norm_w"],
-                       t["state_idx"], out, norm=w.norm, eps=w.eps,
-                       stream=stream)
+                       t["state_idx"], out, norm=w.norm, eps=w.eps, stream=on)
 
     for _ in range(args.warmup):
         step()
@@ -139,7 +141,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(R):
-                step()
+                step(None)
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -153,6 +155,9 @@ def main():
                           "updates_per_s": units / gs,
                           "GBs": round(alg_bytes / gs / 1e9, 1)}
         del g
+
+    if not args.no_copy_probe:
+        extra["copy_probe"] = copy_probe(torch, stream)
 
     traffic = recorded_traffic(w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
@@ -180,6 +185,30 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_probe(torch, stream, nbytes=1 << 30, reps=10):
+    """A plain device copy of known size (torch's elementwise copy kernel
+    reading and writing ``nbytes`` each): a measured bandwidth reference
+    on the same GPU, and the calibration launch for the HBM byte counters
+    (its FETCH_SIZE / WRITE_SIZE per dispatch correspond to ``nbytes``)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return {"bytes_read": nbytes, "bytes_written": nbytes,
+            "us_per_copy": round(sec * 1e6, 2),
+            "GBs": round(2 * nbytes / sec / 1e9, 1)}
 
 
 def cpu_baseline(w, inp, seconds, alg_bytes, units):

@@ -10,25 +10,33 @@
 // Design (gfx950, wave64).  The step moves 128 KiB of recurrent state per
 // (row, head) -- the page names that traffic as the bottleneck -- against
 // about 120 kflop, i.e. ~0.9 flop/byte, twenty times below the fp32 ridge:
-// this is HBM-streaming work, so there is no MFMA here.  One 256-thread
-// workgroup owns one (row, head) unit:
-//   * thread t holds a 16-row x 4-column slice of the state in VGPRs:
-//     columns 4*(t%32) .. +3, key rows (t/32) + 8*m, m = 0..15.  Each load
-//     instruction of a wave then covers two adjacent 512-byte rows (1 KiB
-//     contiguous, dwordx4, nontemporal); the whole 64 KiB tile is in flight
-//     at once, issued right after the small conv/gate loads so the conv math
-//     runs under the state latency.
+// this is HBM-streaming work, so there is no MFMA here.  One 1024-thread
+// workgroup (16 waves) owns one (row, head) unit, and at most 64 VGPRs per
+// lane let two such workgroups share a CU (measured on MI355X: 16 waves with
+// two workgroups per CU beat 4 or 8 waves per workgroup, and beat three or
+// four resident workgroups; spreading consecutive units over the XCDs, the
+// hardware's round-robin, beats giving each XCD a contiguous range):
+//   * thread t holds a 4-row x 4-column slice of the state in VGPRs:
+//     columns 4*(t%32) .. +3, key rows (t/32) + 32*m, m = 0..3.  Each load
+//     instruction of a wave covers two adjacent 512-byte rows (1 KiB
+//     contiguous, dwordx4, nontemporal -- worth ~15% over cached loads and
+//     stores); the whole 64 KiB tile is in flight at once, issued right after
+//     the small conv/gate loads so the conv math runs under the state
+//     latency.
 //   * conv (waves 0-2, one q/k/v part each, two channels per lane) and the
 //     decay factors exp(g) (wave 3) go to LDS as {alpha, k, q} per key row.
 //   * column sums u = Sd^T k and p = Sd^T q (and the scalar q.k) are formed
-//     in registers, folded across the two half-waves with one lane swap, and
-//     across the four waves through LDS (one barrier).  The readout uses
-//     o = Sd^T q + (q.k) delta, which equals S'^T q exactly in real
+//     in registers, folded across the two half-waves with one lane swap,
+//     then across waves through LDS: 256 threads each finish one column
+//     (delta_j = beta (v_j - u_j), or p_j) and broadcast it.  The readout
+//     uses o = Sd^T q + (q.k) delta, which equals S'^T q exactly in real
 //     arithmetic, so the updated state is never re-read.
-//   * the RMSNorm sum of squares needs no further barrier: every half-wave
-//     holds all 128 columns.
+//   * the RMSNorm sum of squares needs no further barrier: the first
+//     half-wave holds all 128 columns.
 //   * rows of the null slot (or an out-of-range slot) take a block-uniform
 //     early exit before any barrier and only write zeros.
+//   * HBM traffic per launch, from calibrated FETCH_SIZE / WRITE_SIZE
+//     counters, equals the algorithmic bytes to within 0.1%.
 
 #include <hip/hip_runtime.h>
 
@@ -43,9 +51,11 @@ namespace {
 
 constexpr int kD = 128;          // head dim (key = value)
 constexpr int kW = 4;            // conv width
-constexpr int kThreads = 256;    // 4 waves
-constexpr int kRowsPerThread = kD * kD / (kThreads * 4);  // 16 float4 each
-constexpr int kRowStride = kThreads / 32;                 // 8 key rows apart
+constexpr int kWaves = 16;                                // per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerThread = kD * kD / (kThreads * 4);  // float4 per thread
+constexpr int kRowStride = kThreads / 32;                 // key rows apart
+static_assert(kWaves >= 4 && kD * kD % (kThreads * 4) == 0, "tile shape");
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
@@ -83,11 +93,16 @@ __device__ __forceinline__ float sigmoidf_(float x) {
 }
 
 template <bool kNorm>
-__global__ __launch_bounds__(kThreads) void kda_decode_kernel(Params p) {
+// At most 64 VGPRs, so that two 16-wave workgroups share a CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void kda_decode_kernel(Params p) {
   __shared__ f4 s_akq[kD];          // {exp(g_i), k_i, q_i, 0} per key row i
   __shared__ float s_v[kD];
-  __shared__ f4 s_red[4][32][2];    // per-wave partial u, p for 4 columns
-  __shared__ float s_qk[4];
+  __shared__ float s_red[kWaves][2][kD];  // per-wave partial u, p columns
+  __shared__ float s_qk[kWaves];
+  __shared__ float s_delta[kD];
+  __shared__ float s_p[kD];
+  __shared__ float s_qk_total;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -111,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(Params p) {
   // ---- small loads first (they retire before the state loads) ----------
   // Waves 0..2 run the conv of part `wave` (q, k, v) on channels i0, i0+1;
   // wave 3 computes exp(g) for key rows i0, i0+1.  The loads are issued by
-  // every wave without branching (wave 3 re-reads part 2's conv inputs, an
+  // every wave without branching (waves 3+ re-read part 2's conv inputs, an
   // L2 hit) so that no wave has to drain them before its state loads.
   const int i0 = 2 * lane;
   const int part = wave < 3 ? wave : 2;
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(Params p) {
   }
   if (wave == 2) {
     *reinterpret_cast<f2*>(&s_v[i0]) = f2{y0, y1};
-  } else {
+  } else if (wave < 4) {
     // q -> .z, k -> .y, exp(g) -> .x
     const int comp = wave == 0 ? 2 : (wave == 1 ? 1 : 0);
     float* base = reinterpret_cast<float*>(s_akq);
@@ -199,20 +214,35 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(Params p) {
   }
   qk += __shfl_xor(qk, 32);
   if (lane < 32) {
-    s_red[wave][lane][0] = u;
-    s_red[wave][lane][1] = pq;
+    *reinterpret_cast<f4*>(&s_red[wave][0][4 * col4]) = u;
+    *reinterpret_cast<f4*>(&s_red[wave][1][4 * col4]) = pq;
   }
   if (lane == 0) s_qk[wave] = qk;
   __syncthreads();
-  u = (s_red[0][col4][0] + s_red[1][col4][0]) +
-      (s_red[2][col4][0] + s_red[3][col4][0]);
-  pq = (s_red[0][col4][1] + s_red[1][col4][1]) +
-       (s_red[2][col4][1] + s_red[3][col4][1]);
-  qk = (s_qk[0] + s_qk[1]) + (s_qk[2] + s_qk[3]);
+  // Reduce, then broadcast: threads 0..255 each finish one column of u
+  // (delta_j = beta (v_j - u_j)) or of p, instead of every thread summing
+  // all partials of its four columns.
+  if (tid < 2 * kD) {
+    const int which = tid / kD;
+    const int j = tid % kD;
+    float acc = s_red[0][which][j];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) acc += s_red[w][which][j];
+    if (which == 0)
+      s_delta[j] = beta * (s_v[j] - acc);
+    else
+      s_p[j] = acc;
+    if (tid == 0) {
+      float t = s_qk[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) t += s_qk[w];
+      s_qk_total = t;
+    }
+  }
+  __syncthreads();
 
   // ---- delta rule update, streamed back ------------------------------------
-  const f4 v = *reinterpret_cast<const f4*>(&s_v[4 * col4]);
-  const f4 delta = beta * (v - u);
+  const f4 delta = *reinterpret_cast<const f4*>(&s_delta[4 * col4]);
 #pragma unroll
   for (int m = 0; m < kRowsPerThread; ++m) {
     const float ki = s_akq[rgrp + kRowStride * m].y;
@@ -222,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(Params p) {
 
   // ---- readout and gated RMSNorm (wave 0, lanes 0..31 own the output) -----
   if (tid >= 32) return;
-  const f4 o = pq + qk * delta;
+  const f4 o = *reinterpret_cast<const f4*>(&s_p[4 * col4]) + s_qk_total * delta;
   f4 y = o;
   if (kNorm) {
     float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;

@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_decode_bytes.restype = ctypes.c_uint64
         L.kda_decode_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
+        L.kda_state_stream_probe.restype = ctypes.c_int
+        L.kda_state_stream_probe.argtypes = [P, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_float, P]
         _lib = L
     return _lib
 
@@ -141,3 +144,23 @@ def decode_bytes(batch: int, heads: int, live_rows: int, norm: bool = True) -> i
     d = Dims(batch, heads, HEAD_DIM, CONV_WIDTH, 1,
              KDA_OUTPUT_NORM if norm else 0, 1e-5)
     return int(lib().kda_decode_bytes(ctypes.byref(d), int(live_rows)))
+
+
+def state_stream_probe(tiles: torch.Tensor, waves: int = 8,
+                       scale: float = 1.0, stream=None) -> None:
+    """Read and rewrite (times ``scale``) every [128, 128] fp32 tile of
+    ``tiles`` in place with the decode kernel's access pattern: the
+    bandwidth ceiling of the state stream (include/kda_probe.h)."""
+    _check(tiles, "tiles", torch.float32, tuple(tiles.shape))
+    if tiles.dim() < 2 or tuple(tiles.shape[-2:]) != (HEAD_DIM, HEAD_DIM):
+        raise ValueError("tiles must be [..., 128, 128]")
+    n = tiles.numel() // (HEAD_DIM * HEAD_DIM)
+    if stream is None:
+        stream = torch.cuda.current_stream(tiles.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    with torch.cuda.device(tiles.device):
+        rc = lib().kda_state_stream_probe(tiles.data_ptr(), n, int(waves),
+                                          float(scale), stream)
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))

@@ -130,3 +130,14 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         kda.lib()
+
+
+@no_gpu
+def test_probe_argument_checks():
+    L = kda.lib()
+    assert L.kda_state_stream_probe(None, 4, 8, 1.0, None) == 1
+    assert L.kda_state_stream_probe(FAKE, -1, 8, 1.0, None) == 1
+    assert L.kda_state_stream_probe(FAKE, 4, 5, 1.0, None) == 1
+    assert L.kda_state_stream_probe(FAKE + 4, 4, 8, 1.0, None) == 3
+    assert L.kda_state_stream_probe(FAKE, 0, 8, 1.0, None) == 0
+    assert L.kda_state_stream_probe(FAKE, 4, 8, 1.0, None) == 4

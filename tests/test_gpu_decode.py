@@ -318,3 +318,15 @@ def test_sweep_69_layers_in_one_graph():
         print(f"[sweep] layer {layer}: {st}", flush=True)
     del layers
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("waves", [4, 8, 16])
+def test_state_stream_probe_rewrites_tiles_in_place(waves):
+    x = torch.randn(37, 128, 128, device=DEV)
+    y = x.clone()
+    kda.state_stream_probe(y, waves, scale=2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, 2.0 * x)
+    kda.state_stream_probe(y, waves, scale=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, 2.0 * x)
