@@ -4,7 +4,8 @@
 
 A step is one kda_decode call over one batch of the workload (default: the
 batch-256, 48-head call with a 512-slot pool and 32 null padding rows),
-with every input resident in HBM.  The timed region is K calls between two
+with every input resident in HBM; for the 69-layer sweep workload a step
+is 69 independent single-layer calls, each with its own weights and pools.  The timed region is K calls between two
 device synchronisations; each call is also bracketed by HIP events on the
 stream it runs on, which give the kernel's average launch duration for the
 roofline.  Prints one JSON line.
@@ -86,44 +87,60 @@ def main():
     from linear_attention_decode_02_amd import kda, synth
 
     w = synth.WORKLOADS[args.workload]
-    if w.layers != 1:
-        sys.exit("use a single-layer workload")
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w)
-    t = synth.to_torch(inp, dev)
-    out = torch.empty(w.batch, w.channels, dtype=torch.bfloat16, device=dev)
+    layers = [synth.to_torch(inp, dev)]
+    if w.layers > 1:
+        # independent layers: own weights, inputs and slots; the pools are
+        # copies of layer 0's (values do not change the work done)
+        for layer in range(1, w.layers):
+            t = synth.to_torch(synth.make_inputs(w, layer, pools=False), dev)
+            t["conv_state"] = layers[0]["conv_state"].clone()
+            t["rec_state"] = layers[0]["rec_state"].clone()
+            layers.append(t)
+    for t in layers:
+        t["out"] = torch.empty(w.batch, w.channels, dtype=torch.bfloat16,
+                               device=dev)
     idx = inp["state_idx"]
     live_rows = int(((idx > 0) & (idx < w.num_slots)).sum())
-    units = live_rows * w.heads
+    units = live_rows * w.heads                      # per layer
     alg_bytes = kda.decode_bytes(w.batch, w.heads, live_rows, w.norm)
+    L = len(layers)
     stream = torch.cuda.current_stream(dev)
+
+    def call(t, on):
+        kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"], t["rec_state"],
+                       t["g"], t["beta"], t["gate"], t["norm_w"],
+                       t["state_idx"], t["out"], norm=w.norm, eps=w.eps,
+                       stream=on)
 
     def step(on=stream):
         # on=None: torch's current stream (the capture stream in a graph)
-        kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"], t["rec_state"],
-                       t["g"], t["beta"], t["gate"], t["norm_w"],
-                       t["state_idx"], out, norm=w.norm, eps=w.eps, stream=on)
+        for t in layers:
+            call(t, on)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     K = args.steps
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K * L)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K * L)]
+    print(f"[bench] timing {K} steps of {L} call(s)", file=sys.stderr,
+          flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        ev0[i].record(stream)
-        step()
-        ev1[i].record(stream)
+        for li, t in enumerate(layers):
+            ev0[i * L + li].record(stream)
+            call(t, stream)
+            ev1[i * L + li].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
     kern_avg_s = float(np.mean(kern_ms)) * 1e-3
     ms_per_step = wall / K * 1e3
-    value = units * K / wall
+    value = units * L * K / wall
     achieved = alg_bytes / kern_avg_s / 1e9
 
     extra = {
@@ -133,11 +150,12 @@ def main():
                       "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "alg_bytes_per_launch": alg_bytes,
         "units_per_launch": units,
-        "wall_GBs": round(alg_bytes * K / wall / 1e9, 1),
+        "launches_per_step": L,
+        "wall_GBs": round(alg_bytes * L * K / wall / 1e9, 1),
     }
 
     if not args.no_graph:
-        R = max(10, K // 4)
+        R = max(1, (max(10, K // 4) + L - 1) // L)      # steps per replay
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(R):
@@ -150,10 +168,12 @@ def main():
         g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        gs = e0.elapsed_time(e1) * 1e-3 / R
-        extra["graph"] = {"calls": R, "us_per_call": round(gs * 1e6, 2),
-                          "updates_per_s": units / gs,
-                          "GBs": round(alg_bytes / gs / 1e9, 1)}
+        gstep = e0.elapsed_time(e1) * 1e-3 / R
+        extra["graph"] = {"steps": R, "calls": R * L,
+                          "us_per_step": round(gstep * 1e6, 2),
+                          "us_per_call": round(gstep / L * 1e6, 2),
+                          "updates_per_s": units * L / gstep,
+                          "GBs": round(alg_bytes * L / gstep / 1e9, 1)}
         del g
 
     if not args.no_copy_probe:
@@ -175,7 +195,8 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads,
+        "config": {"workload": w.name, "layers": L, "batch": w.batch,
+                   "heads": w.heads,
                    "head_dim": w.head_dim, "conv_width": w.conv_width,
                    "num_slots": w.num_slots, "null_rows": w.batch - live_rows,
                    "output_norm": w.norm, "io": "bf16 qkv/conv_state/gate/out",
@@ -245,8 +266,9 @@ def cpu_baseline(w, inp, seconds, alg_bytes, units):
     del np
     return {"value": round(units * reps / el, 1), "unit": "updates/s",
             "cores": cores, "kind": "oracle",
-            "sample": f"full {w.name} batch ({units} updates) x {reps} calls "
-                      f"in place, {el:.1f} s, fp32, {model}",
+            "sample": (f"{'one layer of the ' if w.layers > 1 else ''}"
+                       f"full {w.name} batch ({units} updates) x {reps} calls "
+                       f"in place, {el:.1f} s, fp32, {model}"),
             "GBs": round(alg_bytes * reps / el / 1e9, 2)}
 
 

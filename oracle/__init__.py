@@ -22,6 +22,17 @@ _LIB_PATH = os.environ.get("KDA_ORACLE_LIB") or os.path.join(
 _lib = None
 
 
+# flag bits of the extended step (see kda_oracle.cpp)
+NORM, NO_CONV_UPDATE, CONV_TAP_MAJOR, QK_L2NORM, GATE_SILU, BOUNDED_GATE = (
+    0x01, 0x02, 0x04, 0x08, 0x10, 0x20)
+
+
+class _Extras(ctypes.Structure):
+    _fields_ = [("conv_bias", ctypes.c_void_p), ("raw_g", ctypes.c_void_p),
+                ("raw_beta", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float)]
+
+
 class _Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("conv_width", ctypes.c_int32),
@@ -42,17 +53,27 @@ def lib() -> ctypes.CDLL:
             f = getattr(_lib, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(_Dims)] + [P] * 11 + [ctypes.c_int]
+        for name in ("kda_oracle_decode_ext_f32", "kda_oracle_decode_ext_f64"):
+            f = getattr(_lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = ([ctypes.POINTER(_Dims)] + [P] * 11 + [ctypes.c_int]
+                          + [ctypes.POINTER(_Extras)])
+        I, SS = ctypes.c_int, ctypes.c_ssize_t
         for suf, flt in (("f64", ctypes.c_double), ("f32", ctypes.c_float)):
             f = getattr(_lib, "kda_oracle_conv_" + suf)
             f.restype = None
-            f.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_ssize_t,
-                          P, P]
+            f.argtypes = [I, I, P, P, SS, P, SS, SS, P, I, P]
             f = getattr(_lib, "kda_oracle_recurrence_" + suf)
             f.restype = None
-            f.argtypes = [ctypes.c_int, P, P, P, P, P, flt, P]
+            f.argtypes = [I, P, P, P, P, P, flt, P]
             f = getattr(_lib, "kda_oracle_gated_norm_" + suf)
             f.restype = None
-            f.argtypes = [ctypes.c_int, P, P, P, flt, ctypes.c_int, P]
+            f.argtypes = [I, P, P, P, flt, I, I, P]
+        _lib.kda_oracle_l2norm_f64.restype = None
+        _lib.kda_oracle_l2norm_f64.argtypes = [I, P, ctypes.c_double]
+        _lib.kda_oracle_raw_gates_f64.restype = None
+        _lib.kda_oracle_raw_gates_f64.argtypes = [
+            I, P, ctypes.c_float, P, I, ctypes.c_float, ctypes.c_uint16, P, P]
         for name in ("kda_oracle_bf16_from_f32", "kda_oracle_f32_from_bf16"):
             f = getattr(_lib, name)
             f.restype = None
@@ -89,21 +110,31 @@ def f32_from_bf16(x) -> np.ndarray:
 
 # -------------------------------------------------------------- stages ----
 
-def conv_stage(x_bits, w, cs_bits, dtype="f64"):
+def conv_stage(x_bits, w, cs_bits, dtype="f64", bias=None, update=True,
+               tap_major=False):
     """Causal conv update of ``nch`` channels.
 
     x_bits: uint16 [nch] current inputs; w: float32 [W, nch] taps (tap W-1
-    multiplies the current input); cs_bits: uint16 [nch, W-1] stored inputs,
-    oldest first.  Returns (y [nch], new cs_bits); inputs are not modified.
+    multiplies the current input); cs_bits: uint16 stored inputs, oldest
+    first, [nch, W-1] (or [W-1, nch] with ``tap_major``); bias: optional
+    float32 [nch].  Returns (y [nch], new cs_bits); inputs are not modified.
     """
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     w = np.ascontiguousarray(w, dtype=np.float32)
     cs = np.array(cs_bits, dtype=np.uint16, order="C", copy=True)
     W, nch = w.shape
-    assert x_bits.shape == (nch,) and cs.shape == (nch, W - 1)
+    assert x_bits.shape == (nch,)
+    if tap_major:
+        assert cs.shape == (W - 1, nch)
+        chan, tap = 1, nch
+    else:
+        assert cs.shape == (nch, W - 1)
+        chan, tap = W - 1, 1
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     y = np.empty(nch, dtype=_f(dtype))
-    getattr(lib(), "kda_oracle_conv_" + dtype)(nch, W, _ptr(x_bits), _ptr(w),
-                                               nch, _ptr(cs), _ptr(y))
+    getattr(lib(), "kda_oracle_conv_" + dtype)(
+        nch, W, _ptr(x_bits), _ptr(w), nch, _ptr(cs), chan, tap, _ptr(b),
+        int(update), _ptr(y))
     return y, cs
 
 
@@ -121,7 +152,8 @@ def recurrence_stage(S, q, k, v, g, beta, dtype="f64"):
     return S2, o
 
 
-def gated_norm_stage(o, gate_bits, norm_w, eps, norm=True, dtype="f64"):
+def gated_norm_stage(o, gate_bits, norm_w, eps, norm=True, dtype="f64",
+                     gate_silu=False):
     """Gated RMSNorm of one unit's D outputs (or identity when norm off)."""
     F = _f(dtype)
     o = np.ascontiguousarray(o, dtype=F)
@@ -131,21 +163,47 @@ def gated_norm_stage(o, gate_bits, norm_w, eps, norm=True, dtype="f64"):
     y = np.empty(D, dtype=F)
     getattr(lib(), "kda_oracle_gated_norm_" + dtype)(
         D, _ptr(o), _ptr(gate_bits), _ptr(norm_w), float(eps), int(norm),
-        _ptr(y))
+        int(gate_silu), _ptr(y))
     return y
+
+
+def l2norm_stage(x, scale=1.0):
+    """x / sqrt(sum x^2 + 1e-6) * scale (float64)."""
+    x = np.array(x, dtype=np.float64, order="C", copy=True)
+    lib().kda_oracle_l2norm_f64(x.shape[0], _ptr(x), float(scale))
+    return x
+
+
+def raw_gates_stage(raw_g_bits, a_log, dt_bias, raw_beta_bits, bounded=False,
+                    lower_bound=0.0):
+    """Gates of one (row, head) from raw inputs: (g [D], beta) in float64."""
+    raw = np.ascontiguousarray(raw_g_bits, dtype=np.uint16)
+    bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
+    D = raw.shape[0]
+    g = np.empty(D, np.float64)
+    beta = np.empty(1, np.float64)
+    lib().kda_oracle_raw_gates_f64(D, _ptr(raw), float(a_log), _ptr(bias),
+                                   int(bounded), float(lower_bound),
+                                   int(raw_beta_bits), _ptr(g), _ptr(beta))
+    return g, float(beta[0])
 
 
 # ----------------------------------------------------------- full step ----
 
 def decode(inp: dict, *, heads: int, head_dim: int = 128, conv_width: int = 4,
            norm: bool = True, eps: float = 1e-5, dtype: str = "f32",
-           nthreads: int | None = None, inplace: bool = False) -> dict:
+           nthreads: int | None = None, inplace: bool = False,
+           flags: int = 0) -> dict:
     """One fused decode call on host arrays (see ``synth`` for layouts).
 
     Returns a dict with ``out`` (uint16 bf16 bits [B, C]), ``y`` (the output
     before bf16 rounding), ``conv_state`` and ``rec_state`` after the call.
     Unless ``inplace`` the input pools are copied first.  ``dtype="f64"``
-    carries the recurrent state in double.
+    carries the recurrent state in double.  ``flags`` adds variant bits
+    (NO_CONV_UPDATE, CONV_TAP_MAJOR -- conv_state then [S, W-1, 3C] --,
+    QK_L2NORM, GATE_SILU, BOUNDED_GATE); optional ``inp`` entries
+    "conv_bias", and "raw_g"/"raw_beta"/"A_log"/"dt_bias"/"lower_bound"
+    (raw gates: then "g" and "beta" are not read).
     """
     F = _f(dtype)
     qkv = np.ascontiguousarray(inp["qkv"], dtype=np.uint16)
@@ -161,26 +219,49 @@ def decode(inp: dict, *, heads: int, head_dim: int = 128, conv_width: int = 4,
         cs = np.array(cs, dtype=np.uint16, order="C", copy=True)
         rs = np.array(rs, dtype=F, order="C", copy=True)
     S = cs.shape[0]
-    assert cs.shape == (S, 3 * C, conv_width - 1)
+    if flags & CONV_TAP_MAJOR:
+        assert cs.shape == (S, conv_width - 1, 3 * C)
+    else:
+        assert cs.shape == (S, 3 * C, conv_width - 1)
     assert rs.shape == (S, heads, head_dim, head_dim)
     conv_w = np.ascontiguousarray(inp["conv_w"], dtype=np.float32)
-    g = np.ascontiguousarray(inp["g"], dtype=np.float32)
-    beta = np.ascontiguousarray(inp["beta"], dtype=np.float32)
+    raw = inp.get("raw_g") is not None
+    g = None if raw else np.ascontiguousarray(inp["g"], dtype=np.float32)
+    beta = None if raw else np.ascontiguousarray(inp["beta"], dtype=np.float32)
     gate = np.ascontiguousarray(inp["gate"], dtype=np.uint16)
     norm_w = np.ascontiguousarray(inp["norm_w"], dtype=np.float32)
     idx = np.ascontiguousarray(inp["state_idx"], dtype=np.int32)
     assert conv_w.shape == (3, conv_width, C)
-    assert g.shape == (B, heads, head_dim) and beta.shape == (B, heads)
+    if not raw:
+        assert g.shape == (B, heads, head_dim) and beta.shape == (B, heads)
+    keep = []
+
+    def opt(key, dt, shape):
+        a = inp.get(key)
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=dt)
+        assert a.shape == shape, (key, a.shape, shape)
+        keep.append(a)
+        return a.ctypes.data
+
+    ex = _Extras(opt("conv_bias", np.float32, (3 * C,)),
+                 opt("raw_g", np.uint16, (B, heads, head_dim)),
+                 opt("raw_beta", np.uint16, (B, heads)),
+                 opt("A_log", np.float32, (heads,)),
+                 opt("dt_bias", np.float32, (C,)),
+                 float(inp.get("lower_bound", 0.0)))
     assert idx.shape == (B,)
     out = np.empty((B, C), dtype=np.uint16)
     y = np.empty((B, C), dtype=F)
-    d = _Dims(B, heads, head_dim, conv_width, S, 1 if norm else 0, eps)
+    d = _Dims(B, heads, head_dim, conv_width, S,
+              (NORM if norm else 0) | (flags & ~NORM), eps)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
-    rc = getattr(lib(), "kda_oracle_decode_" + dtype)(
+    rc = getattr(lib(), "kda_oracle_decode_ext_" + dtype)(
         ctypes.byref(d), _ptr(qkv), _ptr(conv_w), _ptr(cs), _ptr(rs), _ptr(g),
         _ptr(beta), _ptr(gate), _ptr(norm_w), _ptr(idx), _ptr(out), _ptr(y),
-        int(nthreads))
+        int(nthreads), ctypes.byref(ex))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (status {rc})")
     return {"out": out, "y": y, "conv_state": cs, "rec_state": rs}

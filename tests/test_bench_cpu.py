@@ -1,0 +1,27 @@
+"""bench.py host-side behaviour (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_only_for_matching_kernel_source(monkeypatch):
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "0" * 16)
+    assert bench.recorded_traffic("b256_h48_pool512_null32") is None
+
+
+def test_traffic_record_parses():
+    text = open(bench.TRAFFIC_FILE).read()
+    assert "traffic_bytes_per_launch:" in text
+    assert "kernel_source_sha256_16:" in text

@@ -31,10 +31,10 @@ MUTANTS = {
     "taps_reversed": (
         "const T prod = T(w[t * wstride]) * T(bf16_to_f32(xt));",
         "const T prod = T(w[(W - 1 - t) * wstride]) * T(bf16_to_f32(xt));"),
-    "shift_wrong_end": ("cs[W - 2] = x;", "cs[0] = x;"),
-    "gate_silu": ("const T gj = sigmoid(T(bf16_to_f32(gate[j])));",
-                  "const T gj = T(bf16_to_f32(gate[j])) * "
-                  "sigmoid(T(bf16_to_f32(gate[j])));"),
+    "shift_wrong_end": ("cs[(W - 2) * cs_stride] = x;", "cs[0] = x;"),
+    "gate_activation_swapped": (
+        "const T gj = gate_silu ? gv * sigmoid(gv) : sigmoid(gv);",
+        "const T gj = gate_silu ? sigmoid(gv) : gv * sigmoid(gv);"),
     "norm_sum_not_mean": ("ss / T(D) + eps", "ss + eps"),
     "null_only_negative": ("if (s <= 0 || s >= S) {", "if (s < 0 || s >= S) {"),
     "channel_offset": ("const int64_t c = p * C + h * D + i;",
@@ -46,6 +46,27 @@ MUTANTS = {
     "g_row_head_swap": ("gg[i] = T(g[(n * H + h) * D + i]);",
                         "gg[i] = T(g[(h * B + n) * D + i]);"),
     "bf16_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0u * lsb;"),
+    # variants and extra inputs
+    "l2_eps_outside_sqrt": ("const T r = T(1) / std::sqrt(ss + T(1e-6));",
+                            "const T r = T(1) / (std::sqrt(ss) + T(1e-6));"),
+    "q_scale_inverted": ("T(1) / std::sqrt(T(D)));", "std::sqrt(T(D)));"),
+    "raw_gate_sign": ("return -(a * softplus(z));", "return a * softplus(z);"),
+    "bounded_gate_no_rate": (
+        "if (bounded) return lower_bound * sigmoid(a * z);",
+        "if (bounded) return lower_bound * sigmoid(z);"),
+    "softplus_dropped": ("return x > T(20) ? x : std::log1p(std::exp(x));",
+                         "return x;"),
+    "raw_beta_not_activated": (
+        "beta_nh = sigmoid(T(bf16_to_f32(ex->raw_beta[n * H + h])));",
+        "beta_nh = T(bf16_to_f32(ex->raw_beta[n * H + h]));"),
+    "tap_major_stride": (
+        "const int64_t cs_tap = (fl & F_CONV_TAP_MAJOR) ? 3 * C : 1;",
+        "const int64_t cs_tap = (fl & F_CONV_TAP_MAJOR) ? C : 1;"),
+    "update_flag_ignored": ("const bool update = !(fl & F_NO_CONV_UPDATE);",
+                            "const bool update = true;"),
+    "conv_bias_channel": (
+        "const T bias = conv_bias ? T(conv_bias[c]) : T(0);",
+        "const T bias = conv_bias ? T(conv_bias[c % C]) : T(0);"),
 }
 
 
@@ -64,7 +85,8 @@ def _run_mutant(name, tmp):
     r = subprocess.run(
         [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
          os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-         os.path.join(ROOT, "tests", "test_oracle_step.py")],
+         os.path.join(ROOT, "tests", "test_oracle_step.py"),
+         os.path.join(ROOT, "tests", "test_oracle_variants.py")],
         cwd=ROOT, env=env, capture_output=True, text=True)
     return r.returncode
 
