@@ -38,10 +38,11 @@
  *   A row whose slot s = state_idx[n] is <= 0 (null padding slot) or
  *   >= num_slots writes +0.0 to its output and reads or writes no state.
  *
- * g and beta arrive already activated (log-decay <= 0, beta in (0, 1));
- * the gate activations of the page's op and the conv bias are not part of
- * this entry point.  q and k are used as produced by the conv (no extra
- * normalisation or scale).
+ * kda_decode takes g and beta already activated (log-decay <= 0, beta in
+ * (0, 1)) and no conv bias; kda_decode_raw_gates takes the raw gate inputs
+ * and the bias of the page's op.  By default q and k are used as produced
+ * by the conv (no normalisation, no scale); the flags below select the
+ * variants.
  */
 #ifndef KDA_DECODE_H
 #define KDA_DECODE_H
@@ -61,8 +62,22 @@ typedef enum kda_status {
   KDA_ERR_LAUNCH = 5       /* the kernel launch reported an error            */
 } kda_status;
 
-/* flags */
-#define KDA_OUTPUT_NORM 0x1u /* apply the gated RMSNorm epilogue */
+/* flags (kda_dims.flags).  The page's kernel has template switches for
+ * the output norm, for updating the conv state and for a "safe" gate
+ * ("Implementation breakdown", item 1); the others guard readings of the
+ * page that it leaves open. */
+#define KDA_OUTPUT_NORM 0x01u    /* apply the gated RMSNorm epilogue         */
+#define KDA_NO_CONV_UPDATE 0x02u /* read the conv state, do not write it     */
+#define KDA_CONV_TAP_MAJOR 0x04u /* conv_state stored [num_slots, W-1, 3C]:
+                                    the page's physical layout, of which the
+                                    default [num_slots, 3C, W-1] is the
+                                    transposed view (kda.py excerpt)        */
+#define KDA_QK_L2NORM 0x08u      /* after the conv: q <- q / sqrt(|q|^2 +
+                                    1e-6) * D^-1/2, k <- k / sqrt(|k|^2 +
+                                    1e-6) (not on the page)                  */
+#define KDA_GATE_SILU 0x10u      /* output gate activation x*sigmoid(x)
+                                    instead of sigmoid(x)                    */
+#define KDA_BOUNDED_GATE 0x20u   /* kda_decode_raw_gates only: bounded gate */
 
 typedef struct kda_dims {
   int32_t batch;      /* B >= 0 rows, one decode token each                 */
@@ -70,7 +85,7 @@ typedef struct kda_dims {
   int32_t head_dim;   /* D = 128 (key dim = value dim)                     */
   int32_t conv_width; /* W = 4                                             */
   int32_t num_slots;  /* state pool size >= 1; slot 0 is the null slot     */
-  uint32_t flags;     /* KDA_OUTPUT_NORM or 0                              */
+  uint32_t flags;     /* KDA_* flags above                                 */
   float norm_eps;     /* > 0 and finite when KDA_OUTPUT_NORM is set        */
 } kda_dims;
 
@@ -82,6 +97,7 @@ typedef struct kda_dims {
  *   qkv        in      bf16 [B, 3C]           q | k | v parts, head-major
  *   conv_w     in      fp32 [3, W, C]         tap W-1 multiplies the token
  *   conv_state in/out  bf16 [num_slots, 3C, W-1]   oldest tap first
+ *                      ([num_slots, W-1, 3C] with KDA_CONV_TAP_MAJOR)
  *   rec_state  in/out  fp32 [num_slots, H, D, D]   [slot][head][key][value]
  *   g          in      fp32 [B, H, D]         log-decay per key channel
  *   beta       in      fp32 [B, H]
@@ -99,10 +115,11 @@ typedef struct kda_dims {
  * an input.  The state_idx values are read on the device only.
  *
  * Errors: checked on the host before anything is queued, in this order:
- * INVALID_ARG, UNSUPPORTED, (B = 0 returns KDA_OK with nothing queued),
- * INVALID_ARG for null pointers, MISALIGNED, DEVICE; LAUNCH if the launch
- * itself fails.  A non-OK status means nothing was queued (except LAUNCH).
- * Thread-safe.
+ * INVALID_ARG (dims, eps, unknown flags -- KDA_BOUNDED_GATE is unknown
+ * here), UNSUPPORTED, (B = 0 returns KDA_OK with nothing queued),
+ * INVALID_ARG / MISALIGNED for null or misaligned pointers, DEVICE; LAUNCH
+ * if the launch itself fails.  A non-OK status means nothing was queued
+ * (except LAUNCH).  Thread-safe.
  */
 kda_status kda_decode(const kda_dims* dims, const void* qkv,
                       const float* conv_w, void* conv_state, float* rec_state,
@@ -110,16 +127,52 @@ kda_status kda_decode(const kda_dims* dims, const void* qkv,
                       const float* norm_w, const int32_t* state_idx, void* out,
                       void* hip_stream);
 
+/*
+ * The page's op with its raw gate inputs and conv bias (kda.py excerpt in
+ * "Key source excerpts": raw_g, raw_beta, A_log, dt_bias, lower_bound,
+ * bias).  The page does not give the gate formula; this entry point reads
+ * the names plainly (softplus with a linear branch above 20):
+ *   z = raw_g[n][h][i] + dt_bias[h*D+i],  a = exp(A_log[h])
+ *   g = -a * softplus(z)                       (default)
+ *   g = lower_bound * sigmoid(a * z)           (KDA_BOUNDED_GATE; g in
+ *                                               (lower_bound, 0))
+ *   beta = sigmoid(raw_beta[n][h])
+ *   conv: a_c = conv_bias[c] + sum_t conv_w[..] * window[t]
+ * then the same step as kda_decode.  Extra buffers (device, 16-byte aligned):
+ *   conv_bias  in  fp32 [3C]     may be NULL (no bias)
+ *   raw_g      in  bf16 [B, H, D]
+ *   raw_beta   in  bf16 [B, H]
+ *   A_log      in  fp32 [H]
+ *   dt_bias    in  fp32 [C]
+ * lower_bound must be finite and < 0 when KDA_BOUNDED_GATE is set (else
+ * KDA_ERR_INVALID_ARG); it is ignored otherwise.  Other rules, checks and
+ * status codes as kda_decode.
+ */
+kda_status kda_decode_raw_gates(const kda_dims* dims, const void* qkv,
+                                const float* conv_w, const float* conv_bias,
+                                void* conv_state, float* rec_state,
+                                const void* raw_g, const void* raw_beta,
+                                const float* A_log, const float* dt_bias,
+                                float lower_bound, const void* gate,
+                                const float* norm_w, const int32_t* state_idx,
+                                void* out, void* hip_stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(kda_status status);
 
 /* Algorithmic HBM bytes one kda_decode call moves, for bandwidth reports:
  * per non-null (row, head) 2*D*D*4 state bytes, 2*3*D*(W-1)*2 conv-state
- * bytes, 3*D*2 input, D*4 + 4 gate-term bytes, plus the D*2 output (and D*2
- * gate when the norm is on); per null (row, head) the D*2 output; plus
- * state_idx, conv_w and norm_w once.  `live_rows` = rows with a valid slot.
- * Returns 0 for invalid dims. */
+ * bytes (read only with KDA_NO_CONV_UPDATE: half), 3*D*2 input, D*4 + 4
+ * gate-term bytes, plus the D*2 output (and D*2 gate when the norm is on);
+ * per null (row, head) the D*2 output; plus state_idx, conv_w and norm_w
+ * once.  `live_rows` = rows with a valid slot.  Returns 0 for invalid dims. */
 uint64_t kda_decode_bytes(const kda_dims* dims, int32_t live_rows);
+
+/* The same for kda_decode_raw_gates: gate terms are D*2 + 2 bytes per
+ * (row, head), plus A_log and dt_bias once, plus conv_bias once when
+ * has_conv_bias is nonzero. */
+uint64_t kda_decode_raw_gates_bytes(const kda_dims* dims, int32_t live_rows,
+                                    int32_t has_conv_bias);
 
 #ifdef __cplusplus
 }

@@ -71,6 +71,14 @@ struct Params {
   const float* norm_w;
   const int32_t* state_idx;
   uint16_t* out;
+  // raw gate inputs (kda_decode_raw_gates) and the optional conv bias
+  const float* conv_bias;   // [3C] or null
+  const uint16_t* raw_g;    // bf16 [B, H, D]
+  const uint16_t* raw_beta; // bf16 [B, H]
+  const float* A_log;       // [H]
+  const float* dt_bias;     // [C]
+  float lower_bound;
+  uint32_t flags;
   int32_t heads;
   int32_t num_slots;
   float eps;
@@ -92,7 +100,15 @@ __device__ __forceinline__ float sigmoidf_(float x) {
   return 1.0f / (1.0f + __expf(-x));
 }
 
-template <bool kNorm>
+// softplus with the usual linear branch above 20
+__device__ __forceinline__ float softplusf_(float z) {
+  return z > 20.0f ? z : log1pf(__expf(z));
+}
+
+// kNorm: gated RMSNorm epilogue; kRawGates: g and beta from raw inputs.
+// Other variants (conv-state layout and update, q/k L2 norm, SiLU gate,
+// bounded gate, conv bias) are block-uniform runtime flags.
+template <bool kNorm, bool kRawGates>
 // At most 64 VGPRs, so that two 16-wave workgroups share a CU.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void kda_decode_kernel(Params p) {
@@ -128,23 +144,51 @@ void kda_decode_kernel(Params p) {
   // wave 3 computes exp(g) for key rows i0, i0+1.  The loads are issued by
   // every wave without branching (waves 3+ re-read part 2's conv inputs, an
   // L2 hit) so that no wave has to drain them before its state loads.
+  const uint32_t flags = p.flags;
+  const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
   const int i0 = 2 * lane;
   const int part = wave < 3 ? wave : 2;
   const int64_t c = part * C + h * kD + i0;
   const uint32_t x2 = *reinterpret_cast<const uint32_t*>(p.qkv + n * 3 * C + c);
-  uint32_t* cs_ptr = reinterpret_cast<uint32_t*>(
-      p.conv_state + (static_cast<int64_t>(slot) * 3 * C + c) * (kW - 1));
-  const uint32_t cw0 = cs_ptr[0];
-  const uint32_t cw1 = cs_ptr[1];
-  const uint32_t cw2 = cs_ptr[2];
+  // Conv state words of channels c, c+1.  [slot][channel][tap]: three
+  // consecutive words hold (c t0, c t1 | c t2, c+1 t0 | c+1 t1, c+1 t2);
+  // [slot][tap][channel]: word t holds (c tap t, c+1 tap t), 3C apart.
+  uint32_t* cs_base = reinterpret_cast<uint32_t*>(
+      p.conv_state + static_cast<int64_t>(slot) * 3 * C * (kW - 1) +
+      (tap_major ? c : c * (kW - 1)));
+  const int64_t cs_step = tap_major ? (3 * C) / 2 : 1;  // in words
+  const uint32_t cw0 = cs_base[0];
+  const uint32_t cw1 = cs_base[cs_step];
+  const uint32_t cw2 = cs_base[2 * cs_step];
   f2 w_t[kW];
 #pragma unroll
   for (int t = 0; t < kW; ++t)
     w_t[t] = *reinterpret_cast<const f2*>(p.conv_w + (part * kW + t) * C +
                                           h * kD + i0);
-  const f2 g2 = *reinterpret_cast<const f2*>(
-      p.g + (static_cast<int64_t>(n) * H + h) * kD + i0);
-  const float beta = p.beta[static_cast<int64_t>(n) * H + h];
+  const f2 bias2 = *reinterpret_cast<const f2*>(
+      (p.conv_bias ? p.conv_bias : p.conv_w) + c);
+  f2 g2;
+  float beta;
+  if (kRawGates) {
+    const uint32_t rg = *reinterpret_cast<const uint32_t*>(
+        p.raw_g + (static_cast<int64_t>(n) * H + h) * kD + i0);
+    const f2 db = *reinterpret_cast<const f2*>(p.dt_bias + h * kD + i0);
+    const float a_rate = __expf(p.A_log[h]);
+    const float z0 = bf16_lo(rg) + db.x, z1 = bf16_hi(rg) + db.y;
+    if (flags & KDA_BOUNDED_GATE) {
+      g2.x = p.lower_bound * sigmoidf_(a_rate * z0);
+      g2.y = p.lower_bound * sigmoidf_(a_rate * z1);
+    } else {
+      g2.x = -(a_rate * softplusf_(z0));
+      g2.y = -(a_rate * softplusf_(z1));
+    }
+    const uint32_t rb = p.raw_beta[static_cast<int64_t>(n) * H + h];
+    beta = sigmoidf_(bf16_lo(rb));
+  } else {
+    g2 = *reinterpret_cast<const f2*>(
+        p.g + (static_cast<int64_t>(n) * H + h) * kD + i0);
+    beta = p.beta[static_cast<int64_t>(n) * H + h];
+  }
 
   // ---- issue the whole state tile ----------------------------------------
   // Keep the small loads above ahead of the 16 state loads: the conv math
@@ -162,26 +206,54 @@ void kda_decode_kernel(Params p) {
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- conv update + SiLU, decay factors ---------------------------------
-  // Computed by every wave without branching (loads used unconditionally
-  // stay where they are issued); only the stores depend on the wave.
-  // channel i0 window: lo(cw0), hi(cw0), lo(cw1), token lo(x2)
-  // channel i0+1 window: hi(cw1), lo(cw2), hi(cw2), token hi(x2)
-  float a0 = w_t[0].x * bf16_lo(cw0);
-  a0 += w_t[1].x * bf16_hi(cw0);
-  a0 += w_t[2].x * bf16_lo(cw1);
+  // Computed by every wave without branching on the wave (loads used
+  // unconditionally stay where they are issued); only the stores depend on
+  // the wave.  Window of channel c: (c0, c1, c2, token lo); of c+1:
+  // (d0, d1, d2, token hi), oldest first.
+  float c0, c1, c2, d0, d1, d2;
+  if (tap_major) {
+    c0 = bf16_lo(cw0); c1 = bf16_lo(cw1); c2 = bf16_lo(cw2);
+    d0 = bf16_hi(cw0); d1 = bf16_hi(cw1); d2 = bf16_hi(cw2);
+  } else {
+    c0 = bf16_lo(cw0); c1 = bf16_hi(cw0); c2 = bf16_lo(cw1);
+    d0 = bf16_hi(cw1); d1 = bf16_lo(cw2); d2 = bf16_hi(cw2);
+  }
+  const bool has_bias = p.conv_bias != nullptr;
+  float a0 = has_bias ? bias2.x : 0.0f;
+  a0 += w_t[0].x * c0;
+  a0 += w_t[1].x * c1;
+  a0 += w_t[2].x * c2;
   a0 += w_t[3].x * bf16_lo(x2);
-  float a1 = w_t[0].y * bf16_hi(cw1);
-  a1 += w_t[1].y * bf16_lo(cw2);
-  a1 += w_t[2].y * bf16_hi(cw2);
+  float a1 = has_bias ? bias2.y : 0.0f;
+  a1 += w_t[0].y * d0;
+  a1 += w_t[1].y * d1;
+  a1 += w_t[2].y * d2;
   a1 += w_t[3].y * bf16_hi(x2);
-  const float y0 = wave < 3 ? a0 * sigmoidf_(a0) : __expf(g2.x);
-  const float y1 = wave < 3 ? a1 * sigmoidf_(a1) : __expf(g2.y);
-  if (wave < 3) {
-    // shifted windows, exact bit copies: (cw0.hi, cw1.lo, x.lo) and
-    // (cw2.lo, cw2.hi, x.hi)
-    cs_ptr[0] = (cw0 >> 16) | (cw1 << 16);
-    cs_ptr[1] = (x2 & 0xffffu) | (cw2 << 16);
-    cs_ptr[2] = (cw2 >> 16) | (x2 & 0xffff0000u);
+  float y0 = wave < 3 ? a0 * sigmoidf_(a0) : __expf(g2.x);
+  float y1 = wave < 3 ? a1 * sigmoidf_(a1) : __expf(g2.y);
+  if ((flags & KDA_QK_L2NORM) && wave < 2) {
+    // wave 0 holds all of q, wave 1 all of k: x / sqrt(sum x^2 + 1e-6),
+    // q also scaled by D^-1/2
+    float ss = y0 * y0 + y1 * y1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    const float r = rsqrtf(ss + 1e-6f) * (wave == 0 ? 0.08838834764831845f
+                                                     : 1.0f);
+    y0 *= r;
+    y1 *= r;
+  }
+  if (wave < 3 && !(flags & KDA_NO_CONV_UPDATE)) {
+    // shifted windows, exact bit copies
+    if (tap_major) {
+      cs_base[0] = cw1;
+      cs_base[cs_step] = cw2;
+      cs_base[2 * cs_step] = x2;
+    } else {
+      // (cw0.hi, cw1.lo, x.lo) and (cw2.lo, cw2.hi, x.hi)
+      cs_base[0] = (cw0 >> 16) | (cw1 << 16);
+      cs_base[1] = (x2 & 0xffffu) | (cw2 << 16);
+      cs_base[2] = (cw2 >> 16) | (x2 & 0xffff0000u);
+    }
   }
   if (wave == 2) {
     *reinterpret_cast<f2*>(&s_v[i0]) = f2{y0, y1};
@@ -262,10 +334,10 @@ void kda_decode_kernel(Params p) {
     const f4 w = *reinterpret_cast<const f4*>(p.norm_w + 4 * col4);
     const uint2 gb = *reinterpret_cast<const uint2*>(
         p.gate + static_cast<int64_t>(n) * C + h * kD + 4 * col4);
-    y.x = o.x * r * w.x * sigmoidf_(bf16_lo(gb.x));
-    y.y = o.y * r * w.y * sigmoidf_(bf16_hi(gb.x));
-    y.z = o.z * r * w.z * sigmoidf_(bf16_lo(gb.y));
-    y.w = o.w * r * w.w * sigmoidf_(bf16_hi(gb.y));
+    f4 gv = {bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
+    f4 ga = {sigmoidf_(gv.x), sigmoidf_(gv.y), sigmoidf_(gv.z), sigmoidf_(gv.w)};
+    if (flags & KDA_GATE_SILU) ga *= gv;
+    y = o * r * w * ga;
   }
   uint2 ob;
   ob.x = pack_bf16x2(y.x, y.y);
@@ -296,10 +368,14 @@ bool aligned16(const void* ptr) {
 
 bool supported_heads(int h) { return h == 12 || h == 24 || h == 48 || h == 96; }
 
-kda_status check_dims(const kda_dims* d) {
+constexpr uint32_t kPlainFlags = KDA_OUTPUT_NORM | KDA_NO_CONV_UPDATE |
+                                 KDA_CONV_TAP_MAJOR | KDA_QK_L2NORM |
+                                 KDA_GATE_SILU;
+
+kda_status check_dims(const kda_dims* d, uint32_t allowed_flags) {
   if (!d) return KDA_ERR_INVALID_ARG;
   if (d->batch < 0 || d->num_heads < 1 || d->head_dim < 1 ||
-      d->conv_width < 2 || d->num_slots < 1 || (d->flags & ~KDA_OUTPUT_NORM))
+      d->conv_width < 2 || d->num_slots < 1 || (d->flags & ~allowed_flags))
     return KDA_ERR_INVALID_ARG;
   if ((d->flags & KDA_OUTPUT_NORM) &&
       !(std::isfinite(d->norm_eps) && d->norm_eps > 0.0f))
@@ -312,6 +388,78 @@ kda_status check_dims(const kda_dims* d) {
   return KDA_OK;
 }
 
+// Pointer checks shared by both entry points (after the dims checks).
+kda_status check_common(const kda_dims* d, const void* qkv, const void* conv_w,
+                        const void* conv_state, const void* rec_state,
+                        const void* gate, const void* norm_w,
+                        const void* state_idx, const void* out) {
+  const bool norm = (d->flags & KDA_OUTPUT_NORM) != 0;
+  if (!qkv || !conv_w || !conv_state || !rec_state || !state_idx || !out ||
+      (norm && (!gate || !norm_w)))
+    return KDA_ERR_INVALID_ARG;
+  if (!aligned16(qkv) || !aligned16(conv_w) || !aligned16(conv_state) ||
+      !aligned16(rec_state) || !aligned16(state_idx) || !aligned16(out) ||
+      (norm && (!aligned16(gate) || !aligned16(norm_w))))
+    return KDA_ERR_MISALIGNED;
+  return KDA_OK;
+}
+
+Params base_params(const kda_dims* d, const void* qkv, const float* conv_w,
+                   void* conv_state, float* rec_state, const void* gate,
+                   const float* norm_w, const int32_t* state_idx, void* out) {
+  Params p{};
+  p.qkv = static_cast<const uint16_t*>(qkv);
+  p.conv_w = conv_w;
+  p.conv_state = static_cast<uint16_t*>(conv_state);
+  p.rec_state = rec_state;
+  p.gate = static_cast<const uint16_t*>(gate);
+  p.norm_w = norm_w;
+  p.state_idx = state_idx;
+  p.out = static_cast<uint16_t*>(out);
+  p.flags = d->flags;
+  p.heads = d->num_heads;
+  p.num_slots = d->num_slots;
+  p.eps = d->norm_eps;
+  return p;
+}
+
+template <bool kRaw>
+kda_status launch(const kda_dims* d, const Params& p, void* hip_stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return KDA_ERR_DEVICE;
+  const dim3 grid(static_cast<unsigned>(d->batch * d->num_heads));
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (d->flags & KDA_OUTPUT_NORM)
+    hipLaunchKernelGGL((kda_decode_kernel<true, kRaw>), grid, dim3(kThreads),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((kda_decode_kernel<false, kRaw>), grid, dim3(kThreads),
+                       0, stream, p);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+uint64_t bytes_model(const kda_dims* d, int32_t live_rows, bool raw_gates,
+                     bool conv_bias) {
+  if (!d || d->batch < 0 || d->num_heads < 1 || d->head_dim < 1 ||
+      d->conv_width < 2 || live_rows < 0 || live_rows > d->batch)
+    return 0;
+  const uint64_t H = d->num_heads, D = d->head_dim, W = d->conv_width;
+  const bool norm = (d->flags & KDA_OUTPUT_NORM) != 0;
+  const bool conv_write = (d->flags & KDA_NO_CONV_UPDATE) == 0;
+  const uint64_t conv_state = 3 * D * (W - 1) * 2;
+  const uint64_t gates = raw_gates ? D * 2 + 2 : D * 4 + 4;
+  const uint64_t per_unit = 2 * D * D * 4 + conv_state * (conv_write ? 2 : 1) +
+                            3 * D * 2 + gates + D * 2 + (norm ? D * 2 : 0);
+  const uint64_t live = static_cast<uint64_t>(live_rows) * H;
+  const uint64_t null_units =
+      static_cast<uint64_t>(d->batch - live_rows) * H;
+  return live * per_unit + null_units * D * 2 +
+         static_cast<uint64_t>(d->batch) * 4 + 3 * W * H * D * 4 +
+         (norm ? D * 4 : 0) + (raw_gates ? H * 4 + H * D * 4 : 0) +
+         (conv_bias ? 3 * H * D * 4 : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,45 +468,51 @@ kda_status kda_decode(const kda_dims* d, const void* qkv, const float* conv_w,
                       void* conv_state, float* rec_state, const float* g,
                       const float* beta, const void* gate, const float* norm_w,
                       const int32_t* state_idx, void* out, void* hip_stream) {
-  const kda_status st = check_dims(d);
+  kda_status st = check_dims(d, kPlainFlags);
   if (st != KDA_OK) return st;
   if (d->batch == 0) return KDA_OK;
-  const bool norm = (d->flags & KDA_OUTPUT_NORM) != 0;
-  if (!qkv || !conv_w || !conv_state || !rec_state || !g || !beta ||
-      !state_idx || !out || (norm && (!gate || !norm_w)))
-    return KDA_ERR_INVALID_ARG;
-  if (!aligned16(qkv) || !aligned16(conv_w) || !aligned16(conv_state) ||
-      !aligned16(rec_state) || !aligned16(g) || !aligned16(beta) ||
-      !aligned16(state_idx) || !aligned16(out) ||
-      (norm && (!aligned16(gate) || !aligned16(norm_w))))
-    return KDA_ERR_MISALIGNED;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
-    return KDA_ERR_DEVICE;
-
-  Params p;
-  p.qkv = static_cast<const uint16_t*>(qkv);
-  p.conv_w = conv_w;
-  p.conv_state = static_cast<uint16_t*>(conv_state);
-  p.rec_state = rec_state;
+  st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                    state_idx, out);
+  if (st != KDA_OK) return st;
+  if (!g || !beta) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(g) || !aligned16(beta)) return KDA_ERR_MISALIGNED;
+  Params p = base_params(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                         state_idx, out);
   p.g = g;
   p.beta = beta;
-  p.gate = static_cast<const uint16_t*>(gate);
-  p.norm_w = norm_w;
-  p.state_idx = state_idx;
-  p.out = static_cast<uint16_t*>(out);
-  p.heads = d->num_heads;
-  p.num_slots = d->num_slots;
-  p.eps = d->norm_eps;
-  const dim3 grid(static_cast<unsigned>(d->batch * d->num_heads));
-  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (norm)
-    hipLaunchKernelGGL(kda_decode_kernel<true>, grid, dim3(kThreads), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL(kda_decode_kernel<false>, grid, dim3(kThreads), 0,
-                       stream, p);
-  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  return launch<false>(d, p, hip_stream);
+}
+
+kda_status kda_decode_raw_gates(const kda_dims* d, const void* qkv,
+                                const float* conv_w, const float* conv_bias,
+                                void* conv_state, float* rec_state,
+                                const void* raw_g, const void* raw_beta,
+                                const float* A_log, const float* dt_bias,
+                                float lower_bound, const void* gate,
+                                const float* norm_w, const int32_t* state_idx,
+                                void* out, void* hip_stream) {
+  kda_status st = check_dims(d, kPlainFlags | KDA_BOUNDED_GATE);
+  if (st != KDA_OK) return st;
+  if ((d->flags & KDA_BOUNDED_GATE) &&
+      !(std::isfinite(lower_bound) && lower_bound < 0.0f))
+    return KDA_ERR_INVALID_ARG;
+  if (d->batch == 0) return KDA_OK;
+  st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                    state_idx, out);
+  if (st != KDA_OK) return st;
+  if (!raw_g || !raw_beta || !A_log || !dt_bias) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(raw_g) || !aligned16(raw_beta) || !aligned16(A_log) ||
+      !aligned16(dt_bias) || (conv_bias && !aligned16(conv_bias)))
+    return KDA_ERR_MISALIGNED;
+  Params p = base_params(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                         state_idx, out);
+  p.conv_bias = conv_bias;
+  p.raw_g = static_cast<const uint16_t*>(raw_g);
+  p.raw_beta = static_cast<const uint16_t*>(raw_beta);
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.lower_bound = lower_bound;
+  return launch<true>(d, p, hip_stream);
 }
 
 const char* kda_status_string(kda_status s) {
@@ -374,19 +528,12 @@ const char* kda_status_string(kda_status s) {
 }
 
 uint64_t kda_decode_bytes(const kda_dims* d, int32_t live_rows) {
-  if (!d || d->batch < 0 || d->num_heads < 1 || d->head_dim < 1 ||
-      d->conv_width < 2 || live_rows < 0 || live_rows > d->batch)
-    return 0;
-  const uint64_t H = d->num_heads, D = d->head_dim, W = d->conv_width;
-  const bool norm = (d->flags & KDA_OUTPUT_NORM) != 0;
-  const uint64_t per_unit = 2 * D * D * 4 + 2 * 3 * D * (W - 1) * 2 +
-                            3 * D * 2 + D * 4 + 4 + D * 2 + (norm ? D * 2 : 0);
-  const uint64_t live = static_cast<uint64_t>(live_rows) * H;
-  const uint64_t null_units =
-      static_cast<uint64_t>(d->batch - live_rows) * H;
-  return live * per_unit + null_units * D * 2 +
-         static_cast<uint64_t>(d->batch) * 4 + 3 * W * H * D * 4 +
-         (norm ? D * 4 : 0);
+  return bytes_model(d, live_rows, false, false);
+}
+
+uint64_t kda_decode_raw_gates_bytes(const kda_dims* d, int32_t live_rows,
+                                    int32_t has_conv_bias) {
+  return bytes_model(d, live_rows, true, has_conv_bias != 0);
 }
 
 }  // extern "C"

@@ -18,7 +18,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda_decode.so")
 
 KDA_OK = 0
-KDA_OUTPUT_NORM = 0x1
+KDA_OUTPUT_NORM = 0x01
+KDA_NO_CONV_UPDATE = 0x02
+KDA_CONV_TAP_MAJOR = 0x04
+KDA_QK_L2NORM = 0x08
+KDA_GATE_SILU = 0x10
+KDA_BOUNDED_GATE = 0x20
 HEAD_DIM = 128
 CONV_WIDTH = 4
 
@@ -56,8 +61,14 @@ def lib() -> ctypes.CDLL:
         L.kda_decode.argtypes = [ctypes.POINTER(Dims)] + [P] * 11
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_decode_raw_gates.restype = ctypes.c_int
+        L.kda_decode_raw_gates.argtypes = (
+            [ctypes.POINTER(Dims)] + [P] * 9 + [ctypes.c_float] + [P] * 5)
         L.kda_decode_bytes.restype = ctypes.c_uint64
         L.kda_decode_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
+        L.kda_decode_raw_gates_bytes.restype = ctypes.c_uint64
+        L.kda_decode_raw_gates_bytes.argtypes = [ctypes.POINTER(Dims),
+                                                 ctypes.c_int32, ctypes.c_int32]
         L.kda_state_stream_probe.restype = ctypes.c_int
         L.kda_state_stream_probe.argtypes = [P, ctypes.c_int64, ctypes.c_int32,
                                              ctypes.c_float, P]
@@ -91,18 +102,20 @@ def _check(t: torch.Tensor, name: str, dtype, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
-def kda_decode(qkv, conv_w, conv_state, rec_state, g, beta, gate, norm_w,
-               state_idx, out, *, norm: bool = True, eps: float = 1e-5,
-               stream=None) -> None:
-    """One fused KDA decode step (in place on ``conv_state``/``rec_state``).
+def _stream(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
 
-    qkv bf16 [B, 3C]; conv_w fp32 [3, 4, C]; conv_state bf16 [S, 3C, 3];
-    rec_state fp32 [S, H, 128, 128]; g fp32 [B, H, 128]; beta fp32 [B, H];
-    gate bf16 [B, C]; norm_w fp32 [128]; state_idx int32 [B]; out bf16
-    [B, C]; C = 128 H.  ``gate``/``norm_w`` may be None when ``norm`` is
-    False.  Queued on ``stream`` (a torch.cuda.Stream, a raw handle, or
-    None for torch's current stream); nothing is synchronised.
-    """
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _common(qkv, conv_w, conv_state, rec_state, gate, norm_w, state_idx, out,
+            norm, variants):
     if rec_state.dim() != 4:
         raise ValueError("rec_state must be [num_slots, H, 128, 128]")
     S, H, D, D2 = rec_state.shape
@@ -111,38 +124,93 @@ def kda_decode(qkv, conv_w, conv_state, rec_state, g, beta, gate, norm_w,
     _check(rec_state, "rec_state", torch.float32, (S, H, D, D2))
     _check(qkv, "qkv", torch.bfloat16, (B, 3 * C))
     _check(conv_w, "conv_w", torch.float32, (3, CONV_WIDTH, C))
-    _check(conv_state, "conv_state", torch.bfloat16, (S, 3 * C, CONV_WIDTH - 1))
-    _check(g, "g", torch.float32, (B, H, D))
-    _check(beta, "beta", torch.float32, (B, H))
+    cs_shape = ((S, CONV_WIDTH - 1, 3 * C) if variants & KDA_CONV_TAP_MAJOR
+                else (S, 3 * C, CONV_WIDTH - 1))
+    _check(conv_state, "conv_state", torch.bfloat16, cs_shape)
     _check(state_idx, "state_idx", torch.int32, (B,))
     _check(out, "out", torch.bfloat16, (B, C))
     if norm:
         _check(gate, "gate", torch.bfloat16, (B, C))
         _check(norm_w, "norm_w", torch.float32, (D,))
-    if stream is None:
-        stream = torch.cuda.current_stream(qkv.device).cuda_stream
-    elif isinstance(stream, torch.cuda.Stream):
-        stream = stream.cuda_stream
-    dims = Dims(B, H, D, CONV_WIDTH, S, KDA_OUTPUT_NORM if norm else 0,
-                float(eps))
+    return B, H, D, S
 
-    def ptr(t):
-        return None if t is None else t.data_ptr()
 
+def kda_decode(qkv, conv_w, conv_state, rec_state, g, beta, gate, norm_w,
+               state_idx, out, *, norm: bool = True, eps: float = 1e-5,
+               variants: int = 0, stream=None) -> None:
+    """One fused KDA decode step (in place on ``conv_state``/``rec_state``).
+
+    qkv bf16 [B, 3C]; conv_w fp32 [3, 4, C]; conv_state bf16 [S, 3C, 3]
+    ([S, 3, 3C] with KDA_CONV_TAP_MAJOR); rec_state fp32 [S, H, 128, 128];
+    g fp32 [B, H, 128]; beta fp32 [B, H]; gate bf16 [B, C]; norm_w fp32
+    [128]; state_idx int32 [B]; out bf16 [B, C]; C = 128 H.  ``gate`` and
+    ``norm_w`` may be None when ``norm`` is False.  ``variants``: OR of
+    KDA_NO_CONV_UPDATE, KDA_CONV_TAP_MAJOR, KDA_QK_L2NORM, KDA_GATE_SILU.
+    Queued on ``stream`` (a torch.cuda.Stream, a raw handle, or None for
+    torch's current stream); nothing is synchronised.
+    """
+    B, H, D, S = _common(qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                         state_idx, out, norm, variants)
+    _check(g, "g", torch.float32, (B, H, D))
+    _check(beta, "beta", torch.float32, (B, H))
+    dims = Dims(B, H, D, CONV_WIDTH, S,
+                (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
     with torch.cuda.device(qkv.device):
-        rc = decode_raw(dims, ptr(qkv), ptr(conv_w), ptr(conv_state),
-                        ptr(rec_state), ptr(g), ptr(beta),
-                        ptr(gate) if norm else None,
-                        ptr(norm_w) if norm else None, ptr(state_idx),
-                        ptr(out), stream)
+        rc = decode_raw(dims, _ptr(qkv), _ptr(conv_w), _ptr(conv_state),
+                        _ptr(rec_state), _ptr(g), _ptr(beta),
+                        _ptr(gate) if norm else None,
+                        _ptr(norm_w) if norm else None, _ptr(state_idx),
+                        _ptr(out), _stream(stream, qkv.device))
     if rc != KDA_OK:
         raise KdaError(rc, status_string(rc))
 
 
-def decode_bytes(batch: int, heads: int, live_rows: int, norm: bool = True) -> int:
+def kda_decode_raw_gates(qkv, conv_w, conv_bias, conv_state, rec_state, raw_g,
+                         raw_beta, A_log, dt_bias, gate, norm_w, state_idx,
+                         out, *, norm: bool = True, eps: float = 1e-5,
+                         lower_bound: float | None = None, variants: int = 0,
+                         stream=None) -> None:
+    """The fused step with raw gate inputs and an optional conv bias.
+
+    raw_g bf16 [B, H, 128]; raw_beta bf16 [B, H]; A_log fp32 [H]; dt_bias
+    fp32 [C]; conv_bias fp32 [3C] or None.  ``lower_bound`` (< 0) selects
+    the bounded gate.  Other arguments as ``kda_decode``.
+    """
+    B, H, D, S = _common(qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                         state_idx, out, norm, variants)
+    C = H * D
+    _check(raw_g, "raw_g", torch.bfloat16, (B, H, D))
+    _check(raw_beta, "raw_beta", torch.bfloat16, (B, H))
+    _check(A_log, "A_log", torch.float32, (H,))
+    _check(dt_bias, "dt_bias", torch.float32, (C,))
+    if conv_bias is not None:
+        _check(conv_bias, "conv_bias", torch.float32, (3 * C,))
+    flags = (KDA_OUTPUT_NORM if norm else 0) | int(variants)
+    if lower_bound is not None:
+        flags |= KDA_BOUNDED_GATE
+    dims = Dims(B, H, D, CONV_WIDTH, S, flags, float(eps))
+    with torch.cuda.device(qkv.device):
+        rc = lib().kda_decode_raw_gates(
+            ctypes.byref(dims), _ptr(qkv), _ptr(conv_w), _ptr(conv_bias),
+            _ptr(conv_state), _ptr(rec_state), _ptr(raw_g), _ptr(raw_beta),
+            _ptr(A_log), _ptr(dt_bias),
+            float(lower_bound if lower_bound is not None else 0.0),
+            _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
+            _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+
+
+def decode_bytes(batch: int, heads: int, live_rows: int, norm: bool = True,
+                 variants: int = 0, raw_gates: bool = False,
+                 conv_bias: bool = False) -> int:
     """Algorithmic HBM bytes of one call (the library's byte model)."""
     d = Dims(batch, heads, HEAD_DIM, CONV_WIDTH, 1,
-             KDA_OUTPUT_NORM if norm else 0, 1e-5)
+             (KDA_OUTPUT_NORM if norm else 0) | int(variants), 1e-5)
+    if raw_gates:
+        return int(lib().kda_decode_raw_gates_bytes(ctypes.byref(d),
+                                                    int(live_rows),
+                                                    int(conv_bias)))
     return int(lib().kda_decode_bytes(ctypes.byref(d), int(live_rows)))
 
 
@@ -155,12 +223,9 @@ def state_stream_probe(tiles: torch.Tensor, waves: int = 8,
     if tiles.dim() < 2 or tuple(tiles.shape[-2:]) != (HEAD_DIM, HEAD_DIM):
         raise ValueError("tiles must be [..., 128, 128]")
     n = tiles.numel() // (HEAD_DIM * HEAD_DIM)
-    if stream is None:
-        stream = torch.cuda.current_stream(tiles.device).cuda_stream
-    elif isinstance(stream, torch.cuda.Stream):
-        stream = stream.cuda_stream
     with torch.cuda.device(tiles.device):
         rc = lib().kda_state_stream_probe(tiles.data_ptr(), n, int(waves),
-                                          float(scale), stream)
+                                          float(scale),
+                                          _stream(stream, tiles.device))
     if rc != KDA_OK:
         raise KdaError(rc, status_string(rc))

@@ -84,7 +84,7 @@ def test_null_dims_rejected():
 @no_gpu
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=-1), 1), (dict(num_slots=0), 1), (dict(num_heads=0), 1),
-    (dict(flags=2), 1), (dict(norm_eps=0.0), 1),
+    (dict(flags=0x40), 1), (dict(flags=0x21), 1), (dict(norm_eps=0.0), 1),
     (dict(norm_eps=float("nan")), 1), (dict(norm_eps=float("inf")), 1),
     (dict(num_heads=16), 2), (dict(num_heads=8), 2), (dict(head_dim=64), 2),
     (dict(conv_width=3), 2),
@@ -141,3 +141,46 @@ def test_probe_argument_checks():
     assert L.kda_state_stream_probe(FAKE + 4, 4, 8, 1.0, None) == 3
     assert L.kda_state_stream_probe(FAKE, 0, 8, 1.0, None) == 0
     assert L.kda_state_stream_probe(FAKE, 4, 8, 1.0, None) == 4
+
+
+
+def call_raw(dims, ptrs=None, lower_bound=0.0):
+    # qkv, conv_w, conv_bias, conv_state, rec_state, raw_g, raw_beta, A_log,
+    # dt_bias | lower_bound | gate, norm_w, state_idx, out, stream
+    p = [FAKE] * 14 if ptrs is None else ptrs
+    return kda.lib().kda_decode_raw_gates(ctypes.byref(dims), *p[:9],
+                                          lower_bound, *p[9:], None)
+
+
+@no_gpu
+def test_raw_gates_entry_checks():
+    assert call_raw(dims()) == 4                       # valid up to device
+    assert call_raw(dims(flags=0x21), lower_bound=-2.0) == 4
+    assert call_raw(dims(flags=0x21), lower_bound=0.0) == 1
+    assert call_raw(dims(flags=0x21), lower_bound=float("-inf")) == 1
+    assert call_raw(dims(flags=0x41)) == 1
+    assert call_raw(dims(batch=0), [None] * 14) == 0
+    p = [FAKE] * 14
+    p[2] = None                                        # no conv bias: fine
+    assert call_raw(dims(), p) == 4
+    p[2] = FAKE + 8                                    # misaligned conv bias
+    assert call_raw(dims(), p) == 3
+    for which in (5, 6, 7, 8):                         # raw gate inputs
+        p = [FAKE] * 14
+        p[which] = None
+        assert call_raw(dims(), p) == 1
+        p[which] = FAKE + 2
+        assert call_raw(dims(), p) == 3
+
+
+def test_byte_model_variants():
+    per_unit = 137476
+    B, H = 8, 12
+    base = kda.decode_bytes(B, H, B)
+    assert base == B * H * per_unit + 4 * B + 3 * 4 * H * 128 * 4 + 512
+    assert kda.decode_bytes(B, H, B, variants=kda.KDA_NO_CONV_UPDATE) == \
+        base - B * H * 2304
+    raw = kda.decode_bytes(B, H, B, raw_gates=True)
+    assert raw == base - B * H * (256 + 2) + H * 4 + H * 128 * 4
+    assert kda.decode_bytes(B, H, B, raw_gates=True, conv_bias=True) == \
+        raw + 3 * H * 128 * 4

@@ -1,0 +1,175 @@
+"""GPU parity of the kernel variants and of kda_decode_raw_gates against the
+CPU oracle (same seeded inputs, same bars as the plain step).
+
+The variants follow the template switches and inputs of the page "PR
+#50654 完整报告 -- [ROCm][Perf] Kimi-K3 Fused kernel for KDA decode"
+("Implementation breakdown", item 1: output norm, conv-state update, safe
+gate; kda.py excerpt: raw gate inputs, conv bias, the transposed conv-state
+view) plus two flagged readings the page leaves open (q/k L2 norm, SiLU
+output gate).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from linear_attention_decode_02_amd import kda, synth
+
+import _parity as P
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+DEV = "cuda:0"
+
+# oracle flag bit == library flag bit
+assert (O.NO_CONV_UPDATE, O.CONV_TAP_MAJOR, O.QK_L2NORM, O.GATE_SILU,
+        O.BOUNDED_GATE) == (kda.KDA_NO_CONV_UPDATE, kda.KDA_CONV_TAP_MAJOR,
+                            kda.KDA_QK_L2NORM, kda.KDA_GATE_SILU,
+                            kda.KDA_BOUNDED_GATE)
+
+
+def add_raw_gates(w, inp, rng, bias=True):
+    B, H, D = w.batch, w.heads, w.head_dim
+    inp.update(
+        raw_g=synth.to_bf16_bits(rng.normal(0, 2, (B, H, D)).astype(np.float32)),
+        raw_beta=synth.to_bf16_bits(rng.normal(0, 1, (B, H)).astype(np.float32)),
+        A_log=rng.normal(0, 0.5, H).astype(np.float32),
+        dt_bias=rng.normal(0, 0.5, H * D).astype(np.float32))
+    if bias:
+        inp["conv_bias"] = rng.normal(0, 0.3, 3 * H * D).astype(np.float32)
+
+
+def run_gpu(w, inp, variants, raw=False, lower_bound=None, t=None):
+    if t is None:
+        t = synth.to_torch(inp, DEV)
+        for key in ("raw_g", "raw_beta"):
+            if key in inp:
+                t[key] = torch.from_numpy(inp[key].view(np.int16)).view(
+                    torch.bfloat16).to(DEV)
+    out = torch.full((w.batch, w.channels), float("nan"), dtype=torch.bfloat16,
+                     device=DEV)
+    if raw:
+        kda.kda_decode_raw_gates(
+            t["qkv"], t["conv_w"], t.get("conv_bias"), t["conv_state"],
+            t["rec_state"], t["raw_g"], t["raw_beta"], t["A_log"],
+            t["dt_bias"], t["gate"] if w.norm else None,
+            t["norm_w"] if w.norm else None, t["state_idx"], out, norm=w.norm,
+            eps=w.eps, lower_bound=lower_bound, variants=variants)
+    else:
+        kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"], t["rec_state"],
+                       t["g"], t["beta"], t["gate"] if w.norm else None,
+                       t["norm_w"] if w.norm else None, t["state_idx"], out,
+                       norm=w.norm, eps=w.eps, variants=variants)
+    torch.cuda.synchronize()
+    return {"out": synth.bf16_bits(out),
+            "conv_state": synth.bf16_bits(t["conv_state"]),
+            "rec_state": t["rec_state"].cpu().numpy()}, t
+
+
+def check(w, inp, got, ref, in_cs, in_rs, flags, scaled=False):
+    cs_got, cs_ref, cs_in = got["conv_state"], ref["conv_state"], in_cs
+    if flags & O.CONV_TAP_MAJOR:       # compare in [S, 3C, W-1] order
+        cs_got, cs_ref, cs_in = (np.ascontiguousarray(a.transpose(0, 2, 1))
+                                 for a in (cs_got, cs_ref, cs_in))
+    st = P.check_states(cs_got, got["rec_state"], cs_ref, ref["rec_state"],
+                        cs_in, in_rs, inp["state_idx"], w.num_slots,
+                        scaled=scaled)
+    st.update(P.check_output(got["out"], ref["y"], inp["state_idx"],
+                             w.num_slots, w.heads))
+    return st
+
+
+CASES = {
+    "no_conv_update": (O.NO_CONV_UPDATE, False, None),
+    "tap_major": (O.CONV_TAP_MAJOR, False, None),
+    "qk_l2norm": (O.QK_L2NORM, False, None),
+    "gate_silu": (O.GATE_SILU, False, None),
+    "combined": (O.QK_L2NORM | O.CONV_TAP_MAJOR | O.GATE_SILU, False, None),
+    "raw_gates": (0, True, None),
+    "raw_gates_bounded": (O.BOUNDED_GATE, True, -5.0),
+    "raw_bounded_l2_tap_nonorm": (O.BOUNDED_GATE | O.QK_L2NORM |
+                                  O.CONV_TAP_MAJOR, True, -3.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("H,B", [(48, 33), (12, 7)])
+def test_variant_parity(name, H, B):
+    flags, raw, lb = CASES[name]
+    rng = np.random.default_rng([sum(map(ord, name)), H])
+    w = synth.small(f"v_{name}", batch=B, heads=H, num_slots=B + 4,
+                    seed=200 + H + B, null_every=4,
+                    norm="nonorm" not in name)
+    inp = synth.make_inputs(w)
+    if raw:
+        add_raw_gates(w, inp, rng)
+        inp["lower_bound"] = lb if lb is not None else 0.0
+    if flags & O.CONV_TAP_MAJOR:
+        inp["conv_state"] = np.ascontiguousarray(
+            inp["conv_state"].transpose(0, 2, 1))
+    print(f"[variant] {name} H={H} B={B} flags={flags:#x} raw={raw}",
+          flush=True)
+    ref = O.decode(inp, heads=H, norm=w.norm, eps=w.eps, dtype="f32",
+                   flags=flags)
+    got, _ = run_gpu(w, inp, flags & ~O.BOUNDED_GATE, raw=raw, lower_bound=lb)
+    st = check(w, inp, got, ref, inp["conv_state"], inp["rec_state"], flags)
+    if flags & O.NO_CONV_UPDATE:
+        assert np.array_equal(got["conv_state"], inp["conv_state"])
+    print(f"[variant] {name}: {st}", flush=True)
+
+
+def test_raw_gate_l2norm_chain_is_contractive():
+    """Eight chained calls in the L2-normalised, raw-gate configuration
+    (unit keys, beta < 1: the update never amplifies the state), compared
+    with the oracle's own trajectory under the absolute 1e-3 bar."""
+    rng = np.random.default_rng(77)
+    w = synth.small("chain", batch=24, heads=96, num_slots=40, seed=78,
+                    null_every=6)
+    inp = synth.make_inputs(w)
+    trng = inp.pop("rng")
+    add_raw_gates(w, inp, rng)
+    flags = O.QK_L2NORM | O.BOUNDED_GATE
+    inp["lower_bound"] = -5.0
+    ref_cs, ref_rs = inp["conv_state"].copy(), inp["rec_state"].copy()
+    gpu_cs, gpu_rs = ref_cs.copy(), ref_rs.copy()
+    t = None
+    for step in range(8):
+        if step:
+            tok = synth.make_token(w, trng)
+            inp.update(qkv=tok["qkv"], gate=tok["gate"],
+                       raw_g=synth.to_bf16_bits(rng.normal(
+                           0, 2, (w.batch, w.heads, 128)).astype(np.float32)),
+                       raw_beta=synth.to_bf16_bits(rng.normal(
+                           0, 1, (w.batch, w.heads)).astype(np.float32)))
+            inp["state_idx"] = np.roll(inp["state_idx"], 5)
+            for key in ("qkv", "gate", "raw_g", "raw_beta"):
+                t[key] = torch.from_numpy(inp[key].view(np.int16)).view(
+                    torch.bfloat16).to(DEV)
+            t["state_idx"] = torch.from_numpy(inp["state_idx"]).to(DEV)
+        got, t = run_gpu(w, inp, flags & ~O.BOUNDED_GATE, raw=True,
+                         lower_bound=-5.0, t=t)
+        ref = O.decode(dict(inp, conv_state=ref_cs, rec_state=ref_rs),
+                       heads=w.heads, norm=True, eps=w.eps, dtype="f32",
+                       flags=flags, inplace=True)
+        st = check(w, inp, got, ref, gpu_cs, gpu_rs, 0)
+        print(f"[chain] step {step}: {st}", flush=True)
+        gpu_cs, gpu_rs = got["conv_state"], got["rec_state"]
+    assert np.abs(ref_rs).max() < 50.0     # stayed O(1): contractive
+
+
+def test_b256_h48_full_size_kda_configuration():
+    """The batch-256, 48-head workload at full size in the configuration
+    with raw gates, conv bias, q/k L2 norm and the bounded gate."""
+    rng = np.random.default_rng(5)
+    w = synth.B256_H48
+    inp = synth.make_inputs(w)
+    add_raw_gates(w, inp, rng)
+    inp["lower_bound"] = -5.0
+    flags = O.QK_L2NORM | O.BOUNDED_GATE
+    ref = O.decode(inp, heads=w.heads, norm=True, eps=w.eps, dtype="f32",
+                   flags=flags)
+    got, _ = run_gpu(w, inp, O.QK_L2NORM, raw=True, lower_bound=-5.0)
+    st = check(w, inp, got, ref, inp["conv_state"], inp["rec_state"], 0)
+    print(f"[b256 kda config] {st}", flush=True)
