@@ -38,6 +38,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "kda_decode_b256_h48_traffic.md")
 
 
+# name -> (flag bits, raw gates + conv bias)
+VARIANTS = {
+    "plain": (0, False),
+    "no_conv_update": (0x02, False),
+    "conv_tap_major": (0x04, False),
+    "qk_l2norm": (0x08, False),
+    "gate_silu": (0x10, False),
+    "raw_gates": (0, True),
+    # raw gates + conv bias + q/k L2 norm + bounded gate
+    "kda_full": (0x08 | 0x20, True),
+}
+
+
 def kernel_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -64,6 +77,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="b256_h48_pool512_null32")
+    ap.add_argument("--variant", default="plain", choices=sorted(VARIANTS),
+                    help="kernel variant (default: the plain step)")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="decode tokens per row and call (> 1: the "
+                         "multi-token entry point, state kept on chip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU-oracle time for the baseline (0: skip)")
     ap.add_argument("--no-graph", action="store_true",
@@ -89,7 +107,14 @@ def main():
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(w)
+    T = args.tokens
+    inp = synth.make_inputs(w) if T == 1 else synth.make_tokens(w, T)
+    vflags, raw = VARIANTS[args.variant]
+    if T > 1 and (raw or w.layers > 1):
+        sys.exit("--tokens > 1 runs the plain flag variants of one layer")
+    if vflags & kda.KDA_CONV_TAP_MAJOR:
+        inp["conv_state"] = np.ascontiguousarray(
+            inp["conv_state"].transpose(0, 2, 1))
     layers = [synth.to_torch(inp, dev)]
     if w.layers > 1:
         # independent layers: own weights, inputs and slots; the pools are
@@ -99,21 +124,53 @@ def main():
             t["conv_state"] = layers[0]["conv_state"].clone()
             t["rec_state"] = layers[0]["rec_state"].clone()
             layers.append(t)
-    for t in layers:
-        t["out"] = torch.empty(w.batch, w.channels, dtype=torch.bfloat16,
+    for li, t in enumerate(layers):
+        t["out"] = torch.empty((w.batch, T, w.channels) if T > 1 else
+                               (w.batch, w.channels), dtype=torch.bfloat16,
                                device=dev)
+        if raw:     # raw gate inputs and conv bias, drawn per layer
+            rh = raw_inputs(w, li, np, synth)
+            if li == 0:
+                inp.update(rh)
+            for key, a in rh.items():
+                if isinstance(a, np.ndarray):
+                    t[key] = (torch.from_numpy(a.view(np.int16)).view(
+                        torch.bfloat16) if a.dtype == np.uint16
+                        else torch.from_numpy(a)).to(dev)
     idx = inp["state_idx"]
     live_rows = int(((idx > 0) & (idx < w.num_slots)).sum())
-    units = live_rows * w.heads                      # per layer
-    alg_bytes = kda.decode_bytes(w.batch, w.heads, live_rows, w.norm)
+    units = live_rows * w.heads * T                  # per layer
+    if T > 1:
+        alg_bytes = kda.decode_tokens_bytes(w.batch, w.heads, T, live_rows,
+                                            w.norm, variants=vflags)
+    else:
+        alg_bytes = kda.decode_bytes(w.batch, w.heads, live_rows, w.norm,
+                                     variants=vflags & ~kda.KDA_BOUNDED_GATE,
+                                     raw_gates=raw, conv_bias=raw)
     L = len(layers)
     stream = torch.cuda.current_stream(dev)
 
     def call(t, on):
-        kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"], t["rec_state"],
-                       t["g"], t["beta"], t["gate"], t["norm_w"],
-                       t["state_idx"], t["out"], norm=w.norm, eps=w.eps,
-                       stream=on)
+        if T > 1:
+            kda.kda_decode_tokens(t["qkv"], t["conv_w"], t["conv_state"],
+                                  t["rec_state"], t["g"], t["beta"],
+                                  t["gate"], t["norm_w"], t["state_idx"],
+                                  t["out"], norm=w.norm, eps=w.eps,
+                                  variants=vflags, stream=on)
+        elif raw:
+            kda.kda_decode_raw_gates(
+                t["qkv"], t["conv_w"], t["conv_bias"], t["conv_state"],
+                t["rec_state"], t["raw_g"], t["raw_beta"], t["A_log"],
+                t["dt_bias"], t["gate"], t["norm_w"], t["state_idx"],
+                t["out"], norm=w.norm, eps=w.eps,
+                lower_bound=-5.0 if vflags & kda.KDA_BOUNDED_GATE else None,
+                variants=vflags & ~kda.KDA_BOUNDED_GATE, stream=on)
+        else:
+            kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"],
+                           t["rec_state"], t["g"], t["beta"], t["gate"],
+                           t["norm_w"], t["state_idx"], t["out"],
+                           norm=w.norm, eps=w.eps, variants=vflags,
+                           stream=on)
 
     def step(on=stream):
         # on=None: torch's current stream (the capture stream in a graph)
@@ -179,7 +236,8 @@ def main():
     if not args.no_copy_probe:
         extra["copy_probe"] = copy_probe(torch, stream)
 
-    traffic = recorded_traffic(w.name)
+    traffic = (recorded_traffic(w.name)
+               if args.variant == "plain" and T == 1 else None)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -187,7 +245,8 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, inp, args.cpu_seconds, alg_bytes, units)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, alg_bytes, units,
+                           vflags, T)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "updates/s",
@@ -195,7 +254,9 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "layers": L, "batch": w.batch,
+        "config": {"workload": w.name, "variant": args.variant,
+                   "tokens_per_row": T, "layers": L,
+                   "batch": w.batch,
                    "heads": w.heads,
                    "head_dim": w.head_dim, "conv_width": w.conv_width,
                    "num_slots": w.num_slots, "null_rows": w.batch - live_rows,
@@ -206,6 +267,22 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def raw_inputs(w, layer, np, synth):
+    """Seeded raw gate inputs and conv bias of one layer (host arrays)."""
+    rng = np.random.default_rng([w.seed, layer, 2])
+    B, H, C = w.batch, w.heads, w.channels
+    return {
+        "raw_g": synth.to_bf16_bits(
+            rng.normal(0, 2, (B, H, 128)).astype(np.float32)),
+        "raw_beta": synth.to_bf16_bits(
+            rng.normal(0, 1, (B, H)).astype(np.float32)),
+        "A_log": rng.normal(0, 0.5, H).astype(np.float32),
+        "dt_bias": rng.normal(0, 0.5, C).astype(np.float32),
+        "conv_bias": rng.normal(0, 0.3, 3 * C).astype(np.float32),
+        "lower_bound": -5.0,
+    }
 
 
 def copy_probe(torch, stream, nbytes=1 << 30, reps=10):
@@ -232,7 +309,7 @@ def copy_probe(torch, stream, nbytes=1 << 30, reps=10):
             "GBs": round(2 * nbytes / sec / 1e9, 1)}
 
 
-def cpu_baseline(w, inp, seconds, alg_bytes, units):
+def cpu_baseline(w, inp, seconds, alg_bytes, units, flags=0, tokens=1):
     """The CPU oracle (fp32, OpenMP over units) on the same batch, repeated
     in place until ``seconds`` have passed."""
     import numpy as np
@@ -248,8 +325,14 @@ def cpu_baseline(w, inp, seconds, alg_bytes, units):
           flush=True)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.decode(work, heads=w.heads, norm=w.norm, eps=w.eps,
-                      dtype="f32", nthreads=cores, inplace=True)
+        if tokens > 1:
+            oracle.decode_tokens(work, heads=w.heads, tokens=tokens,
+                                 norm=w.norm, eps=w.eps, dtype="f32",
+                                 nthreads=cores, flags=flags, inplace=True)
+        else:
+            oracle.decode(work, heads=w.heads, norm=w.norm, eps=w.eps,
+                          dtype="f32", nthreads=cores, inplace=True,
+                          flags=flags)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:

@@ -157,6 +157,27 @@ kda_status kda_decode_raw_gates(const kda_dims* dims, const void* qkv,
                                 const float* norm_w, const int32_t* state_idx,
                                 void* out, void* hip_stream);
 
+/*
+ * Multi-token decode: `tokens` (T, 1..1024) successive tokens per row in
+ * one call, equal to T successive kda_decode calls on the same slots (the
+ * page's fused op covers one token per sequence and excludes speculative
+ * decoding -- the gate's num_spec == 0 -- so this extends it).  The state
+ * tile is read once and written once per (row, head); the conv window
+ * advances once per token.  Token-major buffers:
+ *   qkv   bf16 [B, T, 3C];  g fp32 [B, T, H, D];  beta fp32 [B, T, H];
+ *   gate  bf16 [B, T, C];   out bf16 [B, T, C]
+ * Other buffers, flags (KDA_BOUNDED_GATE excluded), rules and status codes
+ * as kda_decode; T outside 1..1024 is KDA_ERR_INVALID_ARG.  With
+ * KDA_NO_CONV_UPDATE every token sees the stored conv window, as T
+ * successive calls with that flag would.
+ */
+kda_status kda_decode_tokens(const kda_dims* dims, int32_t tokens,
+                             const void* qkv, const float* conv_w,
+                             void* conv_state, float* rec_state, const float* g,
+                             const float* beta, const void* gate,
+                             const float* norm_w, const int32_t* state_idx,
+                             void* out, void* hip_stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(kda_status status);
 
@@ -173,6 +194,11 @@ uint64_t kda_decode_bytes(const kda_dims* dims, int32_t live_rows);
  * has_conv_bias is nonzero. */
 uint64_t kda_decode_raw_gates_bytes(const kda_dims* dims, int32_t live_rows,
                                     int32_t has_conv_bias);
+
+/* The same for kda_decode_tokens: state and conv-state bytes once per
+ * (row, head), inputs and outputs once per token. */
+uint64_t kda_decode_tokens_bytes(const kda_dims* dims, int32_t tokens,
+                                 int32_t live_rows);
 
 #ifdef __cplusplus
 }

@@ -26,9 +26,9 @@
 //   * conv (waves 0-2, one q/k/v part each, two channels per lane) and the
 //     decay factors exp(g) (wave 3) go to LDS as {alpha, k, q} per key row.
 //   * column sums u = Sd^T k and p = Sd^T q (and the scalar q.k) are formed
-//     in registers, folded across the two half-waves with one lane swap,
-//     then across waves through LDS: 256 threads each finish one column
-//     (delta_j = beta (v_j - u_j), or p_j) and broadcast it.  The readout
+//     in registers and published
+//     per half-wave (32 partial rows) in LDS: 256 threads each finish one
+//     column (delta_j = beta (v_j - u_j), or p_j) and broadcast it.  The readout
 //     uses o = Sd^T q + (q.k) delta, which equals S'^T q exactly in real
 //     arithmetic, so the updated state is never re-read.
 //   * the RMSNorm sum of squares needs no further barrier: the first
@@ -44,6 +44,7 @@
 #include <cstring>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "kda_decode.h"
 
@@ -59,6 +60,7 @@ static_assert(kWaves >= 4 && kD * kD % (kThreads * 4) == 0, "tile shape");
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 struct Params {
   const uint16_t* qkv;
@@ -96,13 +98,250 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const unsigned short b = __builtin_bit_cast(unsigned short, (__bf16)hi);
   return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
 }
+// 1 / (1 + e^-x) with the hardware reciprocal (v_rcp_f32, ~1 ulp) instead
+// of the IEEE division sequence
 __device__ __forceinline__ float sigmoidf_(float x) {
-  return 1.0f / (1.0f + __expf(-x));
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// softplus with the usual linear branch above 20
+// Global-memory pointers (address space 1).
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+
+// A wave-uniform global pointer made opaque to the compiler (readfirstlane
+// of both halves): it stays in SGPRs and is not merged with per-lane
+// offsets into 64-bit VGPR addresses kept live across loops.
+template <typename T>
+__device__ __forceinline__ gptr<T> uniform_gptr(T* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<gptr<T>>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// base + a 32-bit byte offset, viewed as U: the access becomes a scalar
+// 64-bit base plus one 32-bit VGPR offset.
+template <typename U, typename T>
+__device__ __forceinline__ gptr<U> at_bytes(gptr<T> base, uint32_t byte_off) {
+  using C = typename std::conditional<std::is_const<T>::value, const char,
+                                      char>::type;
+  return reinterpret_cast<gptr<U>>(
+      reinterpret_cast<__attribute__((address_space(1))) C*>(base) + byte_off);
+}
+
+// Cross-lane sums on the VALU (DPP) plus scalar lane reads: no lane-address
+// registers (ds_bpermute needs one per pattern, which the compiler keeps
+// live across loops) and no LDS round trips.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                         0xF, 0xF, false));
+}
+// Sum over each row of 16 lanes, in every lane of the row: quad_perm
+// [1,0,3,2] and [2,3,0,1] (quads), row_half_mirror (8), row_mirror (16).
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+// v of lane l (a wave-uniform value)
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// softplus with the usual linear branch above 20 (for z < -17 the result
+// rounds to 0 instead of e^z; the decay exp(-a e^z) is then 1 either way)
 __device__ __forceinline__ float softplusf_(float z) {
-  return z > 20.0f ? z : log1pf(__expf(z));
+  return z > 20.0f ? z : __logf(1.0f + __expf(z));
+}
+
+// The thread's m-th float4 of a [128, 128] fp32 tile: key row rgrp + 32 m,
+// columns 4 col4 .. 4 col4 + 3, as a uniform row-block base plus the lane's
+// byte offset lane_off = rgrp * 512 + col4 * 16.
+__device__ __forceinline__ gptr<f4> tile_at(f4* st, uint32_t lane_off, int m) {
+  return at_bytes<f4>(uniform_gptr(st + m * kRowStride * (kD / 4)), lane_off);
+}
+__device__ __forceinline__ uint32_t tile_lane_off(int rgrp, int col4) {
+  return static_cast<uint32_t>(rgrp * (kD * 4) + col4 * 16);
+}
+
+// Workgroup-shared buffers of one unit.
+struct Lds {
+  f4 akq[kD];                // {exp(g_i), k_i, q_i, -} per key row i
+  float v[kD];
+  float red[2 * kWaves][2][kD];  // per-half-wave partial sums of u and p
+  float qk[2 * kWaves];          // per-half-wave partial q.k
+  float delta[kD];
+  float p[kD];
+  float qk_total;
+};
+
+// Conv window of channels c, c+1 from the three state words: element t of
+// the window of c is c[t], of c+1 is d[t] (oldest first).  [slot][channel]
+// [tap]: the words hold (c0, c1 | c2, d0 | d1, d2); [slot][tap][channel]:
+// word t holds (c_t, d_t).
+__device__ __forceinline__ void unpack_window(bool tap_major, uint32_t w0,
+                                              uint32_t w1, uint32_t w2,
+                                              float c[3], float d[3]) {
+  if (tap_major) {
+    c[0] = bf16_lo(w0); c[1] = bf16_lo(w1); c[2] = bf16_lo(w2);
+    d[0] = bf16_hi(w0); d[1] = bf16_hi(w1); d[2] = bf16_hi(w2);
+  } else {
+    c[0] = bf16_lo(w0); c[1] = bf16_hi(w0); c[2] = bf16_lo(w1);
+    d[0] = bf16_hi(w1); d[1] = bf16_lo(w2); d[2] = bf16_hi(w2);
+  }
+}
+
+// The three state words after appending token pair x2 (exact bit moves).
+__device__ __forceinline__ void shift_window(bool tap_major, uint32_t& w0,
+                                             uint32_t& w1, uint32_t& w2,
+                                             uint32_t x2) {
+  if (tap_major) {
+    w0 = w1;
+    w1 = w2;
+    w2 = x2;
+  } else {
+    // (c1, c2, x.lo) and (d1, d2, x.hi)
+    const uint32_t n0 = (w0 >> 16) | (w1 << 16);
+    const uint32_t n1 = (x2 & 0xffffu) | (w2 << 16);
+    const uint32_t n2 = (w2 >> 16) | (x2 & 0xffff0000u);
+    w0 = n0;
+    w1 = n1;
+    w2 = n2;
+  }
+}
+
+// Per-lane inputs of one token: waves 0..2 produce q, k or v of channels
+// i0, i0+1 (4-tap conv + SiLU, then optional L2 normalisation of q and k
+// across the wave); wave 3 produces exp(g) of key rows i0, i0+1.  Every
+// wave computes without branching on the wave; the caller stores.
+__device__ __forceinline__ void token_inputs(
+    uint32_t flags, int wave, uint32_t w0, uint32_t w1, uint32_t w2,
+    uint32_t x2, const f2 (&w_t)[kW], f2 bias2, bool has_bias, f2 g2,
+    float& y0, float& y1) {
+  float c[3], d[3];
+  unpack_window((flags & KDA_CONV_TAP_MAJOR) != 0, w0, w1, w2, c, d);
+  float a0 = has_bias ? bias2.x : 0.0f;
+  a0 += w_t[0].x * c[0];
+  a0 += w_t[1].x * c[1];
+  a0 += w_t[2].x * c[2];
+  a0 += w_t[3].x * bf16_lo(x2);
+  float a1 = has_bias ? bias2.y : 0.0f;
+  a1 += w_t[0].y * d[0];
+  a1 += w_t[1].y * d[1];
+  a1 += w_t[2].y * d[2];
+  a1 += w_t[3].y * bf16_hi(x2);
+  y0 = wave < 3 ? a0 * sigmoidf_(a0) : __expf(g2.x);
+  y1 = wave < 3 ? a1 * sigmoidf_(a1) : __expf(g2.y);
+  if ((flags & KDA_QK_L2NORM) && wave < 2) {
+    // wave 0 holds all of q, wave 1 all of k: x / sqrt(sum x^2 + 1e-6),
+    // q also scaled by D^-1/2
+    const float rows = sum16(y0 * y0 + y1 * y1);
+    const float ss = (lane_value(rows, 0) + lane_value(rows, 16)) +
+                     (lane_value(rows, 32) + lane_value(rows, 48));
+    const float r =
+        rsqrtf(ss + 1e-6f) * (wave == 0 ? 0.08838834764831845f : 1.0f);
+    y0 *= r;
+    y1 *= r;
+  }
+}
+
+__device__ __forceinline__ void store_token_inputs(Lds& L, int wave, int i0,
+                                                   float y0, float y1,
+                                                   f4* akq_rows = nullptr) {
+  if (wave == 2) {
+    *reinterpret_cast<f2*>(&L.v[i0]) = f2{y0, y1};
+  } else if (wave < 4) {
+    // q -> .z, k -> .y, exp(g) -> .x
+    const int comp = wave == 0 ? 2 : (wave == 1 ? 1 : 0);
+    float* base = reinterpret_cast<float*>(akq_rows ? akq_rows : L.akq);
+    base[i0 * 4 + comp] = y0;
+    base[(i0 + 1) * 4 + comp] = y1;
+  }
+}
+
+// Decay the thread's state rows in place and publish the half-wave's
+// partial column sums u = Sd^T k, p = Sd^T q and q.k (each half-wave covers
+// all 128 columns for its key rows).  k_rows receives k_i of the rows.
+// kLean: at most two rows' LDS reads in flight (fewer live VGPRs).
+// akq: the {exp(g), k, q} rows to use (L.akq by default).
+template <bool kLean = false>
+__device__ __forceinline__ void decay_and_partials(
+    Lds& L, f4 (&s)[kRowsPerThread], float (&k_rows)[kRowsPerThread],
+    int rgrp, int wave, int lane, int col4, const f4* akq_rows = nullptr) {
+  const f4* rows = akq_rows ? akq_rows : L.akq;
+  f4 u = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+  float qk = 0.f;
+#pragma unroll
+  for (int m = 0; m < kRowsPerThread; ++m) {
+    const f4 akq = rows[rgrp + kRowStride * m];
+    const f4 sd = s[m] * akq.x;
+    s[m] = sd;
+    u += akq.y * sd;
+    pq += akq.z * sd;
+    qk += akq.y * akq.z;
+    k_rows[m] = akq.y;
+    if (kLean && (m & 1)) __builtin_amdgcn_sched_barrier(0);
+  }
+  const int half = 2 * wave + (lane >> 5);  // == rgrp
+  *reinterpret_cast<f4*>(&L.red[half][0][4 * col4]) = u;
+  *reinterpret_cast<f4*>(&L.red[half][1][4 * col4]) = pq;
+  if ((lane & 31) == 0) L.qk[half] = qk;
+}
+
+// Reduce, then broadcast: threads 0..255 each finish one column of u
+// (delta_j = beta (v_j - u_j)) or of p, instead of every thread summing
+// all partials of its four columns.
+__device__ __forceinline__ void finish_columns(Lds& L, int tid, float beta) {
+  if (tid < 2 * kD) {
+    const int which = tid / kD;
+    const int j = tid % kD;
+    float acc = L.red[0][which][j];
+#pragma unroll
+    for (int r = 1; r < 2 * kWaves; ++r) acc += L.red[r][which][j];
+    if (which == 0)
+      L.delta[j] = beta * (L.v[j] - acc);
+    else
+      L.p[j] = acc;
+    if (tid == 0) {
+      float t = L.qk[0];
+#pragma unroll
+      for (int r = 1; r < 2 * kWaves; ++r) t += L.qk[r];
+      L.qk_total = t;
+    }
+  }
+}
+
+// Readout o = Sd^T q + (q.k) delta and the gated RMSNorm of one token, by
+// lanes 0..31 of wave 0 (four columns each); writes 4 bf16 at out4.
+template <bool kNorm>
+__device__ __forceinline__ void emit_output(const Lds& L, const float* norm_w,
+                                            uint32_t flags, float eps, int col4,
+                                            f4 delta, u2 gb,
+                                            gptr<uint16_t> out4) {
+  const f4 o = *reinterpret_cast<const f4*>(&L.p[4 * col4]) +
+               L.qk_total * delta;
+  f4 y = o;
+  if (kNorm) {
+    const float rows = sum16(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+    const float ss = lane_value(rows, 0) + lane_value(rows, 16);
+    const float r = rsqrtf(ss * (1.0f / kD) + eps);
+    const f4 w = *reinterpret_cast<const f4*>(norm_w + 4 * col4);
+    const f4 gv = {bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
+    f4 ga = {sigmoidf_(gv.x), sigmoidf_(gv.y), sigmoidf_(gv.z),
+             sigmoidf_(gv.w)};
+    if (flags & KDA_GATE_SILU) ga *= gv;
+    y = o * r * w * ga;
+  }
+  u2 ob;
+  ob.x = pack_bf16x2(y.x, y.y);
+  ob.y = pack_bf16x2(y.z, y.w);
+  *reinterpret_cast<gptr<u2>>(out4) = ob;
 }
 
 // kNorm: gated RMSNorm epilogue; kRawGates: g and beta from raw inputs.
@@ -112,13 +351,7 @@ template <bool kNorm, bool kRawGates>
 // At most 64 VGPRs, so that two 16-wave workgroups share a CU.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void kda_decode_kernel(Params p) {
-  __shared__ f4 s_akq[kD];          // {exp(g_i), k_i, q_i, 0} per key row i
-  __shared__ float s_v[kD];
-  __shared__ float s_red[kWaves][2][kD];  // per-wave partial u, p columns
-  __shared__ float s_qk[kWaves];
-  __shared__ float s_delta[kD];
-  __shared__ float s_p[kD];
-  __shared__ float s_qk_total;
+  __shared__ Lds L;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -150,16 +383,14 @@ void kda_decode_kernel(Params p) {
   const int part = wave < 3 ? wave : 2;
   const int64_t c = part * C + h * kD + i0;
   const uint32_t x2 = *reinterpret_cast<const uint32_t*>(p.qkv + n * 3 * C + c);
-  // Conv state words of channels c, c+1.  [slot][channel][tap]: three
-  // consecutive words hold (c t0, c t1 | c t2, c+1 t0 | c+1 t1, c+1 t2);
-  // [slot][tap][channel]: word t holds (c tap t, c+1 tap t), 3C apart.
+  // conv state words of channels c, c+1 (see unpack_window)
   uint32_t* cs_base = reinterpret_cast<uint32_t*>(
       p.conv_state + static_cast<int64_t>(slot) * 3 * C * (kW - 1) +
       (tap_major ? c : c * (kW - 1)));
   const int64_t cs_step = tap_major ? (3 * C) / 2 : 1;  // in words
-  const uint32_t cw0 = cs_base[0];
-  const uint32_t cw1 = cs_base[cs_step];
-  const uint32_t cw2 = cs_base[2 * cs_step];
+  uint32_t cw0 = cs_base[0];
+  uint32_t cw1 = cs_base[cs_step];
+  uint32_t cw2 = cs_base[2 * cs_step];
   f2 w_t[kW];
 #pragma unroll
   for (int t = 0; t < kW; ++t)
@@ -191,159 +422,238 @@ void kda_decode_kernel(Params p) {
   }
 
   // ---- issue the whole state tile ----------------------------------------
-  // Keep the small loads above ahead of the 16 state loads: the conv math
+  // Keep the small loads above ahead of the state loads: the conv math
   // then waits only for them (vmcnt retires in issue order).
   __builtin_amdgcn_sched_barrier(0);
   const int col4 = tid & 31;
   const int rgrp = tid >> 5;
   f4* st = reinterpret_cast<f4*>(
       p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD));
+  const uint32_t lane_off = tile_lane_off(rgrp, col4);
   f4 s[kRowsPerThread];
 #pragma unroll
   for (int m = 0; m < kRowsPerThread; ++m)
-    s[m] = __builtin_nontemporal_load(st + (rgrp + kRowStride * m) * (kD / 4) +
-                                      col4);
+    s[m] = __builtin_nontemporal_load(tile_at(st, lane_off, m));
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- conv update + SiLU, decay factors ---------------------------------
-  // Computed by every wave without branching on the wave (loads used
-  // unconditionally stay where they are issued); only the stores depend on
-  // the wave.  Window of channel c: (c0, c1, c2, token lo); of c+1:
-  // (d0, d1, d2, token hi), oldest first.
-  float c0, c1, c2, d0, d1, d2;
-  if (tap_major) {
-    c0 = bf16_lo(cw0); c1 = bf16_lo(cw1); c2 = bf16_lo(cw2);
-    d0 = bf16_hi(cw0); d1 = bf16_hi(cw1); d2 = bf16_hi(cw2);
-  } else {
-    c0 = bf16_lo(cw0); c1 = bf16_hi(cw0); c2 = bf16_lo(cw1);
-    d0 = bf16_hi(cw1); d1 = bf16_lo(cw2); d2 = bf16_hi(cw2);
-  }
-  const bool has_bias = p.conv_bias != nullptr;
-  float a0 = has_bias ? bias2.x : 0.0f;
-  a0 += w_t[0].x * c0;
-  a0 += w_t[1].x * c1;
-  a0 += w_t[2].x * c2;
-  a0 += w_t[3].x * bf16_lo(x2);
-  float a1 = has_bias ? bias2.y : 0.0f;
-  a1 += w_t[0].y * d0;
-  a1 += w_t[1].y * d1;
-  a1 += w_t[2].y * d2;
-  a1 += w_t[3].y * bf16_hi(x2);
-  float y0 = wave < 3 ? a0 * sigmoidf_(a0) : __expf(g2.x);
-  float y1 = wave < 3 ? a1 * sigmoidf_(a1) : __expf(g2.y);
-  if ((flags & KDA_QK_L2NORM) && wave < 2) {
-    // wave 0 holds all of q, wave 1 all of k: x / sqrt(sum x^2 + 1e-6),
-    // q also scaled by D^-1/2
-    float ss = y0 * y0 + y1 * y1;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    const float r = rsqrtf(ss + 1e-6f) * (wave == 0 ? 0.08838834764831845f
-                                                     : 1.0f);
-    y0 *= r;
-    y1 *= r;
-  }
+  float y0, y1;
+  token_inputs(flags, wave, cw0, cw1, cw2, x2, w_t, bias2,
+               p.conv_bias != nullptr, g2, y0, y1);
   if (wave < 3 && !(flags & KDA_NO_CONV_UPDATE)) {
-    // shifted windows, exact bit copies
-    if (tap_major) {
-      cs_base[0] = cw1;
-      cs_base[cs_step] = cw2;
-      cs_base[2 * cs_step] = x2;
-    } else {
-      // (cw0.hi, cw1.lo, x.lo) and (cw2.lo, cw2.hi, x.hi)
-      cs_base[0] = (cw0 >> 16) | (cw1 << 16);
-      cs_base[1] = (x2 & 0xffffu) | (cw2 << 16);
-      cs_base[2] = (cw2 >> 16) | (x2 & 0xffff0000u);
-    }
+    shift_window(tap_major, cw0, cw1, cw2, x2);
+    cs_base[0] = cw0;
+    cs_base[cs_step] = cw1;
+    cs_base[2 * cs_step] = cw2;
   }
-  if (wave == 2) {
-    *reinterpret_cast<f2*>(&s_v[i0]) = f2{y0, y1};
-  } else if (wave < 4) {
-    // q -> .z, k -> .y, exp(g) -> .x
-    const int comp = wave == 0 ? 2 : (wave == 1 ? 1 : 0);
-    float* base = reinterpret_cast<float*>(s_akq);
-    base[i0 * 4 + comp] = y0;
-    base[(i0 + 1) * 4 + comp] = y1;
-  }
+  store_token_inputs(L, wave, i0, y0, y1);
   __syncthreads();
 
-  // ---- decay and column sums ---------------------------------------------
-  f4 u = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-  float qk = 0.f;
-#pragma unroll
-  for (int m = 0; m < kRowsPerThread; ++m) {
-    const f4 akq = s_akq[rgrp + kRowStride * m];
-    const f4 sd = s[m] * akq.x;
-    s[m] = sd;
-    u += akq.y * sd;
-    pq += akq.z * sd;
-    qk += akq.y * akq.z;
-  }
-  // fold the two half-waves (key rows rgrp and rgrp+1 of this wave)
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    u[e] += __shfl_xor(u[e], 32);
-    pq[e] += __shfl_xor(pq[e], 32);
-  }
-  qk += __shfl_xor(qk, 32);
-  if (lane < 32) {
-    *reinterpret_cast<f4*>(&s_red[wave][0][4 * col4]) = u;
-    *reinterpret_cast<f4*>(&s_red[wave][1][4 * col4]) = pq;
-  }
-  if (lane == 0) s_qk[wave] = qk;
+  // ---- decay, column sums, delta --------------------------------------------
+  float k_rows[kRowsPerThread];
+  decay_and_partials(L, s, k_rows, rgrp, wave, lane, col4);
   __syncthreads();
-  // Reduce, then broadcast: threads 0..255 each finish one column of u
-  // (delta_j = beta (v_j - u_j)) or of p, instead of every thread summing
-  // all partials of its four columns.
-  if (tid < 2 * kD) {
-    const int which = tid / kD;
-    const int j = tid % kD;
-    float acc = s_red[0][which][j];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) acc += s_red[w][which][j];
-    if (which == 0)
-      s_delta[j] = beta * (s_v[j] - acc);
-    else
-      s_p[j] = acc;
-    if (tid == 0) {
-      float t = s_qk[0];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) t += s_qk[w];
-      s_qk_total = t;
-    }
-  }
+  finish_columns(L, tid, beta);
   __syncthreads();
 
   // ---- delta rule update, streamed back ------------------------------------
-  const f4 delta = *reinterpret_cast<const f4*>(&s_delta[4 * col4]);
+  const f4 delta = *reinterpret_cast<const f4*>(&L.delta[4 * col4]);
 #pragma unroll
-  for (int m = 0; m < kRowsPerThread; ++m) {
-    const float ki = s_akq[rgrp + kRowStride * m].y;
-    __builtin_nontemporal_store(s[m] + ki * delta,
-                                st + (rgrp + kRowStride * m) * (kD / 4) + col4);
-  }
+  for (int m = 0; m < kRowsPerThread; ++m)
+    __builtin_nontemporal_store(s[m] + k_rows[m] * delta,
+                                tile_at(st, lane_off, m));
 
   // ---- readout and gated RMSNorm (wave 0, lanes 0..31 own the output) -----
   if (tid >= 32) return;
-  const f4 o = *reinterpret_cast<const f4*>(&s_p[4 * col4]) + s_qk_total * delta;
-  f4 y = o;
-  if (kNorm) {
-    float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 32);
-    const float r = rsqrtf(ss * (1.0f / kD) + p.eps);
-    const f4 w = *reinterpret_cast<const f4*>(p.norm_w + 4 * col4);
-    const uint2 gb = *reinterpret_cast<const uint2*>(
-        p.gate + static_cast<int64_t>(n) * C + h * kD + 4 * col4);
-    f4 gv = {bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
-    f4 ga = {sigmoidf_(gv.x), sigmoidf_(gv.y), sigmoidf_(gv.z), sigmoidf_(gv.w)};
-    if (flags & KDA_GATE_SILU) ga *= gv;
-    y = o * r * w * ga;
+  const u2 gb = kNorm ? *reinterpret_cast<const u2*>(
+                             p.gate + static_cast<int64_t>(n) * C + h * kD +
+                             4 * col4)
+                       : u2{0u, 0u};
+  emit_output<kNorm>(L, p.norm_w, flags, p.eps, col4, delta, gb,
+                     at_bytes<uint16_t>(uniform_gptr(p.out + n * C + h * kD),
+                                        8 * col4));
+}
+
+// T decode tokens per row in one launch, equal to T successive single-token
+// steps on the same slots: the state tile is read once, kept in VGPRs
+// across the tokens and written once, the conv window advances in
+// registers.  Buffers carry a token axis after the row axis (qkv [B, T, 3C],
+// g [B, T, H, D], beta [B, T, H], gate and out [B, T, C]).  Three barriers
+// per token; the next token's small inputs are fetched while the current
+// one is processed.
+template <bool kNorm>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void kda_decode_tokens_kernel(Params p, int T) {
+  __shared__ Lds L;
+  __shared__ f2 s_w[3][kW][kD / 2];   // conv taps, per part and lane
+  __shared__ float s_norm_w[kD];
+  // {exp(g), k, q} rows by token parity: the update of token t re-reads k
+  // while token t+1's rows are being written into the other buffer
+  __shared__ f4 s_akq[2][kD];
+  // conv window words of waves 0..2, kept in LDS across the token loop
+  __shared__ uint32_t s_win[3][3][kD / 2];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int unit = blockIdx.x;
+  const int H = p.heads;
+  const int n = unit / H;
+  const int h = unit - n * H;
+  const int C = H * kD;
+  const int64_t row_tok = static_cast<int64_t>(n) * T;  // first (row, token)
+
+  const int32_t slot = p.state_idx[n];
+  if (slot <= 0 || slot >= p.num_slots) {
+    for (int i = tid; i < T * (kD / 8); i += kThreads) {
+      uint4* o = reinterpret_cast<uint4*>(
+          p.out + (row_tok + i / (kD / 8)) * C + h * kD);
+      o[i % (kD / 8)] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
   }
-  uint2 ob;
-  ob.x = pack_bf16x2(y.x, y.y);
-  ob.y = pack_bf16x2(y.z, y.w);
-  *reinterpret_cast<uint2*>(p.out + static_cast<int64_t>(n) * C + h * kD +
-                            4 * col4) = ob;
+
+  const uint32_t flags = p.flags;
+  const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
+  const int i0 = 2 * lane;
+  const int part = wave < 3 ? wave : 2;
+  // per-lane 32-bit offsets from per-token uniform bases
+  const uint32_t c = part * C + h * kD + i0;         // into a qkv token row
+  const uint32_t gi = h * kD + i0;                   // into a g token row
+  const uint32_t oc = h * kD + 4 * (tid & 31);       // into gate/out rows
+  const uint16_t* qkv_row = p.qkv + row_tok * 3 * C;
+  const float* g_row = p.g + row_tok * H * kD;
+  const float* beta_row = p.beta + row_tok * H;
+  uint32_t x2 = *at_bytes<const uint32_t>(uniform_gptr(qkv_row), 2 * c);
+  f2 g2 = *at_bytes<const f2>(uniform_gptr(g_row), 4 * gi);
+  float beta = beta_row[h];
+  // output gate words of lanes 0..31 (wave 0 loads them; lanes 32..63
+  // mirror 0..31)
+  u2 gate_w = {0u, 0u};
+  if (kNorm && wave == 0)
+    gate_w = *at_bytes<const u2>(uniform_gptr(p.gate + row_tok * C), 2 * oc);
+  uint32_t* cs_slot = reinterpret_cast<uint32_t*>(
+      p.conv_state + static_cast<int64_t>(slot) * 3 * C * (kW - 1));
+  const uint32_t cs_off = (tap_major ? c : c * (kW - 1)) / 2;  // in words
+  const uint32_t cs_step = tap_major ? (3 * C) / 2 : 1;
+  const gptr<uint32_t> cs_g = uniform_gptr(cs_slot);
+  if (wave < 3) {
+    s_win[0][wave][lane] = *at_bytes<uint32_t>(cs_g, 4 * cs_off);
+    s_win[1][wave][lane] = *at_bytes<uint32_t>(cs_g, 4 * (cs_off + cs_step));
+    s_win[2][wave][lane] =
+        *at_bytes<uint32_t>(cs_g, 4 * (cs_off + 2 * cs_step));
+  }
+  // conv taps and norm weights go to LDS once (read per token: fewer live
+  // VGPRs across the token loop)
+  if (wave < 3) {
+#pragma unroll
+    for (int t = 0; t < kW; ++t)
+      s_w[wave][t][lane] = *reinterpret_cast<const f2*>(
+          p.conv_w + (wave * kW + t) * C + h * kD + i0);
+  } else if (wave == 3 && kNorm) {
+    *reinterpret_cast<f2*>(&s_norm_w[i0]) =
+        *reinterpret_cast<const f2*>(p.norm_w + i0);
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  const int col4 = tid & 31;
+  const int rgrp = tid >> 5;
+  f4* st = reinterpret_cast<f4*>(
+      p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD));
+  const uint32_t lane_off = tile_lane_off(rgrp, col4);
+  f4 s[kRowsPerThread];
+#pragma unroll
+  for (int m = 0; m < kRowsPerThread; ++m)
+    s[m] = __builtin_nontemporal_load(tile_at(st, lane_off, m));
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();   // s_w, s_norm_w visible
+
+  for (int t = 0; t < T; ++t) {
+    // Lane-derived offsets are recomputed every token from an opaque copy
+    // of the thread id: cheaper than keeping a dozen of them live across
+    // the loop (they would not fit the 64-VGPR budget otherwise).
+    int tid_t = tid;
+    asm volatile("" : "+v"(tid_t));
+    const int wave_t = tid_t >> 6;
+    const int lane_t = tid_t & 63;
+    const int i0_t = 2 * lane_t;
+    const int part_t = wave_t < 3 ? wave_t : 2;
+    const int col4_t = tid_t & 31;
+    const int rgrp_t = tid_t >> 5;
+    const uint32_t c_t = part_t * C + h * kD + i0_t;
+    const uint32_t gi_t = h * kD + i0_t;
+    const uint32_t oc_t = h * kD + 4 * col4_t;
+
+    f4* akq_t = s_akq[t & 1];
+    if (wave_t < 4) {   // per-token inputs: waves 0..3 only (uniform branch)
+      f2 w_t[kW];
+#pragma unroll
+      for (int tap = 0; tap < kW; ++tap) w_t[tap] = s_w[part_t][tap][lane_t];
+      // each lane of waves 0..2 owns its window words
+      uint32_t cw0 = 0, cw1 = 0, cw2 = 0;
+      if (wave_t < 3) {
+        cw0 = s_win[0][wave_t][lane_t];
+        cw1 = s_win[1][wave_t][lane_t];
+        cw2 = s_win[2][wave_t][lane_t];
+      }
+      float y0, y1;
+      token_inputs(flags, wave_t, cw0, cw1, cw2, x2, w_t, f2{0.f, 0.f}, false,
+                   g2, y0, y1);
+      // successive calls with the update off all see the stored window
+      if (wave_t < 3 && !(flags & KDA_NO_CONV_UPDATE)) {
+        shift_window(tap_major, cw0, cw1, cw2, x2);
+        s_win[0][wave_t][lane_t] = cw0;
+        s_win[1][wave_t][lane_t] = cw1;
+        s_win[2][wave_t][lane_t] = cw2;
+      }
+      store_token_inputs(L, wave_t, i0_t, y0, y1, akq_t);
+    }
+    __syncthreads();
+    float k_unused[kRowsPerThread];
+    decay_and_partials<true>(L, s, k_unused, rgrp_t, wave_t, lane_t, col4_t,
+                             akq_t);
+    __syncthreads();
+
+    // fetch the next token's small inputs; they are used one iteration
+    // later (issued after the decay phase, the register peak)
+    const int tn = t + 1 < T ? t + 1 : t;
+    const uint32_t x2_next = *at_bytes<const uint32_t>(
+        uniform_gptr(qkv_row + static_cast<int64_t>(tn) * 3 * C), 2 * c_t);
+    const f2 g2_next = *at_bytes<const f2>(
+        uniform_gptr(g_row + static_cast<int64_t>(tn) * H * kD), 4 * gi_t);
+    const float beta_next = beta_row[static_cast<int64_t>(tn) * H + h];
+    u2 gate_next = {0u, 0u};
+    if (kNorm && wave_t == 0)
+      gate_next = *at_bytes<const u2>(
+          uniform_gptr(p.gate + (row_tok + tn) * C), 2 * oc_t);
+
+    finish_columns(L, tid_t, beta);
+    __syncthreads();
+    const f4 delta = *reinterpret_cast<const f4*>(&L.delta[4 * col4_t]);
+#pragma unroll
+    for (int m = 0; m < kRowsPerThread; ++m)
+      s[m] += akq_t[rgrp_t + kRowStride * m].y * delta;
+    if (tid_t < 32) {
+      emit_output<kNorm>(L, s_norm_w, flags, p.eps, col4_t, delta, gate_w,
+                         at_bytes<uint16_t>(
+                             uniform_gptr(p.out + (row_tok + t) * C), 2 * oc_t));
+    }
+    x2 = x2_next;
+    g2 = g2_next;
+    beta = beta_next;
+    gate_w = gate_next;
+  }
+
+  // ---- write back: state tile once, conv window once ----------------------
+#pragma unroll
+  for (int m = 0; m < kRowsPerThread; ++m)
+    __builtin_nontemporal_store(s[m], tile_at(st, lane_off, m));
+  if (wave < 3 && !(flags & KDA_NO_CONV_UPDATE)) {
+    *at_bytes<uint32_t>(cs_g, 4 * cs_off) = s_win[0][wave][lane];
+    *at_bytes<uint32_t>(cs_g, 4 * (cs_off + cs_step)) = s_win[1][wave][lane];
+    *at_bytes<uint32_t>(cs_g, 4 * (cs_off + 2 * cs_step)) =
+        s_win[2][wave][lane];
+  }
 }
 
 // ---- host side -----------------------------------------------------------
@@ -367,6 +677,8 @@ bool aligned16(const void* ptr) {
 }
 
 bool supported_heads(int h) { return h == 12 || h == 24 || h == 48 || h == 96; }
+
+constexpr int32_t kMaxTokens = 1024;
 
 constexpr uint32_t kPlainFlags = KDA_OUTPUT_NORM | KDA_NO_CONV_UPDATE |
                                  KDA_CONV_TAP_MAJOR | KDA_QK_L2NORM |
@@ -513,6 +825,59 @@ kda_status kda_decode_raw_gates(const kda_dims* d, const void* qkv,
   p.dt_bias = dt_bias;
   p.lower_bound = lower_bound;
   return launch<true>(d, p, hip_stream);
+}
+
+kda_status kda_decode_tokens(const kda_dims* d, int32_t tokens,
+                             const void* qkv, const float* conv_w,
+                             void* conv_state, float* rec_state, const float* g,
+                             const float* beta, const void* gate,
+                             const float* norm_w, const int32_t* state_idx,
+                             void* out, void* hip_stream) {
+  kda_status st = check_dims(d, kPlainFlags);
+  if (st != KDA_OK) return st;
+  if (tokens < 1 || tokens > kMaxTokens) return KDA_ERR_INVALID_ARG;
+  if (d->batch == 0) return KDA_OK;
+  st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                    state_idx, out);
+  if (st != KDA_OK) return st;
+  if (!g || !beta) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(g) || !aligned16(beta)) return KDA_ERR_MISALIGNED;
+  Params p = base_params(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                         state_idx, out);
+  p.g = g;
+  p.beta = beta;
+  // one token: the buffers are the single-token layout
+  if (tokens == 1) return launch<false>(d, p, hip_stream);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return KDA_ERR_DEVICE;
+  const dim3 grid(static_cast<unsigned>(d->batch * d->num_heads));
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (d->flags & KDA_OUTPUT_NORM)
+    hipLaunchKernelGGL(kda_decode_tokens_kernel<true>, grid, dim3(kThreads), 0,
+                       stream, p, tokens);
+  else
+    hipLaunchKernelGGL(kda_decode_tokens_kernel<false>, grid, dim3(kThreads),
+                       0, stream, p, tokens);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+uint64_t kda_decode_tokens_bytes(const kda_dims* d, int32_t tokens,
+                                 int32_t live_rows) {
+  if (tokens < 1) return 0;
+  const uint64_t one = bytes_model(d, live_rows, false, false);
+  if (one == 0) return 0;
+  // per (row, head): the state and conv-state traffic once, the per-token
+  // inputs and outputs T times; per call: the weights once
+  const uint64_t H = d->num_heads, D = d->head_dim;
+  const bool norm = (d->flags & KDA_OUTPUT_NORM) != 0;
+  const uint64_t per_token_unit = 3 * D * 2 + D * 4 + 4 + D * 2 +
+                                  (norm ? D * 2 : 0);
+  const uint64_t live = static_cast<uint64_t>(live_rows) * H;
+  const uint64_t null_units = static_cast<uint64_t>(d->batch - live_rows) * H;
+  const uint64_t extra = static_cast<uint64_t>(tokens - 1) *
+                         (live * per_token_unit + null_units * D * 2);
+  return one + extra;
 }
 
 const char* kda_status_string(kda_status s) {

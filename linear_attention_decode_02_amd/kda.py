@@ -64,6 +64,12 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_raw_gates.restype = ctypes.c_int
         L.kda_decode_raw_gates.argtypes = (
             [ctypes.POINTER(Dims)] + [P] * 9 + [ctypes.c_float] + [P] * 5)
+        L.kda_decode_tokens.restype = ctypes.c_int
+        L.kda_decode_tokens.argtypes = ([ctypes.POINTER(Dims), ctypes.c_int32]
+                                        + [P] * 11)
+        L.kda_decode_tokens_bytes.restype = ctypes.c_uint64
+        L.kda_decode_tokens_bytes.argtypes = [ctypes.POINTER(Dims),
+                                              ctypes.c_int32, ctypes.c_int32]
         L.kda_decode_bytes.restype = ctypes.c_uint64
         L.kda_decode_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
         L.kda_decode_raw_gates_bytes.restype = ctypes.c_uint64
@@ -199,6 +205,56 @@ def kda_decode_raw_gates(qkv, conv_w, conv_bias, conv_state, rec_state, raw_g,
             _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
     if rc != KDA_OK:
         raise KdaError(rc, status_string(rc))
+
+
+def kda_decode_tokens(qkv, conv_w, conv_state, rec_state, g, beta, gate,
+                      norm_w, state_idx, out, *, norm: bool = True,
+                      eps: float = 1e-5, variants: int = 0,
+                      stream=None) -> None:
+    """T decode tokens per row in one call (= T successive kda_decode).
+
+    qkv bf16 [B, T, 3C]; g fp32 [B, T, H, 128]; beta fp32 [B, T, H]; gate
+    bf16 [B, T, C]; out bf16 [B, T, C]; other arguments as kda_decode.
+    """
+    if qkv.dim() != 3:
+        raise ValueError("qkv must be [B, T, 3C]")
+    B, T = qkv.shape[0], qkv.shape[1]
+    if rec_state.dim() != 4:
+        raise ValueError("rec_state must be [num_slots, H, 128, 128]")
+    S, H, D, D2 = rec_state.shape
+    C = H * D
+    _check(rec_state, "rec_state", torch.float32, (S, H, D, D2))
+    _check(qkv, "qkv", torch.bfloat16, (B, T, 3 * C))
+    _check(conv_w, "conv_w", torch.float32, (3, CONV_WIDTH, C))
+    cs_shape = ((S, CONV_WIDTH - 1, 3 * C) if variants & KDA_CONV_TAP_MAJOR
+                else (S, 3 * C, CONV_WIDTH - 1))
+    _check(conv_state, "conv_state", torch.bfloat16, cs_shape)
+    _check(state_idx, "state_idx", torch.int32, (B,))
+    _check(out, "out", torch.bfloat16, (B, T, C))
+    _check(g, "g", torch.float32, (B, T, H, D))
+    _check(beta, "beta", torch.float32, (B, T, H))
+    if norm:
+        _check(gate, "gate", torch.bfloat16, (B, T, C))
+        _check(norm_w, "norm_w", torch.float32, (D,))
+    dims = Dims(B, H, D, CONV_WIDTH, S,
+                (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
+    with torch.cuda.device(qkv.device):
+        rc = lib().kda_decode_tokens(
+            ctypes.byref(dims), int(T), _ptr(qkv), _ptr(conv_w),
+            _ptr(conv_state), _ptr(rec_state), _ptr(g), _ptr(beta),
+            _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
+            _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+
+
+def decode_tokens_bytes(batch: int, heads: int, tokens: int, live_rows: int,
+                        norm: bool = True, variants: int = 0) -> int:
+    """Algorithmic HBM bytes of one kda_decode_tokens call."""
+    d = Dims(batch, heads, HEAD_DIM, CONV_WIDTH, 1,
+             (KDA_OUTPUT_NORM if norm else 0) | int(variants), 1e-5)
+    return int(lib().kda_decode_tokens_bytes(ctypes.byref(d), int(tokens),
+                                             int(live_rows)))
 
 
 def decode_bytes(batch: int, heads: int, live_rows: int, norm: bool = True,

@@ -181,6 +181,20 @@ def make_inputs(w: Workload, layer: int = 0, pools: bool = True) -> dict:
     }
 
 
+def make_tokens(w: Workload, tokens: int, layer: int = 0) -> dict:
+    """Inputs of a T-token call: the pools and weights of make_inputs plus
+    per-token qkv [B, T, 3C], g [B, T, H, D], beta [B, T, H], gate
+    [B, T, C] (token 0 is make_inputs' token, then make_token draws)."""
+    inp = make_inputs(w, layer)
+    rng = inp.pop("rng")
+    toks = [{k: inp[k] for k in ("qkv", "g", "beta", "gate")}]
+    for _ in range(tokens - 1):
+        toks.append(make_token(w, rng))
+    for k in ("qkv", "g", "beta", "gate"):
+        inp[k] = np.ascontiguousarray(np.stack([t[k] for t in toks], axis=1))
+    return inp
+
+
 def small(name: str, batch: int, heads: int, num_slots: int, seed: int,
           **kw) -> Workload:
     """A test-sized workload with the reference distributions."""

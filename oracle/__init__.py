@@ -265,3 +265,35 @@ def decode(inp: dict, *, heads: int, head_dim: int = 128, conv_width: int = 4,
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (status {rc})")
     return {"out": out, "y": y, "conv_state": cs, "rec_state": rs}
+
+
+def decode_tokens(inp: dict, *, heads: int, tokens: int, head_dim: int = 128,
+                  conv_width: int = 4, norm: bool = True, eps: float = 1e-5,
+                  dtype: str = "f32", nthreads: int | None = None,
+                  flags: int = 0, inplace: bool = False) -> dict:
+    """T tokens per row: by definition T successive single-token calls on
+    the same slots.  Token-major inputs: qkv [B, T, 3C], g [B, T, H, D],
+    beta [B, T, H], gate [B, T, C]; returns out/y [B, T, C] and the pools
+    after the last token (updated in place with ``inplace``, else copied)."""
+    F = _f(dtype)
+    if inplace:
+        cs, rs = inp["conv_state"], inp["rec_state"]
+    else:
+        cs = np.array(inp["conv_state"], dtype=np.uint16, order="C", copy=True)
+        rs = np.array(inp["rec_state"], dtype=F, order="C", copy=True)
+    B = inp["qkv"].shape[0]
+    C = heads * head_dim
+    assert inp["qkv"].shape == (B, tokens, 3 * C)
+    out = np.empty((B, tokens, C), np.uint16)
+    y = np.empty((B, tokens, C), F)
+    for t in range(tokens):
+        step = dict(inp, conv_state=cs, rec_state=rs,
+                    qkv=np.ascontiguousarray(inp["qkv"][:, t]),
+                    g=np.ascontiguousarray(inp["g"][:, t]),
+                    beta=np.ascontiguousarray(inp["beta"][:, t]),
+                    gate=np.ascontiguousarray(inp["gate"][:, t]))
+        r = decode(step, heads=heads, head_dim=head_dim,
+                   conv_width=conv_width, norm=norm, eps=eps, dtype=dtype,
+                   nthreads=nthreads, inplace=True, flags=flags)
+        out[:, t], y[:, t] = r["out"], r["y"]
+    return {"out": out, "y": y, "conv_state": cs, "rec_state": rs}

@@ -215,3 +215,20 @@ def test_hand_worked_example(oracle_mod):
         synth.to_bf16_bits(np.array([c["window"]], np.float32)))
     np.testing.assert_allclose(yc, [c["y"]], rtol=1e-14)
     assert np.array_equal(bits_to_f64(cs[0]), c["window_new"])
+
+
+def test_tokens_equal_successive_calls(oracle_mod):
+    """decode_tokens is T successive single-token calls (its definition)."""
+    w = synth.small("tok", batch=5, heads=12, num_slots=9, seed=21,
+                    null_every=4)
+    inp = synth.make_tokens(w, 3)
+    got = oracle_mod.decode_tokens(inp, heads=12, tokens=3)
+    cs, rs = inp["conv_state"].copy(), inp["rec_state"].copy()
+    for t in range(3):
+        step = dict(inp, conv_state=cs, rec_state=rs,
+                    **{k: np.ascontiguousarray(inp[k][:, t])
+                       for k in ("qkv", "g", "beta", "gate")})
+        r = run(oracle_mod, w, step, dtype="f32", inplace=True)
+        assert np.array_equal(got["out"][:, t], r["out"])
+    assert np.array_equal(got["rec_state"], rs)
+    assert np.array_equal(got["conv_state"], cs)
