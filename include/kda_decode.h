@@ -178,6 +178,47 @@ kda_status kda_decode_tokens(const kda_dims* dims, int32_t tokens,
                              const float* norm_w, const int32_t* state_idx,
                              void* out, void* hip_stream);
 
+/*
+ * Variable-length prefill: dims->batch = N sequences; sequence n covers
+ * tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 (device int32 [N+1],
+ * non-decreasing; a decreasing pair counts as empty) of token-major
+ * buffers qkv bf16 [tokens, 3C], g fp32 [tokens, H, D], beta fp32
+ * [tokens, H], gate bf16 [tokens, C], out bf16 [tokens, C], and slot
+ * state_idx[n].  The result is the single-token step applied to each
+ * sequence's tokens in order, from the state held in its slot (the state
+ * tile stays on chip across the sequence).  Empty sequences and rows of the
+ * null slot leave every state untouched (null rows write +0.0 outputs).
+ * The prefill is the workload of the page "PR #51862 完整报告 -- Remove
+ * prefill pipeline stall in chunk KDA" (chunked there; its chunk
+ * algorithm is not on the page).  Flags as kda_decode_tokens; status codes
+ * as kda_decode (cu_seqlens NULL: INVALID_ARG).
+ */
+kda_status kda_prefill(const kda_dims* dims, const int32_t* cu_seqlens,
+                       const void* qkv, const float* conv_w, void* conv_state,
+                       float* rec_state, const float* g, const float* beta,
+                       const void* gate, const float* norm_w,
+                       const int32_t* state_idx, void* out, void* hip_stream);
+
+/*
+ * Device-side chunk bookkeeping of a variable-length batch (page "PR
+ * #51862 完整报告", implementation item 2 and the kda_metadata.py excerpt):
+ * sequence i of cu_seqlens (device int32 [num_seqs + 1]) gets
+ * nt_i = ceil(len_i / chunk_size) chunks (a negative length counts as
+ * empty); chunk_offsets (int64 [num_seqs + 1]) receives the first chunk row
+ * of every sequence and the total; chunk_indices (int32 [total, 2])
+ * receives (i, c) for c < nt_i in sequence order.  No host synchronisation:
+ * size chunk_indices with kda_chunk_count on a host copy of cu_seqlens.
+ * Errors: num_seqs < 0, chunk_size < 1 or a null pointer: INVALID_ARG;
+ * MISALIGNED (16 bytes), DEVICE, LAUNCH as kda_decode.
+ */
+kda_status kda_chunk_metadata(const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t chunk_size, int32_t* chunk_indices,
+                              int64_t* chunk_offsets, void* hip_stream);
+
+/* Host helper: total chunk count of a host cu_seqlens (-1 on bad input). */
+int64_t kda_chunk_count(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                        int32_t chunk_size);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(kda_status status);
 

@@ -80,6 +80,7 @@ struct Params {
   const float* A_log;       // [H]
   const float* dt_bias;     // [C]
   float lower_bound;
+  const int32_t* cu_seqlens;  // prefill: token range of each row (or null)
   uint32_t flags;
   int32_t heads;
   int32_t num_slots;
@@ -474,16 +475,18 @@ void kda_decode_kernel(Params p) {
                                         8 * col4));
 }
 
-// T decode tokens per row in one launch, equal to T successive single-token
+// Several tokens per row in one launch, equal to successive single-token
 // steps on the same slots: the state tile is read once, kept in VGPRs
-// across the tokens and written once, the conv window advances in
-// registers.  Buffers carry a token axis after the row axis (qkv [B, T, 3C],
-// g [B, T, H, D], beta [B, T, H], gate and out [B, T, C]).  Three barriers
-// per token; the next token's small inputs are fetched while the current
-// one is processed.
+// across the tokens and written once, the conv window advances in LDS.
+// Token-major buffers (qkv [tokens, 3C], g [tokens, H, D], beta
+// [tokens, H], gate and out [tokens, C]); row n covers tokens
+// n*T_fixed .. +T_fixed-1, or cu_seqlens[n] .. cu_seqlens[n+1]-1 when
+// p.cu_seqlens is set (variable-length prefill).  Three barriers per
+// token; the next token's small inputs are fetched while the current one
+// is processed.
 template <bool kNorm>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void kda_decode_tokens_kernel(Params p, int T) {
+void kda_decode_tokens_kernel(Params p, int T_fixed) {
   __shared__ Lds L;
   __shared__ f2 s_w[3][kW][kD / 2];   // conv taps, per part and lane
   __shared__ float s_norm_w[kD];
@@ -501,7 +504,17 @@ void kda_decode_tokens_kernel(Params p, int T) {
   const int n = unit / H;
   const int h = unit - n * H;
   const int C = H * kD;
-  const int64_t row_tok = static_cast<int64_t>(n) * T;  // first (row, token)
+  int64_t row_tok;  // first token of the row
+  int T;            // tokens of the row
+  if (p.cu_seqlens) {
+    const int32_t bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+    row_tok = bos;
+    T = eos > bos ? eos - bos : 0;
+    if (T == 0) return;  // empty sequence: no output, state untouched
+  } else {
+    row_tok = static_cast<int64_t>(n) * T_fixed;
+    T = T_fixed;
+  }
 
   const int32_t slot = p.state_idx[n];
   if (slot <= 0 || slot >= p.num_slots) {
@@ -653,6 +666,53 @@ void kda_decode_tokens_kernel(Params p, int T) {
     *at_bytes<uint32_t>(cs_g, 4 * (cs_off + cs_step)) = s_win[1][wave][lane];
     *at_bytes<uint32_t>(cs_g, 4 * (cs_off + 2 * cs_step)) =
         s_win[2][wave][lane];
+  }
+}
+
+// Chunk bookkeeping of a variable-length batch: one workgroup per sequence
+// i computes its chunk count nt_i = ceil(len_i / BT) (a negative length
+// counts as empty), its first chunk row base_i = sum_{j<i} nt_j (a
+// workgroup reduction over the earlier sequences), writes
+// chunk_offsets[i] = base_i (workgroup 0 also the total at [N]) and the
+// rows (i, c) for c < nt_i at chunk_indices[base_i + c].
+constexpr int kMetaThreads = 256;
+
+__device__ __forceinline__ int64_t chunks_of(const int32_t* cu, int j,
+                                             int bt) {
+  const int64_t len = static_cast<int64_t>(cu[j + 1]) - cu[j];
+  return len > 0 ? (len + bt - 1) / bt : 0;
+}
+
+__global__ __launch_bounds__(kMetaThreads) void chunk_metadata_kernel(
+    const int32_t* cu, int n_seqs, int bt, int32_t* chunk_indices,
+    int64_t* chunk_offsets) {
+  __shared__ int64_t s_part[kMetaThreads];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  // block 0 sums all sequences (for the total), block i those before i
+  const int upto = i == 0 ? n_seqs : i;
+  int64_t acc = 0, before = 0;
+  for (int j = tid; j < upto; j += kMetaThreads) {
+    const int64_t nt = chunks_of(cu, j, bt);
+    acc += nt;
+    if (j < i) before += nt;
+  }
+  // reduce `before` (and for block 0 the total) over the workgroup
+  s_part[tid] = i == 0 ? acc : before;
+  __syncthreads();
+  for (int w = kMetaThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) s_part[tid] += s_part[tid + w];
+    __syncthreads();
+  }
+  const int64_t base = i == 0 ? 0 : s_part[0];
+  if (tid == 0) {
+    chunk_offsets[i] = base;
+    if (i == 0) chunk_offsets[n_seqs] = s_part[0];
+  }
+  const int64_t nt_i = i < n_seqs ? chunks_of(cu, i, bt) : 0;
+  for (int64_t c = tid; c < nt_i; c += kMetaThreads) {
+    chunk_indices[(base + c) * 2] = i;
+    chunk_indices[(base + c) * 2 + 1] = static_cast<int32_t>(c);
   }
 }
 
@@ -878,6 +938,79 @@ uint64_t kda_decode_tokens_bytes(const kda_dims* d, int32_t tokens,
   const uint64_t extra = static_cast<uint64_t>(tokens - 1) *
                          (live * per_token_unit + null_units * D * 2);
   return one + extra;
+}
+
+kda_status kda_prefill(const kda_dims* d, const int32_t* cu_seqlens,
+                       const void* qkv, const float* conv_w, void* conv_state,
+                       float* rec_state, const float* g, const float* beta,
+                       const void* gate, const float* norm_w,
+                       const int32_t* state_idx, void* out, void* hip_stream) {
+  kda_status st = check_dims(d, kPlainFlags);
+  if (st != KDA_OK) return st;
+  if (d->batch == 0) return KDA_OK;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(cu_seqlens)) return KDA_ERR_MISALIGNED;
+  st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                    state_idx, out);
+  if (st != KDA_OK) return st;
+  if (!g || !beta) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(g) || !aligned16(beta)) return KDA_ERR_MISALIGNED;
+  Params p = base_params(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                         state_idx, out);
+  p.g = g;
+  p.beta = beta;
+  p.cu_seqlens = cu_seqlens;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return KDA_ERR_DEVICE;
+  const dim3 grid(static_cast<unsigned>(d->batch * d->num_heads));
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (d->flags & KDA_OUTPUT_NORM)
+    hipLaunchKernelGGL(kda_decode_tokens_kernel<true>, grid, dim3(kThreads), 0,
+                       stream, p, 0);
+  else
+    hipLaunchKernelGGL(kda_decode_tokens_kernel<false>, grid, dim3(kThreads),
+                       0, stream, p, 0);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_chunk_metadata(const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t chunk_size, int32_t* chunk_indices,
+                              int64_t* chunk_offsets, void* hip_stream) {
+  if (num_seqs < 0 || chunk_size < 1) return KDA_ERR_INVALID_ARG;
+  if (!cu_seqlens || !chunk_offsets) return KDA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && !chunk_indices) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(cu_seqlens) || !aligned16(chunk_offsets) ||
+      (chunk_indices && !aligned16(chunk_indices)))
+    return KDA_ERR_MISALIGNED;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return KDA_ERR_DEVICE;
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (num_seqs == 0) {
+    // chunk_offsets = [0]: a one-workgroup launch with nothing else to do
+    hipLaunchKernelGGL(chunk_metadata_kernel, dim3(1), dim3(kMetaThreads), 0,
+                       stream, cu_seqlens, 0, chunk_size, chunk_indices,
+                       chunk_offsets);
+  } else {
+    hipLaunchKernelGGL(chunk_metadata_kernel,
+                       dim3(static_cast<unsigned>(num_seqs)),
+                       dim3(kMetaThreads), 0, stream, cu_seqlens, num_seqs,
+                       chunk_size, chunk_indices, chunk_offsets);
+  }
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int64_t kda_chunk_count(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                        int32_t chunk_size) {
+  if (!cu_seqlens_host || num_seqs < 0 || chunk_size < 1) return -1;
+  int64_t total = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t len =
+        static_cast<int64_t>(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
+    if (len > 0) total += (len + chunk_size - 1) / chunk_size;
+  }
+  return total;
 }
 
 const char* kda_status_string(kda_status s) {

@@ -70,6 +70,13 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_tokens_bytes.restype = ctypes.c_uint64
         L.kda_decode_tokens_bytes.argtypes = [ctypes.POINTER(Dims),
                                               ctypes.c_int32, ctypes.c_int32]
+        L.kda_prefill.restype = ctypes.c_int
+        L.kda_prefill.argtypes = [ctypes.POINTER(Dims)] + [P] * 12
+        L.kda_chunk_metadata.restype = ctypes.c_int
+        L.kda_chunk_metadata.argtypes = [P, ctypes.c_int32, ctypes.c_int32,
+                                         P, P, P]
+        L.kda_chunk_count.restype = ctypes.c_int64
+        L.kda_chunk_count.argtypes = [P, ctypes.c_int32, ctypes.c_int32]
         L.kda_decode_bytes.restype = ctypes.c_uint64
         L.kda_decode_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
         L.kda_decode_raw_gates_bytes.restype = ctypes.c_uint64
@@ -246,6 +253,69 @@ def kda_decode_tokens(qkv, conv_w, conv_state, rec_state, g, beta, gate,
             _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
     if rc != KDA_OK:
         raise KdaError(rc, status_string(rc))
+
+
+def kda_prefill(cu_seqlens, qkv, conv_w, conv_state, rec_state, g, beta,
+                gate, norm_w, state_idx, out, *, norm: bool = True,
+                eps: float = 1e-5, variants: int = 0, stream=None) -> None:
+    """Variable-length prefill: sequence n covers tokens cu_seqlens[n] ..
+    cu_seqlens[n+1]-1 of token-major qkv [tokens, 3C], g [tokens, H, 128],
+    beta [tokens, H], gate/out [tokens, C]; slot state_idx[n]."""
+    if rec_state.dim() != 4 or qkv.dim() != 2:
+        raise ValueError("rec_state [S, H, 128, 128], qkv [tokens, 3C]")
+    S, H, D, D2 = rec_state.shape
+    C = H * D
+    N = state_idx.shape[0]
+    tokens = qkv.shape[0]
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    _check(rec_state, "rec_state", torch.float32, (S, H, D, D2))
+    _check(qkv, "qkv", torch.bfloat16, (tokens, 3 * C))
+    _check(conv_w, "conv_w", torch.float32, (3, CONV_WIDTH, C))
+    cs_shape = ((S, CONV_WIDTH - 1, 3 * C) if variants & KDA_CONV_TAP_MAJOR
+                else (S, 3 * C, CONV_WIDTH - 1))
+    _check(conv_state, "conv_state", torch.bfloat16, cs_shape)
+    _check(state_idx, "state_idx", torch.int32, (N,))
+    _check(g, "g", torch.float32, (tokens, H, D))
+    _check(beta, "beta", torch.float32, (tokens, H))
+    _check(out, "out", torch.bfloat16, (tokens, C))
+    if norm:
+        _check(gate, "gate", torch.bfloat16, (tokens, C))
+        _check(norm_w, "norm_w", torch.float32, (D,))
+    dims = Dims(N, H, D, CONV_WIDTH, S,
+                (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
+    with torch.cuda.device(qkv.device):
+        rc = lib().kda_prefill(
+            ctypes.byref(dims), _ptr(cu_seqlens), _ptr(qkv), _ptr(conv_w),
+            _ptr(conv_state), _ptr(rec_state), _ptr(g), _ptr(beta),
+            _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
+            _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+
+
+def chunk_metadata(cu_seqlens, chunk_size: int, cu_seqlens_host=None,
+                   stream=None):
+    """(chunk_indices int32 [total, 2], chunk_offsets int64 [N + 1]) of a
+    device cu_seqlens (int32 [N + 1]).  The total is computed on the host
+    from ``cu_seqlens_host`` (a CPU tensor; copied from the device if
+    omitted, which synchronises)."""
+    _check(cu_seqlens, "cu_seqlens", torch.int32, tuple(cu_seqlens.shape))
+    N = cu_seqlens.shape[0] - 1
+    host = (cu_seqlens.cpu() if cu_seqlens_host is None
+            else cu_seqlens_host).to(torch.int32).contiguous()
+    total = int(lib().kda_chunk_count(host.data_ptr(), N, int(chunk_size)))
+    if total < 0:
+        raise ValueError("bad cu_seqlens or chunk_size")
+    dev = cu_seqlens.device
+    indices = torch.empty(max(total, 1), 2, dtype=torch.int32, device=dev)
+    offsets = torch.empty(N + 1, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().kda_chunk_metadata(_ptr(cu_seqlens), N, int(chunk_size),
+                                      _ptr(indices), _ptr(offsets),
+                                      _stream(stream, dev))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+    return indices[:total], offsets
 
 
 def decode_tokens_bytes(batch: int, heads: int, tokens: int, live_rows: int,

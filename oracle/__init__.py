@@ -297,3 +297,69 @@ def decode_tokens(inp: dict, *, heads: int, tokens: int, head_dim: int = 128,
                    nthreads=nthreads, inplace=True, flags=flags)
         out[:, t], y[:, t] = r["out"], r["y"]
     return {"out": out, "y": y, "conv_state": cs, "rec_state": rs}
+
+
+def chunk_metadata(cu_seqlens, chunk_size: int):
+    """Chunk bookkeeping of a variable-length batch (plain numpy).
+
+    Sequence i spans cu_seqlens[i] .. cu_seqlens[i+1]; its chunk count is
+    ceil(len / chunk_size) (a negative length counts as empty).  Returns
+    (chunk_indices int32 [total, 2] holding (sequence, chunk within the
+    sequence) in sequence order, chunk_offsets int64 [N + 1] with the first
+    chunk row of each sequence and the total last).
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    lens = np.maximum(cu[1:] - cu[:-1], 0)
+    nt = (lens + chunk_size - 1) // chunk_size
+    offsets = np.concatenate([[0], np.cumsum(nt)]).astype(np.int64)
+    seq = np.repeat(np.arange(nt.size, dtype=np.int64), nt)
+    within = np.arange(int(offsets[-1]), dtype=np.int64) - np.repeat(
+        offsets[:-1], nt)
+    indices = np.stack([seq, within], axis=1).astype(np.int32)
+    return indices.reshape(-1, 2), offsets
+
+
+def prefill(inp: dict, cu_seqlens, *, heads: int, head_dim: int = 128,
+            conv_width: int = 4, norm: bool = True, eps: float = 1e-5,
+            nthreads: int | None = None, flags: int = 0) -> dict:
+    """Variable-length prefill on host arrays: the tokens of sequence n
+    (cu_seqlens[n] .. cu_seqlens[n+1]-1 of the token-major qkv [tokens, 3C],
+    g [tokens, H, D], beta [tokens, H], gate [tokens, C]) run through the
+    single-token step in order on slot state_idx[n].  fp32."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    N = cu.size - 1
+    C = heads * head_dim
+    qkv = np.ascontiguousarray(inp["qkv"], dtype=np.uint16)
+    tokens = qkv.shape[0]
+    assert qkv.shape == (tokens, 3 * C) and int(cu[-1]) <= tokens
+    cs = np.array(inp["conv_state"], dtype=np.uint16, order="C", copy=True)
+    rs = np.array(inp["rec_state"], dtype=np.float32, order="C", copy=True)
+    S = cs.shape[0]
+    conv_w = np.ascontiguousarray(inp["conv_w"], dtype=np.float32)
+    g = np.ascontiguousarray(inp["g"], dtype=np.float32)
+    beta = np.ascontiguousarray(inp["beta"], dtype=np.float32)
+    gate = np.ascontiguousarray(inp["gate"], dtype=np.uint16)
+    norm_w = np.ascontiguousarray(inp["norm_w"], dtype=np.float32)
+    idx = np.ascontiguousarray(inp["state_idx"], dtype=np.int32)
+    assert g.shape == (tokens, heads, head_dim) and beta.shape == (tokens,
+                                                                   heads)
+    assert idx.shape == (N,)
+    out = np.zeros((tokens, C), np.uint16)
+    y = np.zeros((tokens, C), np.float32)
+    L = lib()
+    if not hasattr(L.kda_oracle_prefill_f32, "_typed"):
+        P = ctypes.c_void_p
+        L.kda_oracle_prefill_f32.restype = ctypes.c_int
+        L.kda_oracle_prefill_f32.argtypes = ([ctypes.POINTER(_Dims)] + [P] * 12
+                                             + [ctypes.c_int])
+        L.kda_oracle_prefill_f32._typed = True
+    assert not flags & (CONV_TAP_MAJOR | BOUNDED_GATE), "not for prefill"
+    d = _Dims(N, heads, head_dim, conv_width, S,
+              (NORM if norm else 0) | (flags & ~NORM), eps)
+    rc = L.kda_oracle_prefill_f32(
+        ctypes.byref(d), _ptr(cu), _ptr(qkv), _ptr(conv_w), _ptr(cs), _ptr(rs),
+        _ptr(g), _ptr(beta), _ptr(gate), _ptr(norm_w), _ptr(idx), _ptr(out),
+        _ptr(y), int(nthreads or os.cpu_count() or 1))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (status {rc})")
+    return {"out": out, "y": y, "conv_state": cs, "rec_state": rs}

@@ -324,6 +324,42 @@ int decode(const Dims* d, const uint16_t* qkv, const float* conv_w,
   return ORC_OK;
 }
 
+// ---- variable-length prefill: each sequence's tokens in order -------------
+// Sequence n covers tokens cu[n] .. cu[n+1]-1 of the token-major inputs
+// (qkv [tokens, 3C], g [tokens, H, D], beta [tokens, H], gate [tokens, C],
+// out [tokens, C]) and uses slot state_idx[n]; the result is that of one
+// single-token step per token, in order.  Sequences are independent.
+template <typename T>
+int prefill(const Dims* d, const int32_t* cu, const uint16_t* qkv,
+            const float* conv_w, uint16_t* conv_state, T* rec_state,
+            const float* g, const float* beta, const uint16_t* gate,
+            const float* norm_w, const int32_t* state_idx, uint16_t* out,
+            T* y_out, int nthreads) {
+  if (!d || d->batch < 0 || !cu) return ORC_ERR_INVALID_ARG;
+  const int64_t N = d->batch;
+  const int64_t H = d->num_heads, D = d->head_dim;
+  const int64_t C = H * D;
+  for (int64_t n = 0; n < N; ++n) {
+    if (cu[n + 1] < cu[n]) return ORC_ERR_INVALID_ARG;
+    const int64_t len = cu[n + 1] - cu[n];
+    if (len == 0) continue;
+    const int32_t slot = state_idx[n];
+    for (int64_t t = 0; t < len; ++t) {
+      const int64_t tok = cu[n] + t;
+      Dims one = *d;
+      one.batch = 1;
+      const int rc = decode<T>(
+          &one, qkv + tok * 3 * C, conv_w, conv_state, rec_state,
+          g + tok * H * D, beta + tok * H,
+          (d->flags & F_NORM) ? gate + tok * C : nullptr, norm_w, &slot,
+          out + tok * C, y_out ? y_out + tok * C : nullptr, nthreads,
+          nullptr);
+      if (rc != ORC_OK) return rc;
+    }
+  }
+  return ORC_OK;
+}
+
 }  // namespace
 
 // ---- exported C entry points (host pointers) -------------------------------
@@ -396,6 +432,20 @@ int kda_oracle_decode_ext_f64(const kda_oracle_dims* d, const uint16_t* qkv,
                         conv_state, rec_state, g, beta, gate, norm_w,
                         state_idx, out, y_out, nthreads,
                         reinterpret_cast<const Extras*>(ex));
+}
+
+// Variable-length prefill (see prefill() above); dims->batch = number of
+// sequences, cu_seqlens [batch + 1] token offsets (non-decreasing).
+int kda_oracle_prefill_f32(const kda_oracle_dims* d, const int32_t* cu_seqlens,
+                           const uint16_t* qkv, const float* conv_w,
+                           uint16_t* conv_state, float* rec_state,
+                           const float* g, const float* beta,
+                           const uint16_t* gate, const float* norm_w,
+                           const int32_t* state_idx, uint16_t* out,
+                           float* y_out, int nthreads) {
+  return prefill<float>(reinterpret_cast<const Dims*>(d), cu_seqlens, qkv,
+                        conv_w, conv_state, rec_state, g, beta, gate, norm_w,
+                        state_idx, out, y_out, nthreads);
 }
 
 // Stage 1 over nch channels: channel c has W-1 stored inputs, tap t at

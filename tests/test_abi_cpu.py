@@ -184,3 +184,38 @@ def test_byte_model_variants():
     assert raw == base - B * H * (256 + 2) + H * 4 + H * 128 * 4
     assert kda.decode_bytes(B, H, B, raw_gates=True, conv_bias=True) == \
         raw + 3 * H * 128 * 4
+
+
+def test_chunk_count_host_helper():
+    import numpy as np
+    import oracle
+    for lens, bt in (([5, 0, 65, 130], 64), ([], 64), ([0, 0], 1),
+                     ([1000, 3, 4097], 16)):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        got = kda.lib().kda_chunk_count(cu.ctypes.data, len(lens), bt)
+        idx, off = oracle.chunk_metadata(cu, bt)
+        assert got == idx.shape[0] == off[-1]
+    cu = np.array([0, 10], np.int32)
+    assert kda.lib().kda_chunk_count(cu.ctypes.data, 1, 0) == -1
+    assert kda.lib().kda_chunk_count(None, 1, 64) == -1
+
+
+@no_gpu
+def test_prefill_and_metadata_argument_checks():
+    L = kda.lib()
+    d = dims()
+    p = [FAKE] * 12   # cu, qkv, conv_w, cs, rs, g, beta, gate, norm_w, idx, out
+    assert L.kda_prefill(ctypes.byref(d), *p[:11], None) == 4
+    q = list(p)
+    q[0] = None
+    assert L.kda_prefill(ctypes.byref(d), *q[:11], None) == 1
+    q[0] = FAKE + 4
+    assert L.kda_prefill(ctypes.byref(d), *q[:11], None) == 3
+    assert L.kda_prefill(ctypes.byref(dims(flags=0x21)), *p[:11], None) == 1
+    assert L.kda_chunk_metadata(FAKE, 3, 64, FAKE, FAKE, None) == 4
+    assert L.kda_chunk_metadata(FAKE, -1, 64, FAKE, FAKE, None) == 1
+    assert L.kda_chunk_metadata(FAKE, 3, 0, FAKE, FAKE, None) == 1
+    assert L.kda_chunk_metadata(None, 3, 64, FAKE, FAKE, None) == 1
+    assert L.kda_chunk_metadata(FAKE, 3, 64, None, FAKE, None) == 1
+    assert L.kda_chunk_metadata(FAKE, 0, 64, None, FAKE, None) == 4
+    assert L.kda_chunk_metadata(FAKE, 3, 64, FAKE + 8, FAKE, None) == 3
