@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--workload", default="b256_h48_pool512_null32")
     ap.add_argument("--variant", default="plain", choices=sorted(VARIANTS),
                     help="kernel variant (default: the plain step)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure the variable-length prefill instead "
+                         "(16 sequences, 48 heads, L2-normalised q/k)")
     ap.add_argument("--tokens", type=int, default=1,
                     help="decode tokens per row and call (> 1: the "
                          "multi-token entry point, state kept on chip)")
@@ -103,6 +106,9 @@ def main():
     import torch
 
     from linear_attention_decode_02_amd import kda, synth
+
+    if args.prefill:
+        return bench_prefill(args, np, torch, kda, synth)
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -235,6 +241,9 @@ def main():
 
     if not args.no_copy_probe:
         extra["copy_probe"] = copy_probe(torch, stream)
+        if args.variant == "plain" and T == 1:
+            extra["stream_ceiling"] = stream_ceiling(
+                torch, kda, stream, w, live_rows, alg_bytes, kern_avg_s)
 
     traffic = (recorded_traffic(w.name)
                if args.variant == "plain" and T == 1 else None)
@@ -265,6 +274,119 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_prefill(args, np, torch, kda, synth):
+    """Variable-length prefill: 16 sequences with seeded lengths (1..4096,
+    log-uniform), 48 heads, q/k L2-normalised, fresh states.  A step is one
+    kda_prefill call over the batch (the chunk metadata kernel is timed
+    beside it)."""
+    import oracle
+
+    H, N = 48, 16
+    rng = np.random.default_rng(7)
+    lens = np.exp(rng.uniform(0, np.log(4096), N)).astype(np.int64) + 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    w = synth.small("prefill_16seq_h48", batch=total, heads=H,
+                    num_slots=N + 1, seed=7)
+    base = synth.make_inputs(synth.small("pf", batch=1, heads=H,
+                                         num_slots=N + 1, seed=7))
+    rng_t = base.pop("rng")
+    tok = synth.make_token(w, rng_t)
+    inp = dict(base, **tok)
+    inp["state_idx"] = np.arange(1, N + 1, dtype=np.int32)
+    inp["rec_state"][:] = 0
+    dev = torch.device("cuda:0")
+    t = synth.to_torch(inp, dev)
+    cu_d = torch.from_numpy(cu).to(dev)
+    out = torch.empty(total, w.channels, dtype=torch.bfloat16, device=dev)
+    flags = kda.KDA_QK_L2NORM
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.kda_prefill(cu_d, t["qkv"], t["conv_w"], t["conv_state"],
+                        t["rec_state"], t["g"], t["beta"], t["gate"],
+                        t["norm_w"], t["state_idx"], out, eps=w.eps,
+                        variants=flags, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = e0.elapsed_time(e1) * 1e-3 / K
+    updates = total * H
+    # bytes: state once per (sequence, head) in + out, conv state, and per
+    # token the inputs and outputs
+    per_tok = (3 * 128 * 2 + 128 * 4 + 4 + 128 * 2 + 128 * 2) * H
+    nbytes = N * H * (2 * 128 * 128 * 4 + 2 * 2304) + total * per_tok
+    # chunk metadata beside it
+    host = torch.from_numpy(cu)
+    kda.chunk_metadata(cu_d, 64, cu_seqlens_host=host)
+    torch.cuda.synchronize()
+    m0 = torch.cuda.Event(enable_timing=True)
+    m1 = torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for _ in range(100):
+        kda.chunk_metadata(cu_d, 64, cu_seqlens_host=host, stream=stream)
+    m1.record(stream)
+    torch.cuda.synchronize()
+    meta_us = m0.elapsed_time(m1) * 1e3 / 100
+    cpu = None
+    if args.cpu_seconds > 0:
+        cores = min(os.cpu_count() or 1,
+                    int(os.environ.get("OMP_NUM_THREADS", "0")) or 16, 16)
+        # a bounded sample: the 4 shortest sequences, repeated
+        order = np.argsort(lens)[:4]
+        sub_lens = lens[order]
+        sub_cu = np.concatenate([[0], np.cumsum(sub_lens)]).astype(np.int32)
+        sel = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order])
+        sub = dict(inp, state_idx=inp["state_idx"][order].copy())
+        for k in ("qkv", "g", "beta", "gate"):
+            sub[k] = np.ascontiguousarray(inp[k][sel])
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            oracle.prefill(sub, sub_cu, heads=H, eps=w.eps, nthreads=cores,
+                           flags=0x08)
+            reps += 1
+            el = time.perf_counter() - c0
+            if el >= args.cpu_seconds:
+                break
+        cpu = {"value": round(int(sub_lens.sum()) * H * reps / el, 1),
+               "unit": "token-head updates/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"4 shortest sequences ({int(sub_lens.sum())} "
+                         f"tokens) x {reps} calls, {el:.1f} s"}
+    line = {
+        "metric": "KDA prefill token-head updates/sec (variable length)",
+        "value": round(updates * K / wall, 1), "unit": "updates/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill_16seq_h48", "sequences": N,
+                   "tokens": total, "lengths": lens.tolist(), "heads": H,
+                   "qk_l2norm": True, "parallelism": "single-gpu"},
+        "roofline": {"bound": "latency", "achieved": round(nbytes / kern / 1e9,
+                                                           1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / kern / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": {"kernel_us": round(kern * 1e6, 2),
+                  "chunk_metadata_us": round(meta_us, 2),
+                  "us_per_token": round(kern * 1e6 / max(lens.max(), 1), 3)},
     }
     print(json.dumps(line), flush=True)
 
@@ -307,6 +429,45 @@ def copy_probe(torch, stream, nbytes=1 << 30, reps=10):
     return {"bytes_read": nbytes, "bytes_written": nbytes,
             "us_per_copy": round(sec * 1e6, 2),
             "GBs": round(2 * nbytes / sec / 1e9, 1)}
+
+
+def stream_ceiling(torch, kda, stream, w, live_rows, alg_bytes, kern_s,
+                   reps=10):
+    """What HBM delivers to this access pattern when reads and writes run
+    alone: the state-tile probe in read-only and in write-only mode over as
+    many [128, 128] fp32 tiles as the call has live units, and the time the
+    call's own reads and writes would take one after the other at those
+    rates (small reads priced at the read rate, conv-state and output
+    writes at the write rate).  A kernel that overlaps its reads with its
+    writes can beat that serial time; the ratio says how far it does."""
+    D = 128
+    live_units = live_rows * w.heads
+    null_units = (w.batch - live_rows) * w.heads
+    conv_state = 3 * D * (w.conv_width - 1) * 2
+    wbytes = live_units * (D * D * 4 + conv_state + D * 2) + null_units * D * 2
+    rbytes = alg_bytes - wbytes
+    tiles = torch.randn(live_units, D, D, dtype=torch.float32, device="cuda:0")
+    rates = {}
+    for name, mode in (("read", kda.PROBE_READ), ("write", kda.PROBE_WRITE)):
+        for _ in range(3):
+            kda.state_stream_probe(tiles, 16, mode=mode, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            kda.state_stream_probe(tiles, 16, mode=mode, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        rates[name] = tiles.numel() * 4 / sec / 1e9
+    del tiles
+    bound = rbytes / (rates["read"] * 1e9) + wbytes / (rates["write"] * 1e9)
+    return {"read_GBs": round(rates["read"], 1),
+            "write_GBs": round(rates["write"], 1),
+            "call_bytes_read": int(rbytes), "call_bytes_written": int(wbytes),
+            "serial_us": round(bound * 1e6, 2),
+            "serial_over_kernel": round(bound / kern_s, 4)}
 
 
 def cpu_baseline(w, inp, seconds, alg_bytes, units, flags=0, tokens=1):

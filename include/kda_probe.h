@@ -24,16 +24,19 @@ extern "C" {
 #endif
 
 /*
- * tiles: device pointer, 16-byte aligned, n_tiles * 128 * 128 fp32 values,
- * read and overwritten in place with value * scale (scale = 1 keeps them).
+ * tiles: device pointer, 16-byte aligned, n_tiles * 128 * 128 fp32 values.
+ * mode 0: each tile is read and written back in place as value * scale
+ *         (scale = 1 keeps the values): the decode kernel's traffic;
+ * mode 1: read only (values are left as they are): the read ceiling;
+ * mode 2: write only, every value set to scale: the write ceiling.
  * waves: workgroup size in waves, one of 4, 8, 16.  Queued on hip_stream;
  * no allocation, no synchronisation.  Returns KDA_ERR_INVALID_ARG for a
- * null pointer, n_tiles < 0 or > INT32_MAX, or another wave count;
- * KDA_ERR_MISALIGNED, KDA_ERR_DEVICE and KDA_ERR_LAUNCH as kda_decode.
- * n_tiles = 0 queues nothing.
+ * null pointer, n_tiles < 0 or > INT32_MAX, another wave count or mode, a
+ * non-finite scale; KDA_ERR_MISALIGNED, KDA_ERR_DEVICE and KDA_ERR_LAUNCH
+ * as kda_decode.  n_tiles = 0 queues nothing.
  */
 kda_status kda_state_stream_probe(float* tiles, int64_t n_tiles, int32_t waves,
-                                  float scale, void* hip_stream);
+                                  int32_t mode, float scale, void* hip_stream);
 
 #ifdef __cplusplus
 }

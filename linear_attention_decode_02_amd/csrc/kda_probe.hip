@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -13,7 +14,9 @@ namespace {
 constexpr int kD = 128;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int kWaves>
+// mode 0: read every float4 and write it back times `scale`; mode 1: read
+// only; mode 2: write only.
+template <int kWaves, int kMode>
 __global__ __launch_bounds__(64 * kWaves) void state_stream_kernel(
     float* tiles, float scale) {
   constexpr int kThreads = 64 * kWaves;
@@ -24,15 +27,47 @@ __global__ __launch_bounds__(64 * kWaves) void state_stream_kernel(
   const int rgrp = tid >> 5;
   f4* st = reinterpret_cast<f4*>(tiles + static_cast<int64_t>(blockIdx.x) *
                                              (kD * kD));
+  if (kMode == 2) {
+    const f4 v = {scale, scale, scale, scale};
+#pragma unroll
+    for (int m = 0; m < kRows; ++m)
+      __builtin_nontemporal_store(v, st + (rgrp + kStride * m) * (kD / 4) +
+                                         col4);
+    return;
+  }
   f4 s[kRows];
 #pragma unroll
   for (int m = 0; m < kRows; ++m)
     s[m] = __builtin_nontemporal_load(st + (rgrp + kStride * m) * (kD / 4) +
                                       col4);
+  if (kMode == 1) {
+    f4 acc = s[0];
+#pragma unroll
+    for (int m = 1; m < kRows; ++m) acc += s[m];
+    // keeps the loads: on the rare tile whose sum equals scale, the first
+    // float4 is written back unchanged
+    if (acc.x + acc.y + acc.z + acc.w == scale)
+      st[rgrp * (kD / 4) + col4] = s[0];
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < kRows; ++m)
     __builtin_nontemporal_store(s[m] * scale,
                                 st + (rgrp + kStride * m) * (kD / 4) + col4);
+}
+
+template <int kWaves>
+void launch_probe(int mode, dim3 grid, hipStream_t s, float* tiles,
+                  float scale) {
+  if (mode == 0)
+    hipLaunchKernelGGL((state_stream_kernel<kWaves, 0>), grid,
+                       dim3(64 * kWaves), 0, s, tiles, scale);
+  else if (mode == 1)
+    hipLaunchKernelGGL((state_stream_kernel<kWaves, 1>), grid,
+                       dim3(64 * kWaves), 0, s, tiles, scale);
+  else
+    hipLaunchKernelGGL((state_stream_kernel<kWaves, 2>), grid,
+                       dim3(64 * kWaves), 0, s, tiles, scale);
 }
 
 bool is_gfx950(int dev) {
@@ -44,10 +79,11 @@ bool is_gfx950(int dev) {
 }  // namespace
 
 extern "C" kda_status kda_state_stream_probe(float* tiles, int64_t n_tiles,
-                                             int32_t waves, float scale,
-                                             void* hip_stream) {
+                                             int32_t waves, int32_t mode,
+                                             float scale, void* hip_stream) {
   if (!tiles || n_tiles < 0 || n_tiles > INT32_MAX ||
-      (waves != 4 && waves != 8 && waves != 16))
+      (waves != 4 && waves != 8 && waves != 16) || mode < 0 || mode > 2 ||
+      !std::isfinite(scale))
     return KDA_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(tiles) & 15u) return KDA_ERR_MISALIGNED;
   if (n_tiles == 0) return KDA_OK;
@@ -57,13 +93,10 @@ extern "C" kda_status kda_state_stream_probe(float* tiles, int64_t n_tiles,
   const dim3 grid(static_cast<unsigned>(n_tiles));
   const hipStream_t s = static_cast<hipStream_t>(hip_stream);
   if (waves == 4)
-    hipLaunchKernelGGL(state_stream_kernel<4>, grid, dim3(256), 0, s, tiles,
-                       scale);
+    launch_probe<4>(mode, grid, s, tiles, scale);
   else if (waves == 8)
-    hipLaunchKernelGGL(state_stream_kernel<8>, grid, dim3(512), 0, s, tiles,
-                       scale);
+    launch_probe<8>(mode, grid, s, tiles, scale);
   else
-    hipLaunchKernelGGL(state_stream_kernel<16>, grid, dim3(1024), 0, s, tiles,
-                       scale);
+    launch_probe<16>(mode, grid, s, tiles, scale);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -84,7 +84,7 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.c_int32, ctypes.c_int32]
         L.kda_state_stream_probe.restype = ctypes.c_int
         L.kda_state_stream_probe.argtypes = [P, ctypes.c_int64, ctypes.c_int32,
-                                             ctypes.c_float, P]
+                                             ctypes.c_int32, ctypes.c_float, P]
         _lib = L
     return _lib
 
@@ -340,18 +340,23 @@ def decode_bytes(batch: int, heads: int, live_rows: int, norm: bool = True,
     return int(lib().kda_decode_bytes(ctypes.byref(d), int(live_rows)))
 
 
-def state_stream_probe(tiles: torch.Tensor, waves: int = 8,
-                       scale: float = 1.0, stream=None) -> None:
-    """Read and rewrite (times ``scale``) every [128, 128] fp32 tile of
-    ``tiles`` in place with the decode kernel's access pattern: the
-    bandwidth ceiling of the state stream (include/kda_probe.h)."""
+PROBE_RMW, PROBE_READ, PROBE_WRITE = 0, 1, 2
+
+
+def state_stream_probe(tiles: torch.Tensor, waves: int = 16,
+                       scale: float = 1.0, mode: int = PROBE_RMW,
+                       stream=None) -> None:
+    """Stream every [128, 128] fp32 tile of ``tiles`` with the decode
+    kernel's access pattern (include/kda_probe.h): read and rewrite times
+    ``scale`` (PROBE_RMW), read only (PROBE_READ) or write ``scale``
+    everywhere (PROBE_WRITE)."""
     _check(tiles, "tiles", torch.float32, tuple(tiles.shape))
     if tiles.dim() < 2 or tuple(tiles.shape[-2:]) != (HEAD_DIM, HEAD_DIM):
         raise ValueError("tiles must be [..., 128, 128]")
     n = tiles.numel() // (HEAD_DIM * HEAD_DIM)
     with torch.cuda.device(tiles.device):
         rc = lib().kda_state_stream_probe(tiles.data_ptr(), n, int(waves),
-                                          float(scale),
+                                          int(mode), float(scale),
                                           _stream(stream, tiles.device))
     if rc != KDA_OK:
         raise KdaError(rc, status_string(rc))

@@ -135,12 +135,14 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 @no_gpu
 def test_probe_argument_checks():
     L = kda.lib()
-    assert L.kda_state_stream_probe(None, 4, 8, 1.0, None) == 1
-    assert L.kda_state_stream_probe(FAKE, -1, 8, 1.0, None) == 1
-    assert L.kda_state_stream_probe(FAKE, 4, 5, 1.0, None) == 1
-    assert L.kda_state_stream_probe(FAKE + 4, 4, 8, 1.0, None) == 3
-    assert L.kda_state_stream_probe(FAKE, 0, 8, 1.0, None) == 0
-    assert L.kda_state_stream_probe(FAKE, 4, 8, 1.0, None) == 4
+    assert L.kda_state_stream_probe(None, 4, 8, 0, 1.0, None) == 1
+    assert L.kda_state_stream_probe(FAKE, -1, 8, 0, 1.0, None) == 1
+    assert L.kda_state_stream_probe(FAKE, 4, 5, 0, 1.0, None) == 1
+    assert L.kda_state_stream_probe(FAKE, 4, 8, 3, 1.0, None) == 1
+    assert L.kda_state_stream_probe(FAKE, 4, 8, 0, float("nan"), None) == 1
+    assert L.kda_state_stream_probe(FAKE + 4, 4, 8, 0, 1.0, None) == 3
+    assert L.kda_state_stream_probe(FAKE, 0, 8, 0, 1.0, None) == 0
+    assert L.kda_state_stream_probe(FAKE, 4, 8, 2, 1.0, None) == 4
 
 
 

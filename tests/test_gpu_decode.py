@@ -321,7 +321,7 @@ def test_sweep_69_layers_in_one_graph():
 
 
 @pytest.mark.parametrize("waves", [4, 8, 16])
-def test_state_stream_probe_rewrites_tiles_in_place(waves):
+def test_state_stream_probe_modes(waves):
     x = torch.randn(37, 128, 128, device=DEV)
     y = x.clone()
     kda.state_stream_probe(y, waves, scale=2.0)
@@ -330,3 +330,9 @@ def test_state_stream_probe_rewrites_tiles_in_place(waves):
     kda.state_stream_probe(y, waves, scale=1.0)
     torch.cuda.synchronize()
     assert torch.equal(y, 2.0 * x)
+    kda.state_stream_probe(y, waves, mode=kda.PROBE_READ)
+    torch.cuda.synchronize()
+    assert torch.equal(y, 2.0 * x)                  # read only
+    kda.state_stream_probe(y, waves, scale=3.0, mode=kda.PROBE_WRITE)
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0)
