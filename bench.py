@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "KDA decode (seq*head) updates/sec + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_02_amd", "csrc",
                           "kda_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
@@ -281,8 +282,9 @@ def main():
 def bench_prefill(args, np, torch, kda, synth):
     """Variable-length prefill: 16 sequences with seeded lengths (1..4096,
     log-uniform), 48 heads, q/k L2-normalised, fresh states.  A step is one
-    kda_prefill call over the batch (the chunk metadata kernel is timed
-    beside it)."""
+    kda_prefill_chunked call over the batch (16-token chunks on the matrix
+    cores); the token-by-token kda_prefill and the chunk metadata kernel
+    are timed beside it."""
     import oracle
 
     H, N = 48, 16
@@ -306,27 +308,38 @@ def bench_prefill(args, np, torch, kda, synth):
     flags = kda.KDA_QK_L2NORM
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(chunked=True):
         kda.kda_prefill(cu_d, t["qkv"], t["conv_w"], t["conv_state"],
                         t["rec_state"], t["g"], t["beta"], t["gate"],
                         t["norm_w"], t["state_idx"], out, eps=w.eps,
-                        variants=flags, stream=stream)
+                        variants=flags, chunked=chunked, stream=stream)
+
+    def timed(k, chunked):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(k):
+            step(chunked)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3 / k
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
     K = args.steps
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(K):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern = e0.elapsed_time(e1) * 1e-3 / K
+    wall, kern = timed(K, True)
+    step(False)
+    _, kern_seq = timed(max(K // 4, 1), False)
     updates = total * H
+    # matrix-core work of the chunked form per (16-token chunk, head): K~S,
+    # Q~S and the state update (3 x 2*16*128*128), the A and B products and
+    # the solve / B Delta products (4 x 2*16*16*128); a ragged last chunk
+    # counts as a full one
+    chunks = int(((lens + 15) // 16).sum())
+    flop_chunk = 3 * 2 * 16 * 128 * 128 + 4 * 2 * 16 * 16 * 128
+    tflops = chunks * H * flop_chunk / kern / 1e12
     # bytes: state once per (sequence, head) in + out, conv state, and per
     # token the inputs and outputs
     per_tok = (3 * 128 * 2 + 128 * 4 + 4 + 128 * 2 + 128 * 2) * H
@@ -378,15 +391,22 @@ def bench_prefill(args, np, torch, kda, synth):
         "config": {"workload": "prefill_16seq_h48", "sequences": N,
                    "tokens": total, "lengths": lens.tolist(), "heads": H,
                    "qk_l2norm": True, "parallelism": "single-gpu"},
-        "roofline": {"bound": "latency", "achieved": round(nbytes / kern / 1e9,
-                                                           1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(nbytes / kern / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_MFMA_TFLOPS, 4),
                      "traffic": None},
         "cpu_baseline": cpu,
         "extra": {"kernel_us": round(kern * 1e6, 2),
-                  "chunk_metadata_us": round(meta_us, 2),
-                  "us_per_token": round(kern * 1e6 / max(lens.max(), 1), 3)},
+                  "path": "kda_prefill_chunked (fp32 MFMA, 16-token chunks)",
+                  "chunk_heads": chunks * H,
+                  "mfma_flop_per_chunk_head": flop_chunk,
+                  "longest_sequence_chunks": int((lens.max() + 15) // 16),
+                  "us_per_chunk_on_longest": round(
+                      kern * 1e6 / int((lens.max() + 15) // 16), 3),
+                  "hbm_GBs": round(nbytes / kern / 1e9, 1),
+                  "sequential_kernel_us": round(kern_seq * 1e6, 2),
+                  "speedup_vs_sequential": round(kern_seq / kern, 2),
+                  "chunk_metadata_us": round(meta_us, 2)},
     }
     print(json.dumps(line), flush=True)
 

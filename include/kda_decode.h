@@ -200,6 +200,27 @@ kda_status kda_prefill(const kda_dims* dims, const int32_t* cu_seqlens,
                        const int32_t* state_idx, void* out, void* hip_stream);
 
 /*
+ * The same prefill computed in chunks of 16 tokens on the matrix cores
+ * (fp32 MFMA): per chunk the deltas solve a 16 x 16 unit lower-triangular
+ * system (I + diag(beta) A) Delta = diag(beta) (V - K~ S), with A the
+ * decayed key Gram matrix of the chunk, K~ the keys scaled by their
+ * cumulative decay and S the state before the chunk; outputs and the next
+ * state follow from Delta by matrix products.  In exact arithmetic this is
+ * the token-by-token recurrence; in fp32 it differs only by rounding.  One
+ * workgroup per (sequence, head) carries the state across the sequence's
+ * chunks.  g must be finite; chunks whose cumulative decay exceeds 80 in
+ * magnitude in any channel take an exact per-entry path.  Arguments, flags,
+ * rules and status codes as kda_prefill.
+ */
+kda_status kda_prefill_chunked(const kda_dims* dims, const int32_t* cu_seqlens,
+                               const void* qkv, const float* conv_w,
+                               void* conv_state, float* rec_state,
+                               const float* g, const float* beta,
+                               const void* gate, const float* norm_w,
+                               const int32_t* state_idx, void* out,
+                               void* hip_stream);
+
+/*
  * Device-side chunk bookkeeping of a variable-length batch (page "PR
  * #51862 完整报告", implementation item 2 and the kda_metadata.py excerpt):
  * sequence i of cu_seqlens (device int32 [num_seqs + 1]) gets

@@ -8,6 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "kda_decode.hip"),
+           os.path.join(PKG, "csrc", "kda_chunked.hip"),
            os.path.join(PKG, "csrc", "kda_probe.hip")]
 LIB = os.path.join(PKG, "libkda_decode.so")
 

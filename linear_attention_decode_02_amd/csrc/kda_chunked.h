@@ -1,0 +1,29 @@
+// Internal interface between the C ABI (kda_decode.hip) and the chunked
+// prefill kernel (kda_chunked.hip).  Not part of the public headers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+struct KdaChunkedArgs {
+  const uint16_t* qkv;        // bf16 [tokens, 3C]
+  const float* conv_w;        // fp32 [3, 4, C]
+  uint16_t* conv_state;       // bf16 [slots, 3C, 3] (or [slots, 3, 3C])
+  float* rec_state;           // fp32 [slots, H, 128, 128]
+  const float* g;             // fp32 [tokens, H, 128]
+  const float* beta;          // fp32 [tokens, H]
+  const uint16_t* gate;       // bf16 [tokens, C] (output norm only)
+  const float* norm_w;        // fp32 [128] (output norm only)
+  const int32_t* state_idx;   // int32 [N]
+  const int32_t* cu_seqlens;  // int32 [N + 1]
+  uint16_t* out;              // bf16 [tokens, C]
+  uint32_t flags;
+  int32_t heads;
+  int32_t num_slots;
+  float eps;
+};
+
+// Queues the chunked prefill of `num_seqs` sequences on `stream`.
+hipError_t kda_chunked_prefill_launch(const KdaChunkedArgs& args,
+                                      int32_t num_seqs, hipStream_t stream);

@@ -46,6 +46,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "kda_chunked.h"
 #include "kda_decode.h"
 
 namespace {
@@ -972,6 +973,49 @@ kda_status kda_prefill(const kda_dims* d, const int32_t* cu_seqlens,
     hipLaunchKernelGGL(kda_decode_tokens_kernel<false>, grid, dim3(kThreads),
                        0, stream, p, 0);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_prefill_chunked(const kda_dims* d, const int32_t* cu_seqlens,
+                               const void* qkv, const float* conv_w,
+                               void* conv_state, float* rec_state,
+                               const float* g, const float* beta,
+                               const void* gate, const float* norm_w,
+                               const int32_t* state_idx, void* out,
+                               void* hip_stream) {
+  kda_status st = check_dims(d, kPlainFlags);
+  if (st != KDA_OK) return st;
+  if (d->batch == 0) return KDA_OK;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(cu_seqlens)) return KDA_ERR_MISALIGNED;
+  st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                    state_idx, out);
+  if (st != KDA_OK) return st;
+  if (!g || !beta) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(g) || !aligned16(beta)) return KDA_ERR_MISALIGNED;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return KDA_ERR_DEVICE;
+  KdaChunkedArgs a{};
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.conv_w = conv_w;
+  a.conv_state = static_cast<uint16_t*>(conv_state);
+  a.rec_state = rec_state;
+  a.g = g;
+  a.beta = beta;
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.norm_w = norm_w;
+  a.state_idx = state_idx;
+  a.cu_seqlens = cu_seqlens;
+  a.out = static_cast<uint16_t*>(out);
+  a.flags = d->flags;
+  a.heads = d->num_heads;
+  a.num_slots = d->num_slots;
+  a.eps = d->norm_eps;
+  return kda_chunked_prefill_launch(a, d->batch,
+                                    static_cast<hipStream_t>(hip_stream)) ==
+                 hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
 }
 
 kda_status kda_chunk_metadata(const int32_t* cu_seqlens, int32_t num_seqs,

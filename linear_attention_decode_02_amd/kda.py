@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
                                               ctypes.c_int32, ctypes.c_int32]
         L.kda_prefill.restype = ctypes.c_int
         L.kda_prefill.argtypes = [ctypes.POINTER(Dims)] + [P] * 12
+        L.kda_prefill_chunked.restype = ctypes.c_int
+        L.kda_prefill_chunked.argtypes = [ctypes.POINTER(Dims)] + [P] * 12
         L.kda_chunk_metadata.restype = ctypes.c_int
         L.kda_chunk_metadata.argtypes = [P, ctypes.c_int32, ctypes.c_int32,
                                          P, P, P]
@@ -257,10 +259,13 @@ def kda_decode_tokens(qkv, conv_w, conv_state, rec_state, g, beta, gate,
 
 def kda_prefill(cu_seqlens, qkv, conv_w, conv_state, rec_state, g, beta,
                 gate, norm_w, state_idx, out, *, norm: bool = True,
-                eps: float = 1e-5, variants: int = 0, stream=None) -> None:
+                eps: float = 1e-5, variants: int = 0, chunked: bool = False,
+                stream=None) -> None:
     """Variable-length prefill: sequence n covers tokens cu_seqlens[n] ..
     cu_seqlens[n+1]-1 of token-major qkv [tokens, 3C], g [tokens, H, 128],
-    beta [tokens, H], gate/out [tokens, C]; slot state_idx[n]."""
+    beta [tokens, H], gate/out [tokens, C]; slot state_idx[n].  ``chunked``
+    selects kda_prefill_chunked (16-token chunks on the matrix cores)
+    instead of the token-by-token kda_prefill."""
     if rec_state.dim() != 4 or qkv.dim() != 2:
         raise ValueError("rec_state [S, H, 128, 128], qkv [tokens, 3C]")
     S, H, D, D2 = rec_state.shape
@@ -284,7 +289,8 @@ def kda_prefill(cu_seqlens, qkv, conv_w, conv_state, rec_state, g, beta,
     dims = Dims(N, H, D, CONV_WIDTH, S,
                 (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
     with torch.cuda.device(qkv.device):
-        rc = lib().kda_prefill(
+        fn = lib().kda_prefill_chunked if chunked else lib().kda_prefill
+        rc = fn(
             ctypes.byref(dims), _ptr(cu_seqlens), _ptr(qkv), _ptr(conv_w),
             _ptr(conv_state), _ptr(rec_state), _ptr(g), _ptr(beta),
             _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,

@@ -207,13 +207,18 @@ def test_prefill_and_metadata_argument_checks():
     L = kda.lib()
     d = dims()
     p = [FAKE] * 12   # cu, qkv, conv_w, cs, rs, g, beta, gate, norm_w, idx, out
-    assert L.kda_prefill(ctypes.byref(d), *p[:11], None) == 4
-    q = list(p)
-    q[0] = None
-    assert L.kda_prefill(ctypes.byref(d), *q[:11], None) == 1
-    q[0] = FAKE + 4
-    assert L.kda_prefill(ctypes.byref(d), *q[:11], None) == 3
-    assert L.kda_prefill(ctypes.byref(dims(flags=0x21)), *p[:11], None) == 1
+    for fn in (L.kda_prefill, L.kda_prefill_chunked):
+        assert fn(ctypes.byref(d), *p[:11], None) == 4
+        q = list(p)
+        q[0] = None
+        assert fn(ctypes.byref(d), *q[:11], None) == 1
+        q[0] = FAKE + 4
+        assert fn(ctypes.byref(d), *q[:11], None) == 3
+        q[0] = FAKE
+        q[5] = None                                   # g
+        assert fn(ctypes.byref(d), *q[:11], None) == 1
+        assert fn(ctypes.byref(dims(flags=0x21)), *p[:11], None) == 1
+        assert fn(ctypes.byref(dims(batch=0)), *p[:11], None) == 0
     assert L.kda_chunk_metadata(FAKE, 3, 64, FAKE, FAKE, None) == 4
     assert L.kda_chunk_metadata(FAKE, -1, 64, FAKE, FAKE, None) == 1
     assert L.kda_chunk_metadata(FAKE, 3, 0, FAKE, FAKE, None) == 1

@@ -73,7 +73,7 @@ def prefill_case(seed, lens, H, S=None, norm=True, null=(), zero_state=False,
     return w, inp, cu
 
 
-def run_prefill(w, inp, cu, variants=0):
+def run_prefill(w, inp, cu, variants=0, chunked=False):
     t = synth.to_torch(inp, DEV)
     cu_d = torch.from_numpy(cu).to(DEV)
     tokens = inp["qkv"].shape[0]
@@ -83,7 +83,8 @@ def run_prefill(w, inp, cu, variants=0):
                     t["rec_state"], t["g"], t["beta"],
                     t["gate"] if w.norm else None,
                     t["norm_w"] if w.norm else None, t["state_idx"], out,
-                    norm=w.norm, eps=w.eps, variants=variants)
+                    norm=w.norm, eps=w.eps, variants=variants,
+                    chunked=chunked)
     torch.cuda.synchronize()
     return {"out": synth.bf16_bits(out),
             "conv_state": synth.bf16_bits(t["conv_state"]),
