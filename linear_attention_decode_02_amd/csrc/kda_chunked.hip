@@ -53,7 +53,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLd = kD + 4;  // padded row of [kC][kD] tables (floats)
 constexpr int kTd = kC + 4;  // padded row of [kD][kC] and [kC][kC] tables
-constexpr float kSafeExp = 80.0f;
+constexpr float kLog2e = 1.44269504088896341f;
+// |G| <= 80 (natural log units): e^{+-80} is a normal fp32 number
+constexpr float kSafeExp2 = 80.0f * kLog2e;
 static_assert(kWaves * 16 == kD, "one 16-column block per wave");
 static_assert(3 * kD + kD == kThreads, "conv and gate threads");
 
@@ -61,7 +63,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 struct alignas(16) Smem {
   float x[3][kC][kLd];        // conv outputs q, k, v (q, k normalised)
-  float G[kC][kLd];           // cumulative log decay inside the chunk
+  float G[kC][kLd];           // cumulative log2 decay inside the chunk
   float qt[kC][kLd];          // q_t e^{G_t}
   float kt[kC][kLd];          // k_t e^{G_t}
   float ki[kC][kLd];          // k_t e^{-G_t}
@@ -81,6 +83,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return __builtin_bit_cast(unsigned short, (__bf16)v);  // RNE
+}
+// 2^x on the transcendental unit (v_exp_f32)
+__device__ __forceinline__ float exp2_(float x) {
+  return __builtin_amdgcn_exp2f(x);
 }
 __device__ __forceinline__ float sigmoid_(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
@@ -159,16 +165,15 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   const int64_t gc = static_cast<int64_t>(part) * C + col0 + ci;
   float cw[kW] = {0.f, 0.f, 0.f, 0.f};
   uint16_t win[kW - 1] = {0, 0, 0};
-  int64_t cs_off[kW - 1] = {0, 0, 0};
+  // element t of the channel's stored window
+  auto cs_at = [&](int t) -> int64_t {
+    return tap_major ? (static_cast<int64_t>(slot) * (kW - 1) + t) * C3 + gc
+                     : (static_cast<int64_t>(slot) * C3 + gc) * (kW - 1) + t;
+  };
   if (conv_thread) {
     for (int t = 0; t < kW; ++t)
       cw[t] = p.conv_w[(static_cast<int64_t>(part) * kW + t) * C + col0 + ci];
-    for (int t = 0; t < kW - 1; ++t) {
-      cs_off[t] = tap_major
-                      ? (static_cast<int64_t>(slot) * (kW - 1) + t) * C3 + gc
-                      : (static_cast<int64_t>(slot) * C3 + gc) * (kW - 1) + t;
-      win[t] = p.conv_state[cs_off[t]];
-    }
+    for (int t = 0; t < kW - 1; ++t) win[t] = p.conv_state[cs_at(t)];
   }
   // the wave's 16 state columns, all 128 key rows: 8 row blocks of 16
   float* st = p.rec_state +
@@ -180,62 +185,79 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     for (int r = 0; r < 4; ++r) S[kb][r] = st[(16 * kb + 4 * gq + r) * kD];
   const float nw = kNorm ? p.norm_w[16 * wave + c] : 0.0f;
 
+  // raw inputs of one chunk, held in registers until the chunk runs: conv
+  // threads the bf16 qkv of their channel, gate threads the g of their key,
+  // every thread the 4 gate values of its output rows
+  uint32_t pf[kC];
+  float pgate[4];
+  float pbeta;
+  // Rows past the end of a short last chunk re-read the last valid row
+  // (branch-free loads; the values are masked where they are used).
+  auto prefetch = [&](int c0) {
+    const int last = (len - c0 < kC ? len - c0 : kC) - 1;
+    const int64_t tk = tb + c0;
+    if (conv_thread) {
+      const uint16_t* base = p.qkv + tk * C3 + gc;
+#pragma unroll
+      for (int t = 0; t < kC; ++t) pf[t] = base[(t < last ? t : last) * C3];
+    } else {
+      const float* base = p.g + (tk * H + h) * kD + (tid - 3 * kD);
+#pragma unroll
+      for (int t = 0; t < kC; ++t)
+        pf[t] = __float_as_uint(base[(t < last ? t : last) * (H * kD)]);
+    }
+    pbeta = p.beta[tk * H + h + (ci < last ? ci : last) * H];
+    const uint16_t* gbase = p.gate + tk * C + col0 + 16 * wave + c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * gq + r;
+      pgate[r] = kNorm ? bf16_to_f32(gbase[(t < last ? t : last) * C]) : 0.0f;
+    }
+  };
+  prefetch(0);
+
   for (int t0 = 0; t0 < len; t0 += kC) {
     const int nv = len - t0 < kC ? len - t0 : kC;
     const int64_t tok0 = tb + t0;
 
     // ---- phase 1: conv + SiLU (q, k, v), cumulative decay, beta ---------
-    float gatev[4] = {0.f, 0.f, 0.f, 0.f};
-    if (kNorm) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * gq + r;
-        if (t < nv)
-          gatev[r] = bf16_to_f32(
-              p.gate[(tok0 + t) * C + col0 + 16 * wave + c]);
-      }
-    }
+    // this chunk's raw inputs arrived during the previous chunk; the next
+    // chunk's are requested now
+    const uint32_t* xr = pf;
+    const float gatev[4] = {pgate[0], pgate[1], pgate[2], pgate[3]};
     if (conv_thread) {
-      uint16_t xb[kC];
-#pragma unroll
-      for (int t = 0; t < kC; ++t)
-        xb[t] = t < nv ? p.qkv[(tok0 + t) * C3 + gc] : uint16_t(0);
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
-        float y = 0.0f;
-        if (t < nv) {
-          const float xv = bf16_to_f32(xb[t]);
-          float a = cw[0] * bf16_to_f32(win[0]);
-          a += cw[1] * bf16_to_f32(win[1]);
-          a += cw[2] * bf16_to_f32(win[2]);
-          a += cw[3] * xv;
-          y = a * sigmoid_(a);
-          if (conv_update) {  // else every token sees the stored window
-            win[0] = win[1];
-            win[1] = win[2];
-            win[2] = xb[t];
-          }
+        const bool valid = t < nv;
+        const uint16_t xb = static_cast<uint16_t>(xr[t]);
+        const float xv = bf16_to_f32(xb);
+        float a = cw[0] * bf16_to_f32(win[0]);
+        a += cw[1] * bf16_to_f32(win[1]);
+        a += cw[2] * bf16_to_f32(win[2]);
+        a += cw[3] * xv;
+        sm.x[part][t][ci] = valid ? a * sigmoid_(a) : 0.0f;
+        if (conv_update) {  // else every token sees the stored window
+          win[0] = valid ? win[1] : win[0];
+          win[1] = valid ? win[2] : win[1];
+          win[2] = valid ? xb : win[2];
         }
-        sm.x[part][t][ci] = y;
       }
     } else {
+      // cumulative decay in log2 units (exp2 on the hardware unit)
       const int i = tid - 3 * kD;
-      float gv[kC];
-#pragma unroll
-      for (int t = 0; t < kC; ++t)
-        gv[t] = t < nv ? p.g[((tok0 + t) * H + h) * kD + i] : 0.0f;
       float G = 0.0f, gmax = 0.0f;
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
-        G += gv[t];
+        G += t < nv ? __uint_as_float(xr[t]) * kLog2e : 0.0f;
         sm.G[t][i] = G;
         gmax = fmaxf(gmax, fabsf(G));
       }
-      if (i < kC) sm.beta[i] = i < nv ? p.beta[(tok0 + i) * H + h] : 0.0f;
-      const bool bad = __any(!(gmax <= kSafeExp));  // NaN counts as unsafe
+      if (i < kC) sm.beta[i] = i < nv ? pbeta : 0.0f;
+      const bool bad = __any(!(gmax <= kSafeExp2));  // NaN counts as unsafe
       if (lane == 0) sm.unsafe[wave - 6] = bad ? 1 : 0;
     }
     __syncthreads();
+    if (t0 + kC < len) prefetch(t0 + kC);  // lands during this chunk
 
     // ---- phase 2: q/k L2 normalisation (optional) -----------------------
     if (l2) {
@@ -267,15 +289,15 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       for (int m = 0; m < kC / 4; ++m) {
         const int t = tq + 4 * m;
         const float G = sm.G[t][i];
-        const float e = expf(G);
+        const float e = exp2_(G);
         const float q = sm.x[0][t][i];
         const float k = sm.x[1][t][i];
         sm.qt[t][i] = q * e;
         sm.kt[t][i] = k * e;
-        sm.khT[i][t] = k * expf(Gl - G);
-        if (!unsafe) sm.ki[t][i] = k * expf(-G);
+        sm.khT[i][t] = k * exp2_(Gl - G);
+        if (!unsafe) sm.ki[t][i] = k * exp2_(-G);
       }
-      if (tq == 0) sm.gam[i] = expf(Gl);
+      if (tq == 0) sm.gam[i] = exp2_(Gl);
     }
     __syncthreads();
 
@@ -315,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       float a = 0.0f, b = 0.0f;
       if (s <= t) {
         for (int i = 0; i < kD; ++i) {
-          const float ks = sm.x[1][s][i] * expf(sm.G[t][i] - sm.G[s][i]);
+          const float ks = sm.x[1][s][i] * exp2_(sm.G[t][i] - sm.G[s][i]);
           a += sm.x[1][t][i] * ks;
           b += sm.x[0][t][i] * ks;
         }
@@ -387,6 +409,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     __syncthreads();
 
     // ---- phase 7: gated RMSNorm and bf16 outputs -------------------------
+    uint16_t* obase = p.out + tok0 * C + col0 + 16 * wave + c;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * gq + r;
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
         const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
         y = ((y * rs) * nw) * ga;
       }
-      p.out[(tok0 + t) * C + col0 + 16 * wave + c] = f32_to_bf16(y);
+      obase[t * C] = f32_to_bf16(y);
     }
   }
 
@@ -411,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) st[(16 * kb + 4 * gq + r) * kD] = S[kb][r];
   if (conv_thread && conv_update)
-    for (int t = 0; t < kW - 1; ++t) p.conv_state[cs_off[t]] = win[t];
+    for (int t = 0; t < kW - 1; ++t) p.conv_state[cs_at(t)] = win[t];
 }
 
 }  // namespace
