@@ -23,18 +23,27 @@
 // most 80 (e^{+-80} stays a normal fp32 number); otherwise each entry is
 // summed with its own exponential, which is exact for any decay.
 //
-// Mapping.  One 512-thread workgroup (8 waves) per (sequence, head).  Wave
-// w owns value columns 16w .. 16w+15 of the [128 key, 128 value] fp32 state,
-// held for the whole sequence in registers in the accumulator layout of
-// v_mfma_f32_16x16x4_f32 (lane l: column l%16, key rows 4(l/16) .. +3 of
-// each 16-row block).  That layout is also the B operand of the next
-// product once the summation index is permuted (key 16kb + 4(l/16) + j in
-// step j), so the state never leaves the registers between chunks.  The
-// other operands (K~, Q~, K^, T, B) are staged in LDS.  Per chunk and
-// wave: 32 MFMAs for K~ S, 32 for Q~ S, 32 for the state update, 8 for the
-// partial A or B products, 8 for the triangular solve and B Delta.  The
-// unit lower-triangular inverse T = (I + diag(beta) A)^{-1} (16 x 16) is one
-// column per lane of wave 0 by forward substitution.
+// Mapping: one 512-thread workgroup (8 waves) per (sequence, head), in two
+// roles that share each SIMD (waves w and w + 4 run on SIMD w):
+//   * state waves 0-3 own value columns 32w .. 32w+31 of the [128 key,
+//     128 value] fp32 state, held for the whole sequence in registers in
+//     the accumulator layout of v_mfma_f32_16x16x4_f32 (lane l: column
+//     l%16, key rows 4(l/16) .. +3 of each 16-row block).  That layout is
+//     also the B operand of the next product once the summation index is
+//     permuted (key 16kb + 4(l/16) + j in step j), so the state never
+//     leaves the registers.  Per chunk and wave: 64 MFMAs for K~ S, 64 for
+//     Q~ S, 16 for the triangular solve and B Delta, 64 for the state
+//     update; every lane also solves for the row of the 16 x 16 inverse
+//     T = (I + diag(beta) A)^{-1} its operand needs, by backward
+//     substitution, in the shadow of its matrix products.
+//   * prep waves 4-7 build the next chunk's operands meanwhile (4 tokens
+//     each): causal conv + SiLU from the raw bf16 inputs, q/k L2
+//     normalisation (wave-local: a wave holds all channels of its tokens),
+//     the cumulative decay, the decayed tables K~, Q~, K^, K e^{-G}, and
+//     then the A / B products on the matrix cores.
+// The tables are double-buffered in LDS; three barriers per chunk hand
+// them over.  The state waves also write the gated-RMSNorm outputs, one
+// 16-byte store per lane.
 
 #include <hip/hip_runtime.h>
 
@@ -49,40 +58,59 @@ namespace {
 constexpr int kD = 128;      // head dim (key = value)
 constexpr int kW = 4;        // conv width
 constexpr int kC = 16;       // tokens per chunk (one MFMA row block)
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kThreads = 512;
 constexpr int kLd = kD + 4;  // padded row of [kC][kD] tables (floats)
 constexpr int kTd = kC + 4;  // padded row of [kD][kC] and [kC][kC] tables
 constexpr float kLog2e = 1.44269504088896341f;
 // |G| <= 80 (natural log units): e^{+-80} is a normal fp32 number
 constexpr float kSafeExp2 = 80.0f * kLog2e;
-static_assert(kWaves * 16 == kD, "one 16-column block per wave");
-static_assert(3 * kD + kD == kThreads, "conv and gate threads");
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-struct alignas(16) Smem {
-  float x[3][kC][kLd];        // conv outputs q, k, v (q, k normalised)
-  float G[kC][kLd];           // cumulative log2 decay inside the chunk
-  float qt[kC][kLd];          // q_t e^{G_t}
-  float kt[kC][kLd];          // k_t e^{G_t}
-  float ki[kC][kLd];          // k_t e^{-G_t}
-  float khT[kD][kTd];         // k_t e^{G_last - G_t}, as [key][token]
-  float part[kWaves][kC][kC]; // partial A (waves 0-3) and B (4-7) products
-  float L[kC][kTd];           // beta_t A_ts for s < t, else 0
-  float B[kC][kTd];           // B_ts for s <= t, else 0
-  float T[kC][kTd];           // (I + L)^{-1}
-  float gam[kD];              // e^{G_last}
+// Operands of one chunk for the state waves (double-buffered).
+struct ChunkTables {
+  float qt[kC][kLd];    // q_t e^{G_t}
+  float kt[kC][kLd];    // k_t e^{G_t}
+  float v[kC][kLd];     // v_t
+  float khT[kD][kTd];   // k_t e^{G_last - G_t}, as [key][token]
+  float gam[kD];        // e^{G_last}
   float beta[kC];
-  float red[kWaves][kC];      // per-wave output sums of squares
-  int unsafe[2];              // |G| > kSafeExp seen by gate wave 6 / 7
 };
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+struct alignas(16) Smem {
+  ChunkTables tab[2];
+  float ki[kC][kLd];    // k_t e^{-G_t}; raw k on the exact path
+  float qraw[kC][kLd];  // exact path: q_t
+  float graw[kC][kLd];  // exact path: cumulative log2 decay
+  float part[4][kC][kC];  // A (keys 0-63, 64-127), B (same)
+  float LT[kC][kTd];    // LT[s][t] = beta_t A_ts for s < t, else 0
+  float B[kC][kTd];     // B_ts for s <= t, else 0
+  float o[kC][kLd];     // this chunk's outputs before the norm
+  float cw[3][kW][kD];  // this head's conv weights
+  float nw[kD];         // norm weight
+  uint32_t win[3][kW - 1][kD / 2];  // stored conv window, channel pairs
+  // raw inputs of the next chunk, copied in by the prep waves' LDS-direct
+  // loads: per prep wave its 7 input rows (3 parts, channel pairs), the
+  // chunk's 16 rows of g and its 16 betas
+  // (g and beta are read by every prep wave: two buffers by chunk parity)
+  uint32_t stage[4][7][3][kD / 2];
+  float gst[2][kC][kD];
+  float bst[2][64];
+  int unsafe;           // exact path for the chunk being prepared
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
 }
-__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
-  return __builtin_bit_cast(unsigned short, (__bf16)v);  // RNE
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {  // RNE
+  return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, (__bf16)lo)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(unsigned short, (__bf16)hi))
+          << 16);
 }
 // 2^x on the transcendental unit (v_exp_f32)
 __device__ __forceinline__ float exp2_(float x) {
@@ -114,6 +142,39 @@ __device__ __forceinline__ float wave_sum(float v) {
          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
 }
+// Global-memory pointers (address space 1).
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+// A wave-uniform global pointer made opaque to the compiler (readfirstlane
+// of both halves): loads become a scalar base plus a 32-bit lane offset
+// instead of a 64-bit address per lane.
+template <typename T>
+__device__ __forceinline__ gptr<const T> uniform_gptr(const T* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<gptr<const T>>((static_cast<uint64_t>(hi) << 32) |
+                                         lo);
+}
+// *(U*)(base + byte_off)
+template <typename U, typename T>
+__device__ __forceinline__ U load_at(gptr<const T> base, uint32_t byte_off) {
+  return *reinterpret_cast<gptr<const U>>(
+      reinterpret_cast<__attribute__((address_space(1))) const char*>(base) +
+      byte_off);
+}
+
+// One dword per lane from global memory straight into LDS: lane l's value
+// lands at dst[l] (dst wave-uniform).  Counted by vmcnt.
+__device__ __forceinline__ void load_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+// s_waitcnt fields (gfx9 encoding): vmcnt 0 with the others at maximum,
+// and lgkmcnt 0 with the others at maximum
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -156,285 +217,433 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   const bool conv_update = (flags & KDA_NO_CONV_UPDATE) == 0;
   const bool l2 = (flags & KDA_QK_L2NORM) != 0;
   const bool gate_silu = (flags & KDA_GATE_SILU) != 0;
+  const int nchunks = (len + kC - 1) / kC;
+  const bool state_wave = wave < 4;
+  const int pw = wave & 3;  // index within the role
 
   // ---- per-sequence set-up ----------------------------------------------
-  // conv threads 0..383: channel part*C + h*D + i; gate threads 384..511
-  const bool conv_thread = tid < 3 * kD;
-  const int part = tid >> 7;
-  const int ci = tid & (kD - 1);
-  const int64_t gc = static_cast<int64_t>(part) * C + col0 + ci;
-  float cw[kW] = {0.f, 0.f, 0.f, 0.f};
-  uint16_t win[kW - 1] = {0, 0, 0};
-  // element t of the channel's stored window
-  auto cs_at = [&](int t) -> int64_t {
-    return tap_major ? (static_cast<int64_t>(slot) * (kW - 1) + t) * C3 + gc
-                     : (static_cast<int64_t>(slot) * C3 + gc) * (kW - 1) + t;
-  };
-  if (conv_thread) {
-    for (int t = 0; t < kW; ++t)
-      cw[t] = p.conv_w[(static_cast<int64_t>(part) * kW + t) * C + col0 + ci];
-    for (int t = 0; t < kW - 1; ++t) win[t] = p.conv_state[cs_at(t)];
+  // state waves: the wave's 32 columns of the state, 2 blocks of 16
+  float* st = p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD) +
+              32 * pw + c;
+  f4 S[2][8];
+  // output lanes: token tid/16 (of the 16), columns 8 (tid%16) .. +7
+  const int ot = (tid & 255) >> 4;
+  const int oc = 8 * (tid & 15);
+  if (state_wave) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[cb][kb][r] = st[(16 * kb + 4 * gq + r) * kD + 16 * cb];
+  } else {
+    // conv weights and the norm weight of this head into LDS
+    const int i = tid - 256;  // 0..255
+    for (int e = i; e < 3 * kW * kD; e += 256) {
+      const int pp = e / (kW * kD), t = (e / kD) % kW, k = e % kD;
+      sm.cw[pp][t][k] =
+          p.conv_w[(static_cast<int64_t>(pp) * kW + t) * C + col0 + k];
+    }
+    if (i < kD) sm.nw[i] = kNorm ? p.norm_w[i] : 0.0f;
+    // the stored window of channels 2 lane, 2 lane + 1 of each part
+    if (i < kD / 2) {
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+        for (int e = 0; e < kW - 1; ++e) {
+          const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * i;
+          uint32_t wv;
+          if (tap_major) {
+            wv = *reinterpret_cast<const uint32_t*>(
+                p.conv_state +
+                (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch);
+          } else {
+            const uint16_t* cs = p.conv_state +
+                                 (static_cast<int64_t>(slot) * C3 + ch) *
+                                     (kW - 1) + e;
+            wv = static_cast<uint32_t>(cs[0]) |
+                 (static_cast<uint32_t>(cs[kW - 1]) << 16);
+          }
+          sm.win[pp][e][i] = wv;
+        }
+    }
   }
-  // the wave's 16 state columns, all 128 key rows: 8 row blocks of 16
-  float* st = p.rec_state +
-              (static_cast<int64_t>(slot) * H + h) * (kD * kD) + 16 * wave + c;
-  f4 S[8];
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S[kb][r] = st[(16 * kb + 4 * gq + r) * kD];
-  const float nw = kNorm ? p.norm_w[16 * wave + c] : 0.0f;
 
-  // raw inputs of one chunk, held in registers until the chunk runs: conv
-  // threads the bf16 qkv of their channel, gate threads the g of their key,
-  // every thread the 4 gate values of its output rows
-  uint32_t pf[kC];
-  float pgate[4];
-  float pbeta;
-  // Rows past the end of a short last chunk re-read the last valid row
-  // (branch-free loads; the values are masked where they are used).
-  auto prefetch = [&](int c0) {
-    const int last = (len - c0 < kC ? len - c0 : kC) - 1;
-    const int64_t tk = tb + c0;
-    if (conv_thread) {
-      const uint16_t* base = p.qkv + tk * C3 + gc;
+  // ---- prep stage 1 of chunk ci: conv, norms, decay, tables (wave-local)
+  // Requests chunk ci's raw inputs into the staging buffers (prep waves):
+  // wave pw the input rows of tokens 4pw-3 .. 4pw+3 (chunk-relative; rows
+  // before the sequence or past its end are clamped to valid rows and
+  // replaced or masked where used), rows 4pw .. 4pw+3 of g, and (wave 0)
+  // the betas.  The loads land while the wave works on the current chunk.
+  auto stage_chunk = [&](int ci) {
+    const int c0 = ci * kC;
+    const int nv = len - c0 < kC ? len - c0 : kC;
+    const int64_t tok0 = tb + c0;
 #pragma unroll
-      for (int t = 0; t < kC; ++t) pf[t] = base[(t < last ? t : last) * C3];
-    } else {
-      const float* base = p.g + (tk * H + h) * kD + (tid - 3 * kD);
+    for (int u = 0; u < 7; ++u) {
+      const int rel = 4 * pw - 3 + u;
+      const int rr =
+          rel < 0 ? (ci > 0 ? rel : 0) : (rel < nv - 1 ? rel : nv - 1);
+      const uint16_t* row = p.qkv + (tok0 + rr) * C3 + col0 + 2 * lane;
 #pragma unroll
-      for (int t = 0; t < kC; ++t)
-        pf[t] = __float_as_uint(base[(t < last ? t : last) * (H * kD)]);
+      for (int pp = 0; pp < 3; ++pp)
+        load_lds(row + pp * C, &sm.stage[pw][u][pp][0]);
     }
-    pbeta = p.beta[tk * H + h + (ci < last ? ci : last) * H];
-    const uint16_t* gbase = p.gate + tk * C + col0 + 16 * wave + c;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * gq + r;
-      pgate[r] = kNorm ? bf16_to_f32(gbase[(t < last ? t : last) * C]) : 0.0f;
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * pw + u;
+      const int rr = t < nv - 1 ? t : nv - 1;
+      const float* row = p.g + ((tok0 + rr) * H + h) * kD + lane;
+      load_lds(row, &sm.gst[ci & 1][t][0]);
+      load_lds(row + 64, &sm.gst[ci & 1][t][64]);
+    }
+    if (pw == 0) {
+      const int rr = lane < nv - 1 ? lane : nv - 1;
+      load_lds(p.beta + (tok0 + rr) * H + h, &sm.bst[ci & 1][0]);
     }
   };
-  prefetch(0);
 
-  for (int t0 = 0; t0 < len; t0 += kC) {
-    const int nv = len - t0 < kC ? len - t0 : kC;
-    const int64_t tok0 = tb + t0;
-
-    // ---- phase 1: conv + SiLU (q, k, v), cumulative decay, beta ---------
-    // this chunk's raw inputs arrived during the previous chunk; the next
-    // chunk's are requested now
-    const uint32_t* xr = pf;
-    const float gatev[4] = {pgate[0], pgate[1], pgate[2], pgate[3]};
-    if (conv_thread) {
+  auto prep_tables = [&](int ci) {
+    ChunkTables& T = sm.tab[ci & 1];
+    const int c0 = ci * kC;
+    const int nv = len - c0 < kC ? len - c0 : kC;
+    // raw[pp][u]: input of token 4pw - 3 + u (chunk-relative) for channels
+    // 2 lane, 2 lane + 1 of part pp (staged during the previous chunk)
+    uint32_t raw[3][7];
 #pragma unroll
-      for (int t = 0; t < kC; ++t) {
-        const bool valid = t < nv;
-        const uint16_t xb = static_cast<uint16_t>(xr[t]);
-        const float xv = bf16_to_f32(xb);
-        float a = cw[0] * bf16_to_f32(win[0]);
-        a += cw[1] * bf16_to_f32(win[1]);
-        a += cw[2] * bf16_to_f32(win[2]);
-        a += cw[3] * xv;
-        sm.x[part][t][ci] = valid ? a * sigmoid_(a) : 0.0f;
-        if (conv_update) {  // else every token sees the stored window
-          win[0] = valid ? win[1] : win[0];
-          win[1] = valid ? win[2] : win[1];
-          win[2] = valid ? xb : win[2];
-        }
-      }
-    } else {
-      // cumulative decay in log2 units (exp2 on the hardware unit)
-      const int i = tid - 3 * kD;
-      float G = 0.0f, gmax = 0.0f;
+    for (int u = 0; u < 7; ++u)
 #pragma unroll
-      for (int t = 0; t < kC; ++t) {
-        G += t < nv ? __uint_as_float(xr[t]) * kLog2e : 0.0f;
-        sm.G[t][i] = G;
-        gmax = fmaxf(gmax, fabsf(G));
-      }
-      if (i < kC) sm.beta[i] = i < nv ? pbeta : 0.0f;
-      const bool bad = __any(!(gmax <= kSafeExp2));  // NaN counts as unsafe
-      if (lane == 0) sm.unsafe[wave - 6] = bad ? 1 : 0;
-    }
-    __syncthreads();
-    if (t0 + kC < len) prefetch(t0 + kC);  // lands during this chunk
-
-    // ---- phase 2: q/k L2 normalisation (optional) -----------------------
-    if (l2) {
-      const float qscale = 1.0f / sqrtf(static_cast<float>(kD));
+      for (int pp = 0; pp < 3; ++pp) raw[pp][u] = sm.stage[pw][u][pp][lane];
+    f2 gl[kC];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int t = 2 * wave + tt;
+    for (int t = 0; t < kC; ++t)
+      gl[t] = *reinterpret_cast<const f2*>(&sm.gst[ci & 1][t][2 * lane]);
+    const float bt = lane < 4 ? sm.bst[ci & 1][4 * pw + lane] : 0.0f;
+    // the staging buffers are free again: request the next chunk
+    wait_lds();
+    if (ci + 1 < nchunks) stage_chunk(ci + 1);
+    uint32_t wv[3][kW - 1];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const float v0 = sm.x[pp][t][lane];
-          const float v1 = sm.x[pp][t][lane + 64];
-          const float ss = wave_sum(v0 * v0 + v1 * v1);
-          const float r = 1.0f / sqrtf(ss + 1e-6f);
-          const float sc = pp == 0 ? qscale : 1.0f;
-          sm.x[pp][t][lane] = (v0 * r) * sc;
-          sm.x[pp][t][lane + 64] = (v1 * r) * sc;
-        }
-      }
-      __syncthreads();
-    }
-    const bool unsafe = (sm.unsafe[0] | sm.unsafe[1]) != 0;
-
-    // ---- phase 3: decayed operand tables --------------------------------
+    for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e) wv[pp][e] = sm.win[pp][e][lane];
+    // cumulative decay of keys 2 lane, 2 lane + 1 (log2 units) over the
+    // whole chunk; the values at this wave's 4 tokens and at the end
+    f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+    f2 G = {0.f, 0.f};
+    float gmax = 0.0f;
     {
-      const int i = tid & (kD - 1);
-      const int tq = tid >> 7;
-      const float Gl = sm.G[kC - 1][i];
 #pragma unroll
-      for (int m = 0; m < kC / 4; ++m) {
-        const int t = tq + 4 * m;
-        const float G = sm.G[t][i];
-        const float e = exp2_(G);
-        const float q = sm.x[0][t][i];
-        const float k = sm.x[1][t][i];
-        sm.qt[t][i] = q * e;
-        sm.kt[t][i] = k * e;
-        sm.khT[i][t] = k * exp2_(Gl - G);
-        if (!unsafe) sm.ki[t][i] = k * exp2_(-G);
+      for (int t = 0; t < kC; ++t) {
+        const f2 gv = gl[t];
+        if (t < nv) G += gv * kLog2e;
+        gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (t == 4 * pw + u) Gu[u] = G;
       }
-      if (tq == 0) sm.gam[i] = exp2_(Gl);
     }
-    __syncthreads();
+    // NaN counts as unsafe; the same verdict in every prep wave
+    const bool unsafe = __any(!(gmax <= kSafeExp2));
+    const float qscale = 1.0f / sqrtf(static_cast<float>(kD));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * pw + u;
+      const bool valid = t < nv;
+      float y[3][2];
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          float a = 0.0f;
+#pragma unroll
+          for (int tap = 0; tap < kW; ++tap) {
+            // with the update a token sees the inputs before it (the stored
+            // window before the sequence); without it, the stored window
+            const int rin = 4 * pw + u - (kW - 1) + tap;
+            const uint32_t w2 =
+                tap == kW - 1 ? raw[pp][u + tap]
+                : conv_update ? (rin < 0 && ci == 0 ? wv[pp][(kW - 1) + rin]
+                                                    : raw[pp][u + tap])
+                              : wv[pp][tap];
+            a += sm.cw[pp][tap][2 * lane + e] *
+                 (e ? bf16_hi(w2) : bf16_lo(w2));
+          }
+          y[pp][e] = valid ? a * sigmoid_(a) : 0.0f;
+        }
+      if (l2) {
+        const float sq = wave_sum(y[0][0] * y[0][0] + y[0][1] * y[0][1]);
+        const float sk = wave_sum(y[1][0] * y[1][0] + y[1][1] * y[1][1]);
+        const float rq = 1.0f / sqrtf(sq + 1e-6f);
+        const float rk = 1.0f / sqrtf(sk + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          y[0][e] = (y[0][e] * rq) * qscale;
+          y[1][e] = y[1][e] * rk;
+        }
+      }
+      const f2 ee = {exp2_(Gu[u].x), exp2_(Gu[u].y)};
+      *reinterpret_cast<f2*>(&T.qt[t][2 * lane]) =
+          f2{y[0][0] * ee.x, y[0][1] * ee.y};
+      *reinterpret_cast<f2*>(&T.kt[t][2 * lane]) =
+          f2{y[1][0] * ee.x, y[1][1] * ee.y};
+      *reinterpret_cast<f2*>(&T.v[t][2 * lane]) = f2{y[2][0], y[2][1]};
+      T.khT[2 * lane][t] = y[1][0] * exp2_(G.x - Gu[u].x);
+      T.khT[2 * lane + 1][t] = y[1][1] * exp2_(G.y - Gu[u].y);
+      if (!unsafe) {
+        *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) =
+            f2{y[1][0] * exp2_(-Gu[u].x), y[1][1] * exp2_(-Gu[u].y)};
+      } else {
+        *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) = f2{y[1][0], y[1][1]};
+        *reinterpret_cast<f2*>(&sm.qraw[t][2 * lane]) = f2{y[0][0], y[0][1]};
+        *reinterpret_cast<f2*>(&sm.graw[t][2 * lane]) = Gu[u];
+      }
+    }
+    if (pw == 0) {
+      *reinterpret_cast<f2*>(&T.gam[2 * lane]) = f2{exp2_(G.x), exp2_(G.y)};
+      if (lane == 0) sm.unsafe = unsafe ? 1 : 0;
+    }
+    if (lane < 4) {
+      const int t = 4 * pw + lane;
+      T.beta[t] = t < nv ? bt : 0.0f;
+    }
+  };
 
-    // ---- phase 4: A = K~ (K e^{-G})^T, B = Q~ (K e^{-G})^T ---------------
-    if (!unsafe) {
-      // waves 0-3: A over keys 32(w%4) .. +31; waves 4-7: B likewise
-      const float(*src)[kLd] = wave < 4 ? sm.kt : sm.qt;
-      const int kbase = 32 * (wave & 3) + 8 * gq;
-      const f4 a0 = ld4(&src[c][kbase]);
-      const f4 a1 = ld4(&src[c][kbase + 4]);
-      const f4 b0 = ld4(&sm.ki[c][kbase]);
-      const f4 b1 = ld4(&sm.ki[c][kbase + 4]);
+  // ---- prep stage 2: A / B products (or the exact per-entry sums) -------
+  auto prep_gram = [&](int ci) {
+    const ChunkTables& T = sm.tab[ci & 1];
+    if (!sm.unsafe) {
+      // wave 4: A over keys 0-63, 5: A over 64-127, 6 / 7: B likewise
+      const float(*src)[kLd] = pw < 2 ? T.kt : T.qt;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma(a0[j], b0[j], acc);
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = 64 * (pw & 1) + 16 * kb + 4 * gq;
+        const f4 a = ld4(&src[c][key]);
+        const f4 b = ld4(&sm.ki[c][key]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma(a1[j], b1[j], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.part[wave][4 * gq + r][c] = acc[r];
-      __syncthreads();
-      const int idx = tid & 255;
-      const int t = idx >> 4;
-      const int s = idx & 15;
-      if (tid < 256) {
-        const float a = sm.part[0][t][s] + sm.part[1][t][s] +
-                        sm.part[2][t][s] + sm.part[3][t][s];
-        sm.L[t][s] = s < t ? sm.beta[t] * a : 0.0f;
-      } else {
-        const float b = sm.part[4][t][s] + sm.part[5][t][s] +
-                        sm.part[6][t][s] + sm.part[7][t][s];
-        sm.B[t][s] = s <= t ? b : 0.0f;
+        for (int j = 0; j < 4; ++j) acc = mfma(a[j], b[j], acc);
       }
-    } else if (tid < 256) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.part[pw][4 * gq + r][c] = acc[r];
+    } else {
       // large decay: one exponential per (t, s, key)
-      const int t = tid >> 4;
+      const int t = (tid & 255) >> 4;
       const int s = tid & 15;
       float a = 0.0f, b = 0.0f;
       if (s <= t) {
         for (int i = 0; i < kD; ++i) {
-          const float ks = sm.x[1][s][i] * exp2_(sm.G[t][i] - sm.G[s][i]);
-          a += sm.x[1][t][i] * ks;
-          b += sm.x[0][t][i] * ks;
+          const float ks = sm.ki[s][i] * exp2_(sm.graw[t][i] - sm.graw[s][i]);
+          a += sm.ki[t][i] * ks;
+          b += sm.qraw[t][i] * ks;
         }
       }
-      sm.L[t][s] = s < t ? sm.beta[t] * a : 0.0f;
+      sm.LT[s][t] = s < t ? T.beta[t] * a : 0.0f;
       sm.B[t][s] = b;
     }
-    __syncthreads();
+  };
 
-    // ---- phase 5: T = (I + L)^{-1} (wave 0), K~ S and Q~ S (all) --------
-    if (wave == 0 && lane < kC) {
-      float tc[kC];
+  // ---- prep stage 3: sum the partial products, mask, scale by beta ------
+  auto prep_reduce = [&](int ci) {
+    if (sm.unsafe) return;
+    const ChunkTables& T = sm.tab[ci & 1];
+    const int t = (tid & 255) >> 4;
+    const int s = tid & 15;
+    const float a = sm.part[0][t][s] + sm.part[1][t][s];
+    const float b = sm.part[2][t][s] + sm.part[3][t][s];
+    sm.LT[s][t] = s < t ? T.beta[t] * a : 0.0f;
+    sm.B[t][s] = s <= t ? b : 0.0f;
+  };
+
+  // ---- state stage: one chunk through the recurrence ---------------------
+  auto state_chunk = [&](int ci) {
+    const ChunkTables& T = sm.tab[ci & 1];
+    f4 ks[2], o[2];
 #pragma unroll
-      for (int t = 0; t < kC; ++t) {
-        float v = t == lane ? 1.0f : 0.0f;
-#pragma unroll
-        for (int s = 0; s < t; ++s) v -= sm.L[t][s] * tc[s];
-        tc[t] = v;
-      }
-#pragma unroll
-      for (int t = 0; t < kC; ++t) sm.T[t][lane] = tc[t];
+    for (int cb = 0; cb < 2; ++cb) {
+      ks[cb] = f4{0.f, 0.f, 0.f, 0.f};
+      o[cb] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    f4 ks = {0.f, 0.f, 0.f, 0.f};  // (K~ S)[token 4gq + r][col c]
-    f4 o = {0.f, 0.f, 0.f, 0.f};   // (Q~ S)[token 4gq + r][col c]
+    // operands one key block ahead; the scheduling fence keeps the
+    // compiler from hoisting all of them (register pressure)
+    f4 ak = ld4(&T.kt[c][4 * gq]);
+    f4 aq = ld4(&T.qt[c][4 * gq]);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const f4 ak = ld4(&sm.kt[c][16 * kb + 4 * gq]);
-      const f4 aq = ld4(&sm.qt[c][16 * kb + 4 * gq]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ks = mfma(ak[j], S[kb][j], ks);
-        o = mfma(aq[j], S[kb][j], o);
+      f4 akn = ak, aqn = aq;
+      if (kb < 7) {
+        akn = ld4(&T.kt[c][16 * kb + 16 + 4 * gq]);
+        aqn = ld4(&T.qt[c][16 * kb + 16 + 4 * gq]);
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          ks[cb] = mfma(ak[j], S[cb][kb][j], ks[cb]);
+          o[cb] = mfma(aq[j], S[cb][kb][j], o[cb]);
+        }
+      ak = akn;
+      aq = aqn;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // beta (V - K~ S) in the accumulator layout
-    f4 br;
+    // row c of T: (I + L)^T y = e_c, backward
+    float y[kC];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * gq + r;
-      br[r] = sm.beta[t] * (sm.x[2][t][16 * wave + c] - ks[r]);
+    for (int t = kC - 1; t >= 0; --t) {
+      float v = t == c ? 1.0f : 0.0f;
+#pragma unroll
+      for (int s4 = 0; s4 < kC; s4 += 4) {
+        if (s4 + 3 <= t) continue;  // all of s4 .. s4+3 <= t
+        const f4 lt = ld4(&sm.LT[t][s4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s4 + u > t) v -= lt[u] * y[s4 + u];
+      }
+      y[t] = v;
     }
-    __syncthreads();
-
-    // ---- phase 6: Delta = T br, O += B Delta, S <- e^{G_last} S + K^^T Delta
-    f4 dl = {0.f, 0.f, 0.f, 0.f};
-    {
-      const f4 at = ld4(&sm.T[c][4 * gq]);
+    f4 at;  // T[c][4gq + j]
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dl = mfma(at[j], br[j], dl);
-      const f4 ab = ld4(&sm.B[c][4 * gq]);
+    for (int j = 0; j < 4; ++j)
+      at[j] = gq == 0 ? y[j] : gq == 1 ? y[4 + j] : gq == 2 ? y[8 + j]
+                                                           : y[12 + j];
+    const f4 ab = ld4(&sm.B[c][4 * gq]);
+    f4 dl[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o = mfma(ab[j], dl[j], o);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const f4 gm = ld4(&sm.gam[16 * kb + 4 * gq]);
-      S[kb] *= gm;
-      const f4 ah = ld4(&sm.khT[16 * kb + c][4 * gq]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[kb] = mfma(ah[j], dl[j], S[kb]);
-    }
-    if (kNorm) {
+    for (int cb = 0; cb < 2; ++cb) {
+      const int col = 32 * pw + 16 * cb + c;
+      f4 br;  // beta (V - K~ S) in the accumulator layout
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ss = row_sum16(o[r] * o[r]);
-        if (c == 0) sm.red[wave][4 * gq + r] = ss;
+        const int t = 4 * gq + r;
+        br[r] = T.beta[t] * (T.v[t][col] - ks[cb][r]);
       }
+      dl[cb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dl[cb] = mfma(at[j], br[j], dl[cb]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[cb] = mfma(ab[j], dl[cb][j], o[cb]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.o[4 * gq + r][col] = o[cb][r];
+    }
+    f4 gm = ld4(&T.gam[4 * gq]);
+    f4 ah = ld4(&T.khT[c][4 * gq]);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      f4 gmn = gm, ahn = ah;
+      if (kb < 7) {
+        gmn = ld4(&T.gam[16 * kb + 16 + 4 * gq]);
+        ahn = ld4(&T.khT[16 * kb + 16 + c][4 * gq]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        S[cb][kb] *= gm;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          S[cb][kb] = mfma(ah[j], dl[cb][j], S[cb][kb]);
+      }
+      gm = gmn;
+      ah = ahn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- state stage: gated RMSNorm and bf16 outputs of a chunk ------------
+  auto emit = [&](int ci, u4 gate_raw) {
+    const int c0 = ci * kC;
+    const int nv = len - c0 < kC ? len - c0 : kC;
+    const f4 v0 = ld4(&sm.o[ot][oc]);
+    const f4 v1 = ld4(&sm.o[ot][oc + 4]);
+    float yv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    if (kNorm) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += yv[j] * yv[j];
+      ss = row_sum16(ss);  // the 16 lanes of token ot
+      const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w2 = gate_raw[j >> 1];
+        const float gv = (j & 1) ? bf16_hi(w2) : bf16_lo(w2);
+        const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
+        yv[j] = ((yv[j] * rs) * sm.nw[oc + j]) * ga;
+      }
+    }
+    if (ot < nv) {
+      const u4 pk = {pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3]),
+                     pack_bf16(yv[4], yv[5]), pack_bf16(yv[6], yv[7])};
+      *reinterpret_cast<u4*>(p.out + (tb + c0 + ot) * C + col0 + oc) = pk;
+    }
+  };
+
+  // ---- the pipeline --------------------------------------------------------
+  if (!state_wave) {
+    stage_chunk(0);
+    wait_vmem();
+  }
+  __syncthreads();  // conv and norm weights, the first chunk's inputs
+  if (!state_wave) prep_tables(0);
+  __syncthreads();
+  if (!state_wave) prep_gram(0);
+  __syncthreads();
+  if (!state_wave) {
+    prep_reduce(0);
+    wait_vmem();
+  }
+  __syncthreads();
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const bool more = ci + 1 < nchunks;
+    u4 gate_raw = {0u, 0u, 0u, 0u};
+    if (state_wave) {
+      if (kNorm) {
+        const int nv = len - ci * kC < kC ? len - ci * kC : kC;
+        const int rr = ot < nv - 1 ? ot : nv - 1;
+        gate_raw = *reinterpret_cast<const u4*>(
+            p.gate + (tb + ci * kC + rr) * C + col0 + oc);
+      }
+      state_chunk(ci);
+    } else if (more) {
+      prep_tables(ci + 1);
     }
     __syncthreads();
-
-    // ---- phase 7: gated RMSNorm and bf16 outputs -------------------------
-    uint16_t* obase = p.out + tok0 * C + col0 + 16 * wave + c;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * gq + r;
-      if (t >= nv) continue;
-      float y = o[r];
-      if (kNorm) {
-        float tot = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) tot += sm.red[w][t];
-        const float rs = 1.0f / sqrtf(tot * (1.0f / kD) + p.eps);
-        const float gv = gatev[r];
-        const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
-        y = ((y * rs) * nw) * ga;
-      }
-      obase[t * C] = f32_to_bf16(y);
-    }
+    if (state_wave)
+      emit(ci, gate_raw);
+    else if (more)
+      prep_gram(ci + 1);
+    __syncthreads();
+    if (!state_wave && more) prep_reduce(ci + 1);
+    if (!state_wave) wait_vmem();  // the staged inputs of the next chunk
+    __syncthreads();
   }
 
   // ---- write back the state and the conv window ---------------------------
+  if (state_wave) {
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st[(16 * kb + 4 * gq + r) * kD] = S[kb][r];
-  if (conv_thread && conv_update)
-    for (int t = 0; t < kW - 1; ++t) p.conv_state[cs_at(t)] = win[t];
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          st[(16 * kb + 4 * gq + r) * kD + 16 * cb] = S[cb][kb][r];
+  }
+  if (conv_update && tid < 3 * kD) {
+    // new window = the last W-1 inputs of (stored window ++ tokens)
+    const int64_t ch =
+        (tid >> 7) * static_cast<int64_t>(C) + col0 + (tid & 127);
+    auto at = [&](int e) -> int64_t {
+      return tap_major ? (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch
+                       : (static_cast<int64_t>(slot) * C3 + ch) * (kW - 1) + e;
+    };
+    uint16_t nwin[kW - 1];
+#pragma unroll
+    for (int e = 0; e < kW - 1; ++e) {
+      const int idx = len - (kW - 1) + e;  // token index in the sequence
+      nwin[e] = idx >= 0 ? p.qkv[(tb + idx) * C3 + ch]
+                         : p.conv_state[at(e + len)];
+    }
+#pragma unroll
+    for (int e = 0; e < kW - 1; ++e) p.conv_state[at(e)] = nwin[e];
+  }
 }
 
 }  // namespace
