@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0
 FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_02_amd", "csrc",
                           "kda_decode.hip")
+KERNEL_END_MARK = "// Several tokens per row in one launch"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "kda_decode_b256_h48_traffic.md")
 
@@ -52,9 +53,16 @@ VARIANTS = {
 }
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash(text: str = None) -> str:
+    """Hash of the device code the single-token kernel is built from: the
+    source from the opening of its namespace to the end of kda_decode_kernel
+    (host code and the other kernels of the file are not part of it)."""
+    if text is None:
+        with open(KERNEL_SRC, encoding="utf-8") as f:
+            text = f.read()
+    start = text.index("namespace {")
+    end = text.index(KERNEL_END_MARK, start)
+    return hashlib.sha256(text[start:end].encode()).hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):

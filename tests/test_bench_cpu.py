@@ -25,3 +25,21 @@ def test_traffic_record_parses():
     text = open(bench.TRAFFIC_FILE).read()
     assert "traffic_bytes_per_launch:" in text
     assert "kernel_source_sha256_16:" in text
+
+
+def test_kernel_hash_covers_only_the_single_token_kernel():
+    """Host code after the kernel does not change the hash; a change inside
+    the kernel's region does."""
+    import bench
+    text = open(bench.KERNEL_SRC, encoding="utf-8").read()
+    h = bench.kernel_hash(text)
+    assert bench.kernel_hash(text + "\n// host-side addition\n") == h
+    i = text.index("namespace {") + len("namespace {")
+    assert bench.kernel_hash(text[:i] + "\n// edit\n" + text[i:]) != h
+
+
+def test_recorded_traffic_matches_this_kernel():
+    import bench
+    t = bench.recorded_traffic("b256_h48_pool512_null32")
+    assert t is not None and abs(t / 1478831616 - 1) < 0.01
+    assert bench.recorded_traffic("b64_h24_pool128") is None
