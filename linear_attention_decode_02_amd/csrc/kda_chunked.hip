@@ -134,14 +134,6 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_<0x140>(v);
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row_sum16(v);
-  const int b = __builtin_bit_cast(int, v);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16)) +
-         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
-         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-}
 // Global-memory pointers (address space 1).
 template <typename T>
 using gptr = __attribute__((address_space(1))) T*;
@@ -174,6 +166,27 @@ __device__ __forceinline__ void load_lds(const void* src, void* dst) {
 // and lgkmcnt 0 with the others at maximum
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Eight wave sums side by side (independent DPP chains), each result in
+// every lane.
+__device__ __forceinline__ void wave_sum8(float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_<0xB1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_<0x4E>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_<0x141>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_<0x140>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = __builtin_bit_cast(int, v[i]);
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  }
+}
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -347,11 +360,18 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     // NaN counts as unsafe; the same verdict in every prep wave
     const bool unsafe = __any(!(gmax <= kSafeExp2));
     const float qscale = 1.0f / sqrtf(static_cast<float>(kD));
+    // conv + SiLU of the 4 tokens (weights read once), then the 8 norm
+    // reductions side by side, then the tables
+    f2 cwv[3][kW];
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+      for (int tap = 0; tap < kW; ++tap)
+        cwv[pp][tap] = *reinterpret_cast<const f2*>(&sm.cw[pp][tap][2 * lane]);
+    float y[4][3][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = 4 * pw + u;
-      const bool valid = t < nv;
-      float y[3][2];
+      const bool valid = 4 * pw + u < nv;
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
@@ -367,36 +387,49 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
                 : conv_update ? (rin < 0 && ci == 0 ? wv[pp][(kW - 1) + rin]
                                                     : raw[pp][u + tap])
                               : wv[pp][tap];
-            a += sm.cw[pp][tap][2 * lane + e] *
-                 (e ? bf16_hi(w2) : bf16_lo(w2));
+            a += cwv[pp][tap][e] * (e ? bf16_hi(w2) : bf16_lo(w2));
           }
-          y[pp][e] = valid ? a * sigmoid_(a) : 0.0f;
+          y[u][pp][e] = valid ? a * sigmoid_(a) : 0.0f;
         }
-      if (l2) {
-        const float sq = wave_sum(y[0][0] * y[0][0] + y[0][1] * y[0][1]);
-        const float sk = wave_sum(y[1][0] * y[1][0] + y[1][1] * y[1][1]);
-        const float rq = 1.0f / sqrtf(sq + 1e-6f);
-        const float rk = 1.0f / sqrtf(sk + 1e-6f);
+    }
+    if (l2) {
+      float ss[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ss[2 * u] = y[u][0][0] * y[u][0][0] + y[u][0][1] * y[u][0][1];
+        ss[2 * u + 1] = y[u][1][0] * y[u][1][0] + y[u][1][1] * y[u][1][1];
+      }
+      wave_sum8(ss);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float rq = 1.0f / sqrtf(ss[2 * u] + 1e-6f);
+        const float rk = 1.0f / sqrtf(ss[2 * u + 1] + 1e-6f);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          y[0][e] = (y[0][e] * rq) * qscale;
-          y[1][e] = y[1][e] * rk;
+          y[u][0][e] = (y[u][0][e] * rq) * qscale;
+          y[u][1][e] = y[u][1][e] * rk;
         }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * pw + u;
       const f2 ee = {exp2_(Gu[u].x), exp2_(Gu[u].y)};
       *reinterpret_cast<f2*>(&T.qt[t][2 * lane]) =
-          f2{y[0][0] * ee.x, y[0][1] * ee.y};
+          f2{y[u][0][0] * ee.x, y[u][0][1] * ee.y};
       *reinterpret_cast<f2*>(&T.kt[t][2 * lane]) =
-          f2{y[1][0] * ee.x, y[1][1] * ee.y};
-      *reinterpret_cast<f2*>(&T.v[t][2 * lane]) = f2{y[2][0], y[2][1]};
-      T.khT[2 * lane][t] = y[1][0] * exp2_(G.x - Gu[u].x);
-      T.khT[2 * lane + 1][t] = y[1][1] * exp2_(G.y - Gu[u].y);
+          f2{y[u][1][0] * ee.x, y[u][1][1] * ee.y};
+      *reinterpret_cast<f2*>(&T.v[t][2 * lane]) = f2{y[u][2][0], y[u][2][1]};
+      T.khT[2 * lane][t] = y[u][1][0] * exp2_(G.x - Gu[u].x);
+      T.khT[2 * lane + 1][t] = y[u][1][1] * exp2_(G.y - Gu[u].y);
       if (!unsafe) {
         *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) =
-            f2{y[1][0] * exp2_(-Gu[u].x), y[1][1] * exp2_(-Gu[u].y)};
+            f2{y[u][1][0] * exp2_(-Gu[u].x), y[u][1][1] * exp2_(-Gu[u].y)};
       } else {
-        *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) = f2{y[1][0], y[1][1]};
-        *reinterpret_cast<f2*>(&sm.qraw[t][2 * lane]) = f2{y[0][0], y[0][1]};
+        *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) =
+            f2{y[u][1][0], y[u][1][1]};
+        *reinterpret_cast<f2*>(&sm.qraw[t][2 * lane]) =
+            f2{y[u][0][0], y[u][0][1]};
         *reinterpret_cast<f2*>(&sm.graw[t][2 * lane]) = Gu[u];
       }
     }
