@@ -33,6 +33,12 @@ if ROOT not in sys.path:
 METRIC = "KDA decode (seq*head) updates/sec + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+# kda_decode_tokens runs the chunked matrix-core form from this many tokens
+CHUNKED_MIN_TOKENS = 16
+# fp32 MFMA flop per (16-token chunk, head) of the chunked form: K~S, Q~S
+# and the state update (3 x 2*16*128*128), A, B, the solve and B Delta
+# (4 x 2*16*16*128)
+CHUNK_MFMA_FLOP = 3 * 2 * 16 * 128 * 128 + 4 * 2 * 16 * 16 * 128
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_02_amd", "csrc",
                           "kda_decode.hip")
 KERNEL_END_MARK = "// Several tokens per row in one launch"
@@ -260,6 +266,16 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic}
+    if T >= CHUNKED_MIN_TOKENS:
+        # the chunked matrix-core form: priced in its fp32 MFMA work per
+        # (16-token chunk, live row, head)
+        chunks = -(-T // 16) * live_rows * w.heads      # per launch
+        tflops = chunks * CHUNK_MFMA_FLOP / kern_avg_s / 1e12
+        extra["hbm_GBs"] = round(achieved, 1)
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2),
+                    "peak": FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / FP32_MFMA_TFLOPS, 4),
+                    "traffic": None}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -346,7 +362,7 @@ def bench_prefill(args, np, torch, kda, synth):
     # the solve / B Delta products (4 x 2*16*16*128); a ragged last chunk
     # counts as a full one
     chunks = int(((lens + 15) // 16).sum())
-    flop_chunk = 3 * 2 * 16 * 128 * 128 + 4 * 2 * 16 * 16 * 128
+    flop_chunk = CHUNK_MFMA_FLOP
     tflops = chunks * H * flop_chunk / kern / 1e12
     # bytes: state once per (sequence, head) in + out, conv state, and per
     # token the inputs and outputs

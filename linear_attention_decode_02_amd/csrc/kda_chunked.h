@@ -16,7 +16,9 @@ struct KdaChunkedArgs {
   const uint16_t* gate;       // bf16 [tokens, C] (output norm only)
   const float* norm_w;        // fp32 [128] (output norm only)
   const int32_t* state_idx;   // int32 [N]
-  const int32_t* cu_seqlens;  // int32 [N + 1]
+  const int32_t* cu_seqlens;  // int32 [N + 1], or null: tokens_per_row
+  int32_t tokens_per_row;     // with cu_seqlens null: row n owns tokens
+                              // n*T .. n*T + T-1
   uint16_t* out;              // bf16 [tokens, C]
   uint32_t flags;
   int32_t heads;

@@ -209,8 +209,9 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   const int C3 = 3 * C;
   const int n = static_cast<int>(blockIdx.x) / H;
   const int h = static_cast<int>(blockIdx.x) % H;
-  const int32_t tb = p.cu_seqlens[n];
-  const int32_t te = p.cu_seqlens[n + 1];
+  const int32_t tb = p.cu_seqlens ? p.cu_seqlens[n] : n * p.tokens_per_row;
+  const int32_t te =
+      p.cu_seqlens ? p.cu_seqlens[n + 1] : (n + 1) * p.tokens_per_row;
   const int len = te > tb ? te - tb : 0;
   if (len == 0) return;
   const int32_t slot = p.state_idx[n];

@@ -796,6 +796,39 @@ Params base_params(const kda_dims* d, const void* qkv, const float* conv_w,
   return p;
 }
 
+// From this many tokens per row on, kda_decode_tokens runs the chunked
+// (matrix-core) kernel: measured on MI355X with 256 rows x 48 heads, the
+// token-by-token kernel takes 1073 us at T = 16 against 934 us chunked
+// (1911 against 1224 at T = 32), and is faster below 16.
+constexpr int32_t kChunkedMinTokens = 16;
+
+KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
+                            int32_t tokens_per_row, const void* qkv,
+                            const float* conv_w, void* conv_state,
+                            float* rec_state, const float* g,
+                            const float* beta, const void* gate,
+                            const float* norm_w, const int32_t* state_idx,
+                            void* out) {
+  KdaChunkedArgs a{};
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.conv_w = conv_w;
+  a.conv_state = static_cast<uint16_t*>(conv_state);
+  a.rec_state = rec_state;
+  a.g = g;
+  a.beta = beta;
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.norm_w = norm_w;
+  a.state_idx = state_idx;
+  a.cu_seqlens = cu_seqlens;
+  a.tokens_per_row = tokens_per_row;
+  a.out = static_cast<uint16_t*>(out);
+  a.flags = d->flags;
+  a.heads = d->num_heads;
+  a.num_slots = d->num_slots;
+  a.eps = d->norm_eps;
+  return a;
+}
+
 template <bool kRaw>
 kda_status launch(const kda_dims* d, const Params& p, void* hip_stream) {
   int dev = -1;
@@ -912,8 +945,20 @@ kda_status kda_decode_tokens(const kda_dims* d, int32_t tokens,
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return KDA_ERR_DEVICE;
-  const dim3 grid(static_cast<unsigned>(d->batch * d->num_heads));
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (tokens >= kChunkedMinTokens) {
+    // [B, T, ...] token-major buffers are the prefill layout with row n
+    // owning tokens n*T .. n*T + T-1
+    if (static_cast<int64_t>(d->batch) * tokens > INT32_MAX)
+      return KDA_ERR_INVALID_ARG;
+    const KdaChunkedArgs a =
+        chunked_args(d, nullptr, tokens, qkv, conv_w, conv_state, rec_state,
+                     g, beta, gate, norm_w, state_idx, out);
+    return kda_chunked_prefill_launch(a, d->batch, stream) == hipSuccess
+               ? KDA_OK
+               : KDA_ERR_LAUNCH;
+  }
+  const dim3 grid(static_cast<unsigned>(d->batch * d->num_heads));
   if (d->flags & KDA_OUTPUT_NORM)
     hipLaunchKernelGGL(kda_decode_tokens_kernel<true>, grid, dim3(kThreads), 0,
                        stream, p, tokens);
@@ -995,22 +1040,9 @@ kda_status kda_prefill_chunked(const kda_dims* d, const int32_t* cu_seqlens,
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return KDA_ERR_DEVICE;
-  KdaChunkedArgs a{};
-  a.qkv = static_cast<const uint16_t*>(qkv);
-  a.conv_w = conv_w;
-  a.conv_state = static_cast<uint16_t*>(conv_state);
-  a.rec_state = rec_state;
-  a.g = g;
-  a.beta = beta;
-  a.gate = static_cast<const uint16_t*>(gate);
-  a.norm_w = norm_w;
-  a.state_idx = state_idx;
-  a.cu_seqlens = cu_seqlens;
-  a.out = static_cast<uint16_t*>(out);
-  a.flags = d->flags;
-  a.heads = d->num_heads;
-  a.num_slots = d->num_slots;
-  a.eps = d->norm_eps;
+  const KdaChunkedArgs a =
+      chunked_args(d, cu_seqlens, 0, qkv, conv_w, conv_state, rec_state, g,
+                   beta, gate, norm_w, state_idx, out);
   return kda_chunked_prefill_launch(a, d->batch,
                                     static_cast<hipStream_t>(hip_stream)) ==
                  hipSuccess
