@@ -224,6 +224,43 @@ kda_status kda_prefill_chunked(const kda_dims* dims, const int32_t* cu_seqlens,
                                void* hip_stream);
 
 /*
+ * The same prefill in two passes over the device-side chunk table (the
+ * structure of the page "PR #51862 完整报告 -- Remove prefill pipeline
+ * stall in chunk KDA": chunk kernels driven by chunk_indices/chunk_offsets
+ * built on the device).  Pass 1 computes, for every (chunk, head) of every
+ * sequence in parallel, everything that does not depend on the state (conv,
+ * q/k normalisation, decay tables, the A / B products and the 16 x 16
+ * inverse) into `workspace`; pass 2 carries each (sequence, head) state
+ * through its chunks.  Same result as kda_prefill_chunked up to rounding.
+ *   chunk_indices  device int32 [total, 2], chunk_offsets device int64
+ *                  [N + 1]: from kda_chunk_metadata(cu_seqlens, N, 16, ...)
+ *                  (chunk size 16).
+ *   max_chunks     >= the total chunk count (kda_chunk_count on a host copy
+ *                  of cu_seqlens, or a bound such as tokens/16 + N); sizes
+ *                  the first pass's grid.
+ *   workspace      device, 16-byte aligned, caller-owned, at least
+ *                  kda_prefill_chunks_workspace_bytes(dims, max_chunks).
+ * A chunk table that does not match cu_seqlens, or holds more than
+ * max_chunks chunks, cannot be detected without a synchronisation: the
+ * kernels then skip what lies outside the workspace (outputs of those
+ * sequences are left as they were) and never access memory out of range.
+ * Other arguments, flags and status codes as kda_prefill; a workspace too
+ * small or max_chunks < 0 is KDA_ERR_INVALID_ARG.
+ */
+uint64_t kda_prefill_chunks_workspace_bytes(const kda_dims* dims,
+                                            int64_t max_chunks);
+kda_status kda_prefill_chunks(const kda_dims* dims, const int32_t* cu_seqlens,
+                              const int32_t* chunk_indices,
+                              const int64_t* chunk_offsets, int64_t max_chunks,
+                              const void* qkv, const float* conv_w,
+                              void* conv_state, float* rec_state,
+                              const float* g, const float* beta,
+                              const void* gate, const float* norm_w,
+                              const int32_t* state_idx, void* out,
+                              void* workspace, uint64_t workspace_bytes,
+                              void* hip_stream);
+
+/*
  * Device-side chunk bookkeeping of a variable-length batch (page "PR
  * #51862 完整报告", implementation item 2 and the kda_metadata.py excerpt):
  * sequence i of cu_seqlens (device int32 [num_seqs + 1]) gets

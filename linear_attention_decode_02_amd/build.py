@@ -9,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "kda_decode.hip"),
            os.path.join(PKG, "csrc", "kda_chunked.hip"),
+           os.path.join(PKG, "csrc", "kda_chunk_pass.hip"),
            os.path.join(PKG, "csrc", "kda_probe.hip")]
 LIB = os.path.join(PKG, "libkda_decode.so")
 

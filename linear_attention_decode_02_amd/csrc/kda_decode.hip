@@ -46,6 +46,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "kda_chunk_pass.h"
 #include "kda_chunked.h"
 #include "kda_decode.h"
 
@@ -1045,6 +1046,72 @@ kda_status kda_prefill_chunked(const kda_dims* d, const int32_t* cu_seqlens,
                    beta, gate, norm_w, state_idx, out);
   return kda_chunked_prefill_launch(a, d->batch,
                                     static_cast<hipStream_t>(hip_stream)) ==
+                 hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+uint64_t kda_prefill_chunks_workspace_bytes(const kda_dims* d,
+                                            int64_t max_chunks) {
+  if (!d || d->num_heads < 1 || max_chunks < 0) return 0;
+  return static_cast<uint64_t>(max_chunks) *
+         static_cast<uint64_t>(d->num_heads) * kda_pass_record_bytes();
+}
+
+kda_status kda_prefill_chunks(const kda_dims* d, const int32_t* cu_seqlens,
+                              const int32_t* chunk_indices,
+                              const int64_t* chunk_offsets, int64_t max_chunks,
+                              const void* qkv, const float* conv_w,
+                              void* conv_state, float* rec_state,
+                              const float* g, const float* beta,
+                              const void* gate, const float* norm_w,
+                              const int32_t* state_idx, void* out,
+                              void* workspace, uint64_t workspace_bytes,
+                              void* hip_stream) {
+  kda_status st = check_dims(d, kPlainFlags);
+  if (st != KDA_OK) return st;
+  if (max_chunks < 0 ||
+      max_chunks * static_cast<int64_t>(d->num_heads) > INT32_MAX)
+    return KDA_ERR_INVALID_ARG;
+  if (d->batch == 0) return KDA_OK;
+  if (!cu_seqlens || !chunk_offsets || !g || !beta ||
+      (max_chunks > 0 && (!chunk_indices || !workspace)))
+    return KDA_ERR_INVALID_ARG;
+  if (workspace_bytes < kda_prefill_chunks_workspace_bytes(d, max_chunks))
+    return KDA_ERR_INVALID_ARG;
+  if (!aligned16(cu_seqlens) || !aligned16(chunk_offsets) ||
+      (chunk_indices && !aligned16(chunk_indices)) ||
+      (workspace && !aligned16(workspace)) || !aligned16(g) ||
+      !aligned16(beta))
+    return KDA_ERR_MISALIGNED;
+  st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
+                    state_idx, out);
+  if (st != KDA_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
+    return KDA_ERR_DEVICE;
+  KdaPassArgs a{};
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.conv_w = conv_w;
+  a.conv_state = static_cast<uint16_t*>(conv_state);
+  a.rec_state = rec_state;
+  a.g = g;
+  a.beta = beta;
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.norm_w = norm_w;
+  a.state_idx = state_idx;
+  a.cu_seqlens = cu_seqlens;
+  a.chunk_indices = chunk_indices;
+  a.chunk_offsets = chunk_offsets;
+  a.workspace = static_cast<float*>(workspace);
+  a.out = static_cast<uint16_t*>(out);
+  a.max_chunks = max_chunks;
+  a.num_seqs = d->batch;
+  a.flags = d->flags;
+  a.heads = d->num_heads;
+  a.num_slots = d->num_slots;
+  a.eps = d->norm_eps;
+  return kda_chunk_pass_launch(a, static_cast<hipStream_t>(hip_stream)) ==
                  hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;

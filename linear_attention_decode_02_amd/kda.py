@@ -74,6 +74,13 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill.argtypes = [ctypes.POINTER(Dims)] + [P] * 12
         L.kda_prefill_chunked.restype = ctypes.c_int
         L.kda_prefill_chunked.argtypes = [ctypes.POINTER(Dims)] + [P] * 12
+        L.kda_prefill_chunks_workspace_bytes.restype = ctypes.c_uint64
+        L.kda_prefill_chunks_workspace_bytes.argtypes = [
+            ctypes.POINTER(Dims), ctypes.c_int64]
+        L.kda_prefill_chunks.restype = ctypes.c_int
+        L.kda_prefill_chunks.argtypes = (
+            [ctypes.POINTER(Dims), P, P, P, ctypes.c_int64] + [P] * 10 +
+            [P, ctypes.c_uint64, P])
         L.kda_chunk_metadata.restype = ctypes.c_int
         L.kda_chunk_metadata.argtypes = [P, ctypes.c_int32, ctypes.c_int32,
                                          P, P, P]
@@ -295,6 +302,65 @@ def kda_prefill(cu_seqlens, qkv, conv_w, conv_state, rec_state, g, beta,
             _ptr(conv_state), _ptr(rec_state), _ptr(g), _ptr(beta),
             _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
             _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+
+
+PREFILL_CHUNK = 16   # chunk size of the chunked prefill paths
+
+
+def prefill_chunks_workspace_bytes(heads: int, max_chunks: int) -> int:
+    """Bytes of workspace kda_prefill_chunks needs for up to max_chunks
+    chunks of 16 tokens."""
+    d = Dims(1, heads, HEAD_DIM, CONV_WIDTH, 1, 0, 1e-5)
+    return int(lib().kda_prefill_chunks_workspace_bytes(ctypes.byref(d),
+                                                        int(max_chunks)))
+
+
+def kda_prefill_chunks(cu_seqlens, chunk_indices, chunk_offsets,
+                       max_chunks: int, qkv, conv_w, conv_state, rec_state, g,
+                       beta, gate, norm_w, state_idx, out, workspace, *,
+                       norm: bool = True, eps: float = 1e-5,
+                       variants: int = 0, stream=None) -> None:
+    """Variable-length prefill in two passes over the device chunk table
+    (chunk_metadata(cu_seqlens, 16)): per-chunk operands of all chunks in
+    parallel into ``workspace`` (a uint8 device tensor of at least
+    prefill_chunks_workspace_bytes bytes), then each sequence's state
+    through its chunks.  Other arguments as kda_prefill."""
+    if rec_state.dim() != 4 or qkv.dim() != 2:
+        raise ValueError("rec_state [S, H, 128, 128], qkv [tokens, 3C]")
+    S, H, D, D2 = rec_state.shape
+    C = H * D
+    N = state_idx.shape[0]
+    tokens = qkv.shape[0]
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    _check(chunk_offsets, "chunk_offsets", torch.int64, (N + 1,))
+    _check(chunk_indices, "chunk_indices", torch.int32,
+           (chunk_indices.shape[0], 2))
+    _check(workspace, "workspace", torch.uint8, (workspace.numel(),))
+    _check(rec_state, "rec_state", torch.float32, (S, H, D, D2))
+    _check(qkv, "qkv", torch.bfloat16, (tokens, 3 * C))
+    _check(conv_w, "conv_w", torch.float32, (3, CONV_WIDTH, C))
+    cs_shape = ((S, CONV_WIDTH - 1, 3 * C) if variants & KDA_CONV_TAP_MAJOR
+                else (S, 3 * C, CONV_WIDTH - 1))
+    _check(conv_state, "conv_state", torch.bfloat16, cs_shape)
+    _check(state_idx, "state_idx", torch.int32, (N,))
+    _check(g, "g", torch.float32, (tokens, H, D))
+    _check(beta, "beta", torch.float32, (tokens, H))
+    _check(out, "out", torch.bfloat16, (tokens, C))
+    if norm:
+        _check(gate, "gate", torch.bfloat16, (tokens, C))
+        _check(norm_w, "norm_w", torch.float32, (D,))
+    dims = Dims(N, H, D, CONV_WIDTH, S,
+                (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
+    with torch.cuda.device(qkv.device):
+        rc = lib().kda_prefill_chunks(
+            ctypes.byref(dims), _ptr(cu_seqlens), _ptr(chunk_indices),
+            _ptr(chunk_offsets), int(max_chunks), _ptr(qkv), _ptr(conv_w),
+            _ptr(conv_state), _ptr(rec_state), _ptr(g), _ptr(beta),
+            _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
+            _ptr(state_idx), _ptr(out), _ptr(workspace),
+            int(workspace.numel()), _stream(stream, qkv.device))
     if rc != KDA_OK:
         raise KdaError(rc, status_string(rc))
 

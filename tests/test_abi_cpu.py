@@ -219,6 +219,21 @@ def test_prefill_and_metadata_argument_checks():
         assert fn(ctypes.byref(d), *q[:11], None) == 1
         assert fn(ctypes.byref(dims(flags=0x21)), *p[:11], None) == 1
         assert fn(ctypes.byref(dims(batch=0)), *p[:11], None) == 0
+    # kda_prefill_chunks: cu, indices, offsets, max, 10 tensors, ws, bytes
+    need = L.kda_prefill_chunks_workspace_bytes(ctypes.byref(d), 5)
+    assert need == 5 * 12 * 36928
+    assert L.kda_prefill_chunks_workspace_bytes(ctypes.byref(d), -1) == 0
+    args = [FAKE, FAKE, FAKE, 5] + [FAKE] * 10 + [FAKE, need, None]
+    assert L.kda_prefill_chunks(ctypes.byref(d), *args) == 4
+    bad = list(args); bad[-2] = need - 1                  # workspace short
+    assert L.kda_prefill_chunks(ctypes.byref(d), *bad) == 1
+    bad = list(args); bad[3] = -1                         # max_chunks
+    assert L.kda_prefill_chunks(ctypes.byref(d), *bad) == 1
+    bad = list(args); bad[2] = None                       # chunk_offsets
+    assert L.kda_prefill_chunks(ctypes.byref(d), *bad) == 1
+    bad = list(args); bad[-3] = FAKE + 8                  # workspace align
+    assert L.kda_prefill_chunks(ctypes.byref(d), *bad) == 3
+    assert L.kda_prefill_chunks(ctypes.byref(dims(batch=0)), *args) == 0
     assert L.kda_chunk_metadata(FAKE, 3, 64, FAKE, FAKE, None) == 4
     assert L.kda_chunk_metadata(FAKE, -1, 64, FAKE, FAKE, None) == 1
     assert L.kda_chunk_metadata(FAKE, 3, 0, FAKE, FAKE, None) == 1

@@ -12,10 +12,12 @@ import pytest
 import torch
 
 import oracle as O
-from linear_attention_decode_02_amd import synth
+from linear_attention_decode_02_amd import kda, synth
 
 import _parity as P
 from test_gpu_prefill import check_prefill, prefill_case, run_prefill
+
+DEV = "cuda:0"
 
 pytestmark = [
     pytest.mark.gpu,
@@ -23,7 +25,44 @@ pytestmark = [
 ]
 
 
-def run_and_check(w, inp, cu, H, flags=0, norm=True, label=""):
+def run_two_pass(w, inp, cu, variants=0):
+    """kda_prefill_chunks: the chunk table from kda_chunk_metadata (chunk
+    size 16, no host synchronisation), the workspace sized for the exact
+    chunk count."""
+    t = synth.to_torch(inp, DEV)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    idx, off = kda.chunk_metadata(cu_d, kda.PREFILL_CHUNK,
+                                  cu_seqlens_host=torch.from_numpy(cu))
+    max_chunks = int(idx.shape[0])
+    H = w.heads
+    ws = torch.empty(max(kda.prefill_chunks_workspace_bytes(H, max_chunks),
+                         16), dtype=torch.uint8, device=DEV)
+    tokens = inp["qkv"].shape[0]
+    out = torch.full((tokens, w.channels), float("nan"), dtype=torch.bfloat16,
+                     device=DEV)
+    kda.kda_prefill_chunks(cu_d, idx, off, max_chunks, t["qkv"], t["conv_w"],
+                           t["conv_state"], t["rec_state"], t["g"], t["beta"],
+                           t["gate"] if w.norm else None,
+                           t["norm_w"] if w.norm else None, t["state_idx"],
+                           out, ws, norm=w.norm, eps=w.eps, variants=variants)
+    torch.cuda.synchronize()
+    return {"out": synth.bf16_bits(out),
+            "conv_state": synth.bf16_bits(t["conv_state"]),
+            "rec_state": t["rec_state"].cpu().numpy()}
+
+
+@pytest.fixture(params=["fused", "two_pass"])
+def path(request):
+    return request.param
+
+
+def run_path(path, w, inp, cu, variants=0):
+    if path == "two_pass":
+        return run_two_pass(w, inp, cu, variants)
+    return run_prefill(w, inp, cu, variants=variants, chunked=True)
+
+
+def run_and_check(w, inp, cu, H, flags=0, norm=True, label="", path="fused"):
     """Oracle in the channel-major conv-state layout; with
     CONV_TAP_MAJOR the GPU gets the transposed pool and its result is
     transposed back before the comparison."""
@@ -36,7 +75,7 @@ def run_and_check(w, inp, cu, H, flags=0, norm=True, label=""):
     if tap:
         gin = dict(inp, conv_state=np.ascontiguousarray(
             inp["conv_state"].transpose(0, 2, 1)))
-    got = run_prefill(w, gin, cu, variants=flags, chunked=True)
+    got = run_path(path, w, gin, cu, variants=flags)
     if tap:
         got["conv_state"] = np.ascontiguousarray(
             got["conv_state"].transpose(0, 2, 1))
@@ -50,9 +89,9 @@ def run_and_check(w, inp, cu, H, flags=0, norm=True, label=""):
     ([40, 3, 0, 25, 16], 48, False, (1,)),
     ([64, 65, 1, 17, 0, 9], 96, True, (3,)),
 ])
-def test_chunked_parity_ragged(lens, H, norm, null):
+def test_chunked_parity_ragged(lens, H, norm, null, path):
     w, inp, cu = prefill_case(170 + H, lens, H, norm=norm, null=null)
-    run_and_check(w, inp, cu, H, norm=norm, label="ragged")
+    run_and_check(w, inp, cu, H, norm=norm, label="ragged", path=path)
 
 
 FLAG_CASES = [
@@ -64,26 +103,27 @@ FLAG_CASES = [
 
 @pytest.mark.parametrize("name,flags", FLAG_CASES,
                          ids=[f[0] for f in FLAG_CASES])
-def test_chunked_parity_flags(name, flags):
+def test_chunked_parity_flags(name, flags, path):
     lens, H = [19, 0, 5, 48, 33], 24
     w, inp, cu = prefill_case(180, lens, H, null=(2,))
-    got, _ = run_and_check(w, inp, cu, H, flags=flags, label=name)
+    got, _ = run_and_check(w, inp, cu, H, flags=flags, label=name, path=path)
     if flags & O.NO_CONV_UPDATE:
         assert np.array_equal(got["conv_state"], inp["conv_state"])
 
 
 @pytest.mark.parametrize("l2", [False, True])
-def test_chunked_fresh_sequences_long(l2):
+def test_chunked_fresh_sequences_long(l2, path):
     """Fresh states, sequences up to 300 tokens, 48 heads; with q/k L2
     normalisation the reference conv-weight distribution is used."""
     lens = [300, 17, 128, 64, 1, 200]
     flags = O.QK_L2NORM if l2 else 0
     w, inp, cu = prefill_case(90, lens, 48, zero_state=True,
                               conv_w_sigma=0.5 if l2 else 0.05)
-    run_and_check(w, inp, cu, 48, flags=flags, label=f"long l2={l2}")
+    run_and_check(w, inp, cu, 48, flags=flags, label=f"long l2={l2}",
+                  path=path)
 
 
-def test_chunked_large_decay_takes_exact_path():
+def test_chunked_large_decay_takes_exact_path(path):
     """Tokens whose decay sums past 80 inside a chunk (g about -9 per
     channel for some tokens): those chunks form A and B entry by entry;
     the others keep the factored matrix-core form."""
@@ -93,11 +133,11 @@ def test_chunked_large_decay_takes_exact_path():
     g[0:16] -= 9.0          # sequence 0, first chunk: cumulative decay > 80
     g[48 + 16:48 + 20] -= 30.0   # sequence 1, second chunk
     inp["g"] = np.ascontiguousarray(g)
-    got, ref = run_and_check(w, inp, cu, H, label="large decay")
+    got, ref = run_and_check(w, inp, cu, H, label="large decay", path=path)
     assert np.isfinite(got["rec_state"]).all()
 
 
-def test_chunked_prefill_16_sequences_h48_full_size():
+def test_chunked_prefill_16_sequences_h48_full_size(path):
     """The prefill measured by bench.py --prefill: 16 sequences of seeded
     log-uniform lengths (5987 tokens), 48 heads, q/k L2-normalised, fresh
     states; every output and state element against the oracle."""
@@ -105,7 +145,8 @@ def test_chunked_prefill_16_sequences_h48_full_size():
     lens = (np.exp(rng.uniform(0, np.log(4096), 16)).astype(np.int64) + 1)
     w, inp, cu = prefill_case(7, lens.tolist(), 48, zero_state=True,
                               conv_w_sigma=0.5)
-    run_and_check(w, inp, cu, 48, flags=O.QK_L2NORM, label="bench size")
+    run_and_check(w, inp, cu, 48, flags=O.QK_L2NORM, label="bench size",
+                  path=path)
 
 
 def test_chunked_matches_sequential_kernel():
@@ -119,3 +160,47 @@ def test_chunked_matches_sequential_kernel():
     do = np.abs(P.bf16_to_f32(a["out"]) - P.bf16_to_f32(b["out"])).max()
     print(f"[chunked vs sequential] state {d:.3g} out {do:.3g}", flush=True)
     assert d <= 1e-4
+
+
+def test_two_pass_matches_fused():
+    """The two chunked paths compute the same chunk form: they agree far
+    inside the oracle bars."""
+    lens, H = [100, 3, 57, 16, 1, 0, 33], 48
+    w, inp, cu = prefill_case(210, lens, H, null=(4,))
+    a = run_prefill(w, inp, cu, chunked=True)
+    b = run_two_pass(w, inp, cu)
+    assert np.array_equal(a["conv_state"], b["conv_state"])
+    d = np.abs(a["rec_state"] - b["rec_state"]).max()
+    print(f"[two-pass vs fused] state {d:.3g}", flush=True)
+    assert d <= 1e-5
+
+
+def test_two_pass_table_larger_than_workspace_is_skipped():
+    """max_chunks below the table's total: the kernels skip the sequences
+    whose records would lie outside the workspace (outputs left as they
+    were, states untouched) and the others are still computed."""
+    lens, H = [40, 20], 12   # 3 + 2 chunks
+    w, inp, cu = prefill_case(220, lens, H)
+    t = synth.to_torch(inp, DEV)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    idx, off = kda.chunk_metadata(cu_d, kda.PREFILL_CHUNK,
+                                  cu_seqlens_host=torch.from_numpy(cu))
+    max_chunks = 3                     # room for sequence 0 only
+    ws = torch.empty(kda.prefill_chunks_workspace_bytes(H, max_chunks),
+                     dtype=torch.uint8, device=DEV)
+    tokens = inp["qkv"].shape[0]
+    out = torch.full((tokens, w.channels), float("nan"), dtype=torch.bfloat16,
+                     device=DEV)
+    kda.kda_prefill_chunks(cu_d, idx, off, max_chunks, t["qkv"], t["conv_w"],
+                           t["conv_state"], t["rec_state"], t["g"], t["beta"],
+                           t["gate"], t["norm_w"], t["state_idx"], out, ws,
+                           eps=w.eps)
+    torch.cuda.synchronize()
+    got = synth.bf16_bits(out)
+    assert np.all(np.isnan(P.bf16_to_f32(got[40:])))   # sequence 1 skipped
+    s1 = inp["state_idx"][1]
+    assert np.array_equal(t["rec_state"][s1].cpu().numpy(),
+                          inp["rec_state"][s1])
+    ref = O.prefill(inp, cu, heads=H, eps=w.eps)
+    P.check_output(got[:40], ref["y"][:40], np.full(40, inp["state_idx"][0]),
+                   w.num_slots, H)
