@@ -325,7 +325,10 @@ def prefill(inp: dict, cu_seqlens, *, heads: int, head_dim: int = 128,
     """Variable-length prefill on host arrays: the tokens of sequence n
     (cu_seqlens[n] .. cu_seqlens[n+1]-1 of the token-major qkv [tokens, 3C],
     g [tokens, H, D], beta [tokens, H], gate [tokens, C]) run through the
-    single-token step in order on slot state_idx[n].  fp32."""
+    single-token step in order on slot state_idx[n].  fp32.  Optional
+    ``inp`` entries as in ``decode``, token-major: "conv_bias" [3C], and the
+    raw gates "raw_g" [tokens, H, D] / "raw_beta" [tokens, H] / "A_log" /
+    "dt_bias" / "lower_bound" (then "g" and "beta" are not read)."""
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     N = cu.size - 1
     C = heads * head_dim
@@ -336,30 +339,50 @@ def prefill(inp: dict, cu_seqlens, *, heads: int, head_dim: int = 128,
     rs = np.array(inp["rec_state"], dtype=np.float32, order="C", copy=True)
     S = cs.shape[0]
     conv_w = np.ascontiguousarray(inp["conv_w"], dtype=np.float32)
-    g = np.ascontiguousarray(inp["g"], dtype=np.float32)
-    beta = np.ascontiguousarray(inp["beta"], dtype=np.float32)
+    raw = inp.get("raw_g") is not None
+    g = None if raw else np.ascontiguousarray(inp["g"], dtype=np.float32)
+    beta = None if raw else np.ascontiguousarray(inp["beta"], dtype=np.float32)
     gate = np.ascontiguousarray(inp["gate"], dtype=np.uint16)
     norm_w = np.ascontiguousarray(inp["norm_w"], dtype=np.float32)
     idx = np.ascontiguousarray(inp["state_idx"], dtype=np.int32)
-    assert g.shape == (tokens, heads, head_dim) and beta.shape == (tokens,
-                                                                   heads)
+    if not raw:
+        assert g.shape == (tokens, heads, head_dim) and beta.shape == (
+            tokens, heads)
     assert idx.shape == (N,)
+    keep = []
+
+    def opt(key, dt, shape):
+        a = inp.get(key)
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=dt)
+        assert a.shape == shape, (key, a.shape, shape)
+        keep.append(a)
+        return a.ctypes.data
+
+    ex = _Extras(opt("conv_bias", np.float32, (3 * C,)),
+                 opt("raw_g", np.uint16, (tokens, heads, head_dim)),
+                 opt("raw_beta", np.uint16, (tokens, heads)),
+                 opt("A_log", np.float32, (heads,)),
+                 opt("dt_bias", np.float32, (C,)),
+                 float(inp.get("lower_bound", 0.0)))
     out = np.zeros((tokens, C), np.uint16)
     y = np.zeros((tokens, C), np.float32)
     L = lib()
-    if not hasattr(L.kda_oracle_prefill_f32, "_typed"):
+    if not hasattr(L.kda_oracle_prefill_ext_f32, "_typed"):
         P = ctypes.c_void_p
-        L.kda_oracle_prefill_f32.restype = ctypes.c_int
-        L.kda_oracle_prefill_f32.argtypes = ([ctypes.POINTER(_Dims)] + [P] * 12
-                                             + [ctypes.c_int])
-        L.kda_oracle_prefill_f32._typed = True
-    assert not flags & (CONV_TAP_MAJOR | BOUNDED_GATE), "not for prefill"
+        L.kda_oracle_prefill_ext_f32.restype = ctypes.c_int
+        L.kda_oracle_prefill_ext_f32.argtypes = (
+            [ctypes.POINTER(_Dims)] + [P] * 12 + [ctypes.c_int,
+                                                  ctypes.POINTER(_Extras)])
+        L.kda_oracle_prefill_ext_f32._typed = True
+    assert not flags & CONV_TAP_MAJOR, "channel-major conv state only"
     d = _Dims(N, heads, head_dim, conv_width, S,
               (NORM if norm else 0) | (flags & ~NORM), eps)
-    rc = L.kda_oracle_prefill_f32(
+    rc = L.kda_oracle_prefill_ext_f32(
         ctypes.byref(d), _ptr(cu), _ptr(qkv), _ptr(conv_w), _ptr(cs), _ptr(rs),
         _ptr(g), _ptr(beta), _ptr(gate), _ptr(norm_w), _ptr(idx), _ptr(out),
-        _ptr(y), int(nthreads or os.cpu_count() or 1))
+        _ptr(y), int(nthreads or os.cpu_count() or 1), ctypes.byref(ex))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (status {rc})")
     return {"out": out, "y": y, "conv_state": cs, "rec_state": rs}

@@ -334,8 +334,9 @@ int prefill(const Dims* d, const int32_t* cu, const uint16_t* qkv,
             const float* conv_w, uint16_t* conv_state, T* rec_state,
             const float* g, const float* beta, const uint16_t* gate,
             const float* norm_w, const int32_t* state_idx, uint16_t* out,
-            T* y_out, int nthreads) {
+            T* y_out, int nthreads, const Extras* ex) {
   if (!d || d->batch < 0 || !cu) return ORC_ERR_INVALID_ARG;
+  const bool raw_gates = ex && ex->raw_g;
   const int64_t N = d->batch;
   const int64_t H = d->num_heads, D = d->head_dim;
   const int64_t C = H * D;
@@ -348,12 +349,22 @@ int prefill(const Dims* d, const int32_t* cu, const uint16_t* qkv,
       const int64_t tok = cu[n] + t;
       Dims one = *d;
       one.batch = 1;
+      // token tok's rows of the per-token gate inputs
+      Extras tex{};
+      if (ex) {
+        tex = *ex;
+        if (raw_gates) {
+          tex.raw_g = ex->raw_g + tok * H * D;
+          tex.raw_beta = ex->raw_beta ? ex->raw_beta + tok * H : nullptr;
+        }
+      }
       const int rc = decode<T>(
           &one, qkv + tok * 3 * C, conv_w, conv_state, rec_state,
-          g + tok * H * D, beta + tok * H,
+          raw_gates ? nullptr : g + tok * H * D,
+          raw_gates ? nullptr : beta + tok * H,
           (d->flags & F_NORM) ? gate + tok * C : nullptr, norm_w, &slot,
           out + tok * C, y_out ? y_out + tok * C : nullptr, nthreads,
-          nullptr);
+          ex ? &tex : nullptr);
       if (rc != ORC_OK) return rc;
     }
   }
@@ -445,7 +456,23 @@ int kda_oracle_prefill_f32(const kda_oracle_dims* d, const int32_t* cu_seqlens,
                            float* y_out, int nthreads) {
   return prefill<float>(reinterpret_cast<const Dims*>(d), cu_seqlens, qkv,
                         conv_w, conv_state, rec_state, g, beta, gate, norm_w,
-                        state_idx, out, y_out, nthreads);
+                        state_idx, out, y_out, nthreads, nullptr);
+}
+
+// The same with the extra inputs of kda_oracle_decode_ext_f32, token-major:
+// raw_g [tokens, H, D] and raw_beta [tokens, H] (g and beta then unread).
+int kda_oracle_prefill_ext_f32(const kda_oracle_dims* d,
+                               const int32_t* cu_seqlens, const uint16_t* qkv,
+                               const float* conv_w, uint16_t* conv_state,
+                               float* rec_state, const float* g,
+                               const float* beta, const uint16_t* gate,
+                               const float* norm_w, const int32_t* state_idx,
+                               uint16_t* out, float* y_out, int nthreads,
+                               const kda_oracle_extras* ex) {
+  return prefill<float>(reinterpret_cast<const Dims*>(d), cu_seqlens, qkv,
+                        conv_w, conv_state, rec_state, g, beta, gate, norm_w,
+                        state_idx, out, y_out, nthreads,
+                        reinterpret_cast<const Extras*>(ex));
 }
 
 // Stage 1 over nch channels: channel c has W-1 stored inputs, tap t at

@@ -121,3 +121,74 @@ def test_prefill_empty_sequence_and_null_slot_leave_state():
     assert np.array_equal(got["rec_state"], inp["rec_state"])
     assert np.array_equal(got["conv_state"], inp["conv_state"])
     assert np.all(got["out"] == 0)
+
+
+def _add_raw_gates(inp, H, D, seed, bias=True):
+    """Raw gate operands for every token (bf16 raw_g / raw_beta, A_log,
+    dt_bias) and optionally a conv bias."""
+    rng = np.random.default_rng(seed)
+    tokens = inp["qkv"].shape[0]
+    inp = dict(inp)
+    inp.update(
+        raw_g=synth.to_bf16_bits(
+            rng.normal(0, 2, (tokens, H, D)).astype(np.float32)),
+        raw_beta=synth.to_bf16_bits(
+            rng.normal(0, 1, (tokens, H)).astype(np.float32)),
+        A_log=rng.normal(0, 0.5, H).astype(np.float32),
+        dt_bias=rng.normal(0, 0.5, H * D).astype(np.float32))
+    if bias:
+        inp["conv_bias"] = rng.normal(0, 0.3, 3 * H * D).astype(np.float32)
+    return inp
+
+
+@pytest.mark.parametrize("bounded", [False, True])
+def test_prefill_raw_gates_equals_single_token_calls(bounded):
+    """Token t of the prefill reads row t of raw_g / raw_beta: the prefill
+    equals single-token raw-gate steps, token by token, bit for bit."""
+    H, D = 12, 128
+    w, inp, cu = _tokens_case(4, [5, 0, 3], H)
+    inp = _add_raw_gates(inp, H, D, 40)
+    flags = 0
+    if bounded:
+        inp["lower_bound"] = -3.0
+        flags = O.BOUNDED_GATE
+    got = O.prefill(inp, cu, heads=H, flags=flags)
+    cs, rs = inp["conv_state"].copy(), inp["rec_state"].copy()
+    for n in range(len(cu) - 1):
+        for tok in range(cu[n], cu[n + 1]):
+            step = dict(inp, conv_state=cs, rec_state=rs,
+                        state_idx=inp["state_idx"][n:n + 1].copy())
+            for k in ("qkv", "gate", "raw_g", "raw_beta"):
+                step[k] = np.ascontiguousarray(inp[k][tok:tok + 1])
+            r = O.decode(step, heads=H, flags=flags, inplace=True)
+            assert np.array_equal(r["out"][0], got["out"][tok])
+    assert np.array_equal(rs, got["rec_state"])
+    assert np.array_equal(cs, got["conv_state"])
+
+
+def test_prefill_raw_gates_match_activated_gates():
+    """The raw-gate prefill against the plain prefill fed the gates that
+    the per-channel gate function computes (in float64) for every token:
+    the same up to the fp32 rounding of the activation."""
+    H, D = 12, 128
+    w, inp, cu = _tokens_case(5, [6, 2], H)
+    inp = _add_raw_gates(inp, H, D, 50, bias=False)
+    tokens = inp["qkv"].shape[0]
+    g = np.empty((tokens, H, D), np.float32)
+    beta = np.empty((tokens, H), np.float32)
+    for t in range(tokens):
+        for h in range(H):
+            gg, bb = O.raw_gates_stage(inp["raw_g"][t, h], inp["A_log"][h],
+                                       inp["dt_bias"][h * D:(h + 1) * D],
+                                       int(inp["raw_beta"][t, h]))
+            g[t, h], beta[t, h] = gg, bb
+    raw = O.prefill(inp, cu, heads=H)
+    plain = dict(inp, g=g, beta=beta)
+    for k in ("raw_g", "raw_beta", "A_log", "dt_bias"):
+        plain.pop(k)
+    ref = O.prefill(plain, cu, heads=H)
+    assert np.array_equal(raw["conv_state"], ref["conv_state"])
+    scale = max(1.0, np.abs(ref["rec_state"]).max())
+    assert np.abs(raw["rec_state"] - ref["rec_state"]).max() <= 1e-5 * scale
+    assert np.abs(raw["y"] - ref["y"]).max() <= 1e-4 * max(
+        1.0, np.abs(ref["y"]).max())
