@@ -77,7 +77,7 @@ typedef enum kda_status {
                                     1e-6) (not on the page)                  */
 #define KDA_GATE_SILU 0x10u      /* output gate activation x*sigmoid(x)
                                     instead of sigmoid(x)                    */
-#define KDA_BOUNDED_GATE 0x20u   /* kda_decode_raw_gates only: bounded gate */
+#define KDA_BOUNDED_GATE 0x20u   /* raw-gate entry points only: bounded gate */
 
 typedef struct kda_dims {
   int32_t batch;      /* B >= 0 rows, one decode token each                 */
@@ -259,6 +259,51 @@ kda_status kda_prefill_chunks(const kda_dims* dims, const int32_t* cu_seqlens,
                               const int32_t* state_idx, void* out,
                               void* workspace, uint64_t workspace_bytes,
                               void* hip_stream);
+
+/*
+ * Raw gate inputs of a prefill call, token-major (the chunk op of the page
+ * "PR #51862 完整报告" is chunk_kda_with_fused_gate: the gate activation
+ * runs inside the chunk kernels).  Per token n (a row of the varlen batch)
+ * and head h the gates are those of kda_decode_raw_gates:
+ *   z = raw_g[n][h][i] + dt_bias[h*D+i],  a = exp(A_log[h])
+ *   g = -a * softplus(z), or lower_bound * sigmoid(a * z) with
+ *       KDA_BOUNDED_GATE
+ *   beta = sigmoid(raw_beta[n][h]); conv: a_c = conv_bias[c] + sum_t ...
+ * All device pointers, 16-byte aligned; the struct itself is host memory,
+ * read during the call only.
+ */
+typedef struct {
+  const float* conv_bias; /* fp32 [3C], or NULL for no bias                */
+  const void* raw_g;      /* bf16 [tokens, H, D]                            */
+  const void* raw_beta;   /* bf16 [tokens, H]                               */
+  const float* A_log;     /* fp32 [H]                                       */
+  const float* dt_bias;   /* fp32 [C]                                       */
+  float lower_bound;      /* KDA_BOUNDED_GATE: finite and < 0               */
+} kda_gate_inputs;
+
+/*
+ * kda_prefill_chunked and kda_prefill_chunks with the gate activation fused
+ * (raw gates in place of g and beta).  Flags as kda_prefill plus
+ * KDA_BOUNDED_GATE.  gates NULL, or any of raw_g, raw_beta, A_log, dt_bias
+ * NULL, or a bad lower_bound with KDA_BOUNDED_GATE: KDA_ERR_INVALID_ARG;
+ * misaligned: KDA_ERR_MISALIGNED.  Other arguments, rules and status codes
+ * as the entry points they extend.
+ */
+kda_status kda_prefill_chunked_raw_gates(const kda_dims* dims,
+                                         const int32_t* cu_seqlens,
+                                         const void* qkv, const float* conv_w,
+                                         void* conv_state, float* rec_state,
+                                         const kda_gate_inputs* gates,
+                                         const void* gate, const float* norm_w,
+                                         const int32_t* state_idx, void* out,
+                                         void* hip_stream);
+kda_status kda_prefill_chunks_raw_gates(
+    const kda_dims* dims, const int32_t* cu_seqlens,
+    const int32_t* chunk_indices, const int64_t* chunk_offsets,
+    int64_t max_chunks, const void* qkv, const float* conv_w, void* conv_state,
+    float* rec_state, const kda_gate_inputs* gates, const void* gate,
+    const float* norm_w, const int32_t* state_idx, void* out, void* workspace,
+    uint64_t workspace_bytes, void* hip_stream);
 
 /*
  * Device-side chunk bookkeeping of a variable-length batch (page "PR

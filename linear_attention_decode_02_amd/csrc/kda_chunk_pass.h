@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "kda_gate_args.h"
+
 struct KdaPassArgs {
   const uint16_t* qkv;           // bf16 [tokens, 3C]
   const float* conv_w;           // fp32 [3, 4, C]
@@ -21,6 +23,7 @@ struct KdaPassArgs {
   const int64_t* chunk_offsets;  // int64 [N + 1]: first chunk of each
   float* workspace;              // max_chunks * H records
   uint16_t* out;                 // bf16 [tokens, C]
+  KdaRawGateArgs rg;             // raw gates (rg.raw_g null: g and beta)
   int64_t max_chunks;            // chunk rows the workspace holds
   int32_t num_seqs;
   uint32_t flags;

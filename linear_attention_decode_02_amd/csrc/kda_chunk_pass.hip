@@ -208,27 +208,61 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
       }
     }
   }
+  const bool raw_gates = p.rg.raw_g != nullptr;
   f2 cw[3][kW];
+  f2 cb[3] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
-  for (int pp = 0; pp < 3; ++pp)
+  for (int pp = 0; pp < 3; ++pp) {
 #pragma unroll
     for (int t = 0; t < kW; ++t)
       cw[pp][t] = *reinterpret_cast<const f2*>(
           p.conv_w + (static_cast<int64_t>(pp) * kW + t) * C + col0 + 2 * lane);
-  // cumulative decay (log2 units) of keys 2 lane, 2 lane + 1
+    if (p.rg.conv_bias)
+      cb[pp] = *reinterpret_cast<const f2*>(
+          p.rg.conv_bias + static_cast<int64_t>(pp) * C + col0 + 2 * lane);
+  }
+  // per-token decays (log2 units) of keys 2 lane, 2 lane + 1
   f2 gl[kC];
+  if (raw_gates) {
+    const f2 db =
+        *reinterpret_cast<const f2*>(p.rg.dt_bias + col0 + 2 * lane);
+    const float a_rate = __expf(p.rg.A_log[h]);
+    const float lb2 = p.rg.lower_bound * kLog2e;
+    uint32_t w[kC];
 #pragma unroll
-  for (int t = 0; t < kC; ++t) {
-    const int rr = t < nv - 1 ? t : nv - 1;
-    gl[t] = *reinterpret_cast<const f2*>(p.g + ((tok0 + rr) * H + h) * kD +
-                                         2 * lane);
+    for (int t = 0; t < kC; ++t) {
+      const int rr = t < nv - 1 ? t : nv - 1;
+      w[t] = *reinterpret_cast<const uint32_t*>(
+          p.rg.raw_g + ((tok0 + rr) * H + h) * kD + 2 * lane);
+    }
+    // one branch for the whole chunk, straight-line code inside
+    if (p.flags & KDA_BOUNDED_GATE) {
+#pragma unroll
+      for (int t = 0; t < kC; ++t)
+        gl[t] = f2{kda_gate2_from_raw<true>(bf16_lo(w[t]) + db.x, a_rate, lb2),
+                   kda_gate2_from_raw<true>(bf16_hi(w[t]) + db.y, a_rate, lb2)};
+    } else {
+#pragma unroll
+      for (int t = 0; t < kC; ++t)
+        gl[t] =
+            f2{kda_gate2_from_raw<false>(bf16_lo(w[t]) + db.x, a_rate, lb2),
+               kda_gate2_from_raw<false>(bf16_hi(w[t]) + db.y, a_rate, lb2)};
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kC; ++t) {
+      const int rr = t < nv - 1 ? t : nv - 1;
+      gl[t] = *reinterpret_cast<const f2*>(p.g + ((tok0 + rr) * H + h) * kD +
+                                           2 * lane) *
+              kLog2e;
+    }
   }
   f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
   f2 G = {0.f, 0.f};
   float gmax = 0.0f;
 #pragma unroll
   for (int t = 0; t < kC; ++t) {
-    if (t < nv) G += gl[t] * kLog2e;
+    if (t < nv) G += gl[t];
     gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -238,7 +272,10 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
   const bool unsafe = __any(!(gmax <= kSafeExp2));
   if (lane < 4) {
     const int t = 4 * pw + lane;
-    const float b = t < nv ? p.beta[(tok0 + t) * H + h] : 0.0f;
+    float b = 0.0f;
+    if (t < nv)
+      b = raw_gates ? sigmoid_(bf16_lo(p.rg.raw_beta[(tok0 + t) * H + h]))
+                    : p.beta[(tok0 + t) * H + h];
     sm.beta[t] = b;
     rec[kRecBeta + t] = b;
   }
@@ -252,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
     for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        float a = 0.0f;
+        float a = cb[pp][e];
 #pragma unroll
         for (int tap = 0; tap < kW; ++tap) {
           const uint32_t w2 = conv_update || tap == kW - 1 ? raw[pp][u + tap]

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "kda_gate_args.h"
+
 struct KdaChunkedArgs {
   const uint16_t* qkv;        // bf16 [tokens, 3C]
   const float* conv_w;        // fp32 [3, 4, C]
@@ -20,6 +22,7 @@ struct KdaChunkedArgs {
   int32_t tokens_per_row;     // with cu_seqlens null: row n owns tokens
                               // n*T .. n*T + T-1
   uint16_t* out;              // bf16 [tokens, C]
+  KdaRawGateArgs rg;          // raw gates (rg.raw_g null: g and beta)
   uint32_t flags;
   int32_t heads;
   int32_t num_slots;

@@ -89,12 +89,15 @@ struct alignas(16) Smem {
   float B[kC][kTd];     // B_ts for s <= t, else 0
   float o[kC][kLd];     // this chunk's outputs before the norm
   float cw[3][kW][kD];  // this head's conv weights
+  float cb[3][kD];      // raw gates: conv bias (zeros without one)
+  float dtb[kD];        // raw gates: this head's dt_bias
   float nw[kD];         // norm weight
   uint32_t win[3][kW - 1][kD / 2];  // stored conv window, channel pairs
   // raw inputs of the next chunk, copied in by the prep waves' LDS-direct
   // loads: per prep wave its 7 input rows (3 parts, channel pairs), the
   // chunk's 16 rows of g and its 16 betas
-  // (g and beta are read by every prep wave: two buffers by chunk parity)
+  // (g and beta are read by every prep wave: two buffers by chunk parity;
+  // raw gates fill the first half of each g row with bf16 pairs)
   uint32_t stage[4][7][3][kD / 2];
   float gst[2][kC][kD];
   float bst[2][64];
@@ -195,9 +198,14 @@ __device__ __forceinline__ f4 ld4(const float* p) {
   return *reinterpret_cast<const f4*>(p);
 }
 
-template <bool kNorm>
+// Gate operands of a launch: activated g and beta, or the raw inputs with
+// the default (softplus) or the bounded gate.
+enum GateForm { kGateInput = 0, kGateSoftplus = 1, kGateBounded = 2 };
+
+template <bool kNorm, int kGate>
 __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     KdaChunkedArgs p) {
+  constexpr bool kRaw = kGate != kGateInput;
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -260,6 +268,15 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
           p.conv_w[(static_cast<int64_t>(pp) * kW + t) * C + col0 + k];
     }
     if (i < kD) sm.nw[i] = kNorm ? p.norm_w[i] : 0.0f;
+    if (kRaw) {
+      for (int e = i; e < 3 * kD; e += 256)
+        sm.cb[e / kD][e % kD] =
+            p.rg.conv_bias
+                ? p.rg.conv_bias[(e / kD) * static_cast<int64_t>(C) + col0 +
+                                 e % kD]
+                : 0.0f;
+      if (i < kD) sm.dtb[i] = p.rg.dt_bias[col0 + i];
+    }
     // the stored window of channels 2 lane, 2 lane + 1 of each part
     if (i < kD / 2) {
 #pragma unroll
@@ -290,6 +307,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   // before the sequence or past its end are clamped to valid rows and
   // replaced or masked where used), rows 4pw .. 4pw+3 of g, and (wave 0)
   // the betas.  The loads land while the wave works on the current chunk.
+  uint32_t rbeta = 0;  // raw gates: bf16 beta of token 4pw + lane (lane < 4)
   auto stage_chunk = [&](int ci) {
     const int c0 = ci * kC;
     const int nv = len - c0 < kC ? len - c0 : kC;
@@ -308,14 +326,51 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     for (int u = 0; u < 4; ++u) {
       const int t = 4 * pw + u;
       const int rr = t < nv - 1 ? t : nv - 1;
-      const float* row = p.g + ((tok0 + rr) * H + h) * kD + lane;
-      load_lds(row, &sm.gst[ci & 1][t][0]);
-      load_lds(row + 64, &sm.gst[ci & 1][t][64]);
+      if (kRaw) {
+        load_lds(p.rg.raw_g + ((tok0 + rr) * H + h) * kD + 2 * lane,
+                 &sm.gst[ci & 1][t][0]);
+      } else {
+        const float* row = p.g + ((tok0 + rr) * H + h) * kD + lane;
+        load_lds(row, &sm.gst[ci & 1][t][0]);
+        load_lds(row + 64, &sm.gst[ci & 1][t][64]);
+      }
     }
-    if (pw == 0) {
+    if (kRaw) {
+      if (lane < 4) {
+        const int t = 4 * pw + lane;
+        const int rr = t < nv - 1 ? t : nv - 1;
+        rbeta = p.rg.raw_beta[(tok0 + rr) * H + h];
+      }
+    } else if (pw == 0) {
       const int rr = lane < nv - 1 ? lane : nv - 1;
       load_lds(p.beta + (tok0 + rr) * H + h, &sm.bst[ci & 1][0]);
     }
+  };
+
+  // Raw gates: once its own requests for chunk cj have landed, prep wave pw
+  // turns its 4 staged g rows (bf16 pairs of raw_g, keys 2 lane, 2 lane + 1
+  // in dword lane) into log2-unit decays in place, and its 4 betas into
+  // bst.  Each wave activates a quarter of the chunk; the barrier that
+  // follows publishes the rows to the other prep waves.
+  auto activate = [&](int cj) {
+    if (!kRaw || cj >= nchunks) return;
+    const f2 db = *reinterpret_cast<const f2*>(&sm.dtb[2 * lane]);
+    const float a_rate = __expf(p.rg.A_log[h]);
+    const float lb2 = p.rg.lower_bound * kLog2e;
+    float(*rows)[kD] = sm.gst[cj & 1];
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = reinterpret_cast<const uint32_t*>(&rows[4 * pw + u][0])[lane];
+    // every lane's read is done before any lane's write lands over it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr bool kB = kGate == kGateBounded;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<f2*>(&rows[4 * pw + u][2 * lane]) =
+          f2{kda_gate2_from_raw<kB>(bf16_lo(w[u]) + db.x, a_rate, lb2),
+             kda_gate2_from_raw<kB>(bf16_hi(w[u]) + db.y, a_rate, lb2)};
+    if (lane < 4) sm.bst[cj & 1][4 * pw + lane] = sigmoid_(bf16_lo(rbeta));
   };
 
   auto prep_tables = [&](int ci) {
@@ -329,10 +384,14 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     for (int u = 0; u < 7; ++u)
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp) raw[pp][u] = sm.stage[pw][u][pp][lane];
+    // per-token decays of keys 2 lane, 2 lane + 1 in log2 units (raw
+    // gates: activated in place by activate())
     f2 gl[kC];
 #pragma unroll
-    for (int t = 0; t < kC; ++t)
+    for (int t = 0; t < kC; ++t) {
       gl[t] = *reinterpret_cast<const f2*>(&sm.gst[ci & 1][t][2 * lane]);
+      if (!kRaw) gl[t] *= kLog2e;
+    }
     const float bt = lane < 4 ? sm.bst[ci & 1][4 * pw + lane] : 0.0f;
     // the staging buffers are free again: request the next chunk
     wait_lds();
@@ -351,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 #pragma unroll
       for (int t = 0; t < kC; ++t) {
         const f2 gv = gl[t];
-        if (t < nv) G += gv * kLog2e;
+        if (t < nv) G += gv;
         gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -364,11 +423,14 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     // conv + SiLU of the 4 tokens (weights read once), then the 8 norm
     // reductions side by side, then the tables
     f2 cwv[3][kW];
+    f2 cbv[3] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp)
+    for (int pp = 0; pp < 3; ++pp) {
 #pragma unroll
       for (int tap = 0; tap < kW; ++tap)
         cwv[pp][tap] = *reinterpret_cast<const f2*>(&sm.cw[pp][tap][2 * lane]);
+      if (kRaw) cbv[pp] = *reinterpret_cast<const f2*>(&sm.cb[pp][2 * lane]);
+    }
     float y[4][3][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -377,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float a = 0.0f;
+          float a = cbv[pp][e];
 #pragma unroll
           for (int tap = 0; tap < kW; ++tap) {
             // with the update a token sees the inputs before it (the stored
@@ -616,6 +678,10 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     wait_vmem();
   }
   __syncthreads();  // conv and norm weights, the first chunk's inputs
+  if (kRaw) {       // (activate reads the dt_bias row written above)
+    if (!state_wave) activate(0);
+    __syncthreads();
+  }
   if (!state_wave) prep_tables(0);
   __syncthreads();
   if (!state_wave) prep_gram(0);
@@ -623,6 +689,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   if (!state_wave) {
     prep_reduce(0);
     wait_vmem();
+    activate(1);
   }
   __syncthreads();
   for (int ci = 0; ci < nchunks; ++ci) {
@@ -646,7 +713,10 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       prep_gram(ci + 1);
     __syncthreads();
     if (!state_wave && more) prep_reduce(ci + 1);
-    if (!state_wave) wait_vmem();  // the staged inputs of the next chunk
+    if (!state_wave) {
+      wait_vmem();  // the staged inputs of the chunk after the next
+      activate(ci + 2);
+    }
     __syncthreads();
   }
 
@@ -680,16 +750,26 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   }
 }
 
+template <int kGate>
+void launch_gate(const KdaChunkedArgs& args, dim3 grid, hipStream_t stream) {
+  if (args.flags & KDA_OUTPUT_NORM)
+    hipLaunchKernelGGL((kda_chunked_prefill_kernel<true, kGate>), grid,
+                       dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((kda_chunked_prefill_kernel<false, kGate>), grid,
+                       dim3(kThreads), 0, stream, args);
+}
+
 }  // namespace
 
 hipError_t kda_chunked_prefill_launch(const KdaChunkedArgs& args,
                                       int32_t num_seqs, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(num_seqs * args.heads));
-  if (args.flags & KDA_OUTPUT_NORM)
-    hipLaunchKernelGGL(kda_chunked_prefill_kernel<true>, grid,
-                       dim3(kThreads), 0, stream, args);
+  if (!args.rg.raw_g)
+    launch_gate<kGateInput>(args, grid, stream);
+  else if (args.flags & KDA_BOUNDED_GATE)
+    launch_gate<kGateBounded>(args, grid, stream);
   else
-    hipLaunchKernelGGL(kda_chunked_prefill_kernel<false>, grid,
-                       dim3(kThreads), 0, stream, args);
+    launch_gate<kGateSoftplus>(args, grid, stream);
   return hipGetLastError();
 }

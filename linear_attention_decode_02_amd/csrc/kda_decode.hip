@@ -1021,14 +1021,59 @@ kda_status kda_prefill(const kda_dims* d, const int32_t* cu_seqlens,
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-kda_status kda_prefill_chunked(const kda_dims* d, const int32_t* cu_seqlens,
-                               const void* qkv, const float* conv_w,
-                               void* conv_state, float* rec_state,
-                               const float* g, const float* beta,
-                               const void* gate, const float* norm_w,
-                               const int32_t* state_idx, void* out,
-                               void* hip_stream) {
-  kda_status st = check_dims(d, kPlainFlags);
+namespace {
+
+// Flags of a prefill call with g and beta (gi null) or the raw gate
+// inputs gi, and the bound of the bounded gate.
+kda_status check_prefill_gates(const kda_dims* d, const kda_gate_inputs* gi) {
+  kda_status st = check_dims(d, gi ? kPlainFlags | KDA_BOUNDED_GATE
+                                   : kPlainFlags);
+  if (st != KDA_OK) return st;
+  if (!gi) return KDA_OK;
+  if ((d->flags & KDA_BOUNDED_GATE) &&
+      !(std::isfinite(gi->lower_bound) && gi->lower_bound < 0.0f))
+    return KDA_ERR_INVALID_ARG;
+  return KDA_OK;
+}
+
+// Pointer checks of the gate operands (after the batch-0 early return).
+kda_status check_gate_ptrs(const float* g, const float* beta,
+                           const kda_gate_inputs* gi) {
+  if (!gi) {
+    if (!g || !beta) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(g) || !aligned16(beta)) return KDA_ERR_MISALIGNED;
+    return KDA_OK;
+  }
+  if (!gi->raw_g || !gi->raw_beta || !gi->A_log || !gi->dt_bias)
+    return KDA_ERR_INVALID_ARG;
+  if (!aligned16(gi->raw_g) || !aligned16(gi->raw_beta) ||
+      !aligned16(gi->A_log) || !aligned16(gi->dt_bias) ||
+      (gi->conv_bias && !aligned16(gi->conv_bias)))
+    return KDA_ERR_MISALIGNED;
+  return KDA_OK;
+}
+
+KdaRawGateArgs raw_gate_args(const kda_gate_inputs* gi) {
+  KdaRawGateArgs r{};
+  if (gi) {
+    r.conv_bias = gi->conv_bias;
+    r.raw_g = static_cast<const uint16_t*>(gi->raw_g);
+    r.raw_beta = static_cast<const uint16_t*>(gi->raw_beta);
+    r.A_log = gi->A_log;
+    r.dt_bias = gi->dt_bias;
+    r.lower_bound = gi->lower_bound;
+  }
+  return r;
+}
+
+kda_status prefill_chunked_impl(const kda_dims* d, const int32_t* cu_seqlens,
+                                const void* qkv, const float* conv_w,
+                                void* conv_state, float* rec_state,
+                                const float* g, const float* beta,
+                                const kda_gate_inputs* gi, const void* gate,
+                                const float* norm_w, const int32_t* state_idx,
+                                void* out, void* hip_stream) {
+  kda_status st = check_prefill_gates(d, gi);
   if (st != KDA_OK) return st;
   if (d->batch == 0) return KDA_OK;
   if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
@@ -1036,19 +1081,45 @@ kda_status kda_prefill_chunked(const kda_dims* d, const int32_t* cu_seqlens,
   st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
                     state_idx, out);
   if (st != KDA_OK) return st;
-  if (!g || !beta) return KDA_ERR_INVALID_ARG;
-  if (!aligned16(g) || !aligned16(beta)) return KDA_ERR_MISALIGNED;
+  st = check_gate_ptrs(g, beta, gi);
+  if (st != KDA_OK) return st;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return KDA_ERR_DEVICE;
-  const KdaChunkedArgs a =
+  KdaChunkedArgs a =
       chunked_args(d, cu_seqlens, 0, qkv, conv_w, conv_state, rec_state, g,
                    beta, gate, norm_w, state_idx, out);
+  a.rg = raw_gate_args(gi);
   return kda_chunked_prefill_launch(a, d->batch,
                                     static_cast<hipStream_t>(hip_stream)) ==
                  hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+kda_status kda_prefill_chunked(const kda_dims* d, const int32_t* cu_seqlens,
+                               const void* qkv, const float* conv_w,
+                               void* conv_state, float* rec_state,
+                               const float* g, const float* beta,
+                               const void* gate, const float* norm_w,
+                               const int32_t* state_idx, void* out,
+                               void* hip_stream) {
+  return prefill_chunked_impl(d, cu_seqlens, qkv, conv_w, conv_state,
+                              rec_state, g, beta, nullptr, gate, norm_w,
+                              state_idx, out, hip_stream);
+}
+
+kda_status kda_prefill_chunked_raw_gates(
+    const kda_dims* d, const int32_t* cu_seqlens, const void* qkv,
+    const float* conv_w, void* conv_state, float* rec_state,
+    const kda_gate_inputs* gates, const void* gate, const float* norm_w,
+    const int32_t* state_idx, void* out, void* hip_stream) {
+  if (!gates) return KDA_ERR_INVALID_ARG;
+  return prefill_chunked_impl(d, cu_seqlens, qkv, conv_w, conv_state,
+                              rec_state, nullptr, nullptr, gates, gate, norm_w,
+                              state_idx, out, hip_stream);
 }
 
 uint64_t kda_prefill_chunks_workspace_bytes(const kda_dims* d,
@@ -1058,32 +1129,32 @@ uint64_t kda_prefill_chunks_workspace_bytes(const kda_dims* d,
          static_cast<uint64_t>(d->num_heads) * kda_pass_record_bytes();
 }
 
-kda_status kda_prefill_chunks(const kda_dims* d, const int32_t* cu_seqlens,
-                              const int32_t* chunk_indices,
-                              const int64_t* chunk_offsets, int64_t max_chunks,
-                              const void* qkv, const float* conv_w,
-                              void* conv_state, float* rec_state,
-                              const float* g, const float* beta,
-                              const void* gate, const float* norm_w,
-                              const int32_t* state_idx, void* out,
-                              void* workspace, uint64_t workspace_bytes,
-                              void* hip_stream) {
-  kda_status st = check_dims(d, kPlainFlags);
+namespace {
+
+kda_status prefill_chunks_impl(
+    const kda_dims* d, const int32_t* cu_seqlens, const int32_t* chunk_indices,
+    const int64_t* chunk_offsets, int64_t max_chunks, const void* qkv,
+    const float* conv_w, void* conv_state, float* rec_state, const float* g,
+    const float* beta, const kda_gate_inputs* gi, const void* gate,
+    const float* norm_w, const int32_t* state_idx, void* out, void* workspace,
+    uint64_t workspace_bytes, void* hip_stream) {
+  kda_status st = check_prefill_gates(d, gi);
   if (st != KDA_OK) return st;
   if (max_chunks < 0 ||
       max_chunks * static_cast<int64_t>(d->num_heads) > INT32_MAX)
     return KDA_ERR_INVALID_ARG;
   if (d->batch == 0) return KDA_OK;
-  if (!cu_seqlens || !chunk_offsets || !g || !beta ||
+  if (!cu_seqlens || !chunk_offsets ||
       (max_chunks > 0 && (!chunk_indices || !workspace)))
     return KDA_ERR_INVALID_ARG;
   if (workspace_bytes < kda_prefill_chunks_workspace_bytes(d, max_chunks))
     return KDA_ERR_INVALID_ARG;
   if (!aligned16(cu_seqlens) || !aligned16(chunk_offsets) ||
       (chunk_indices && !aligned16(chunk_indices)) ||
-      (workspace && !aligned16(workspace)) || !aligned16(g) ||
-      !aligned16(beta))
+      (workspace && !aligned16(workspace)))
     return KDA_ERR_MISALIGNED;
+  st = check_gate_ptrs(g, beta, gi);
+  if (st != KDA_OK) return st;
   st = check_common(d, qkv, conv_w, conv_state, rec_state, gate, norm_w,
                     state_idx, out);
   if (st != KDA_OK) return st;
@@ -1111,10 +1182,43 @@ kda_status kda_prefill_chunks(const kda_dims* d, const int32_t* cu_seqlens,
   a.heads = d->num_heads;
   a.num_slots = d->num_slots;
   a.eps = d->norm_eps;
+  a.rg = raw_gate_args(gi);
   return kda_chunk_pass_launch(a, static_cast<hipStream_t>(hip_stream)) ==
                  hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+kda_status kda_prefill_chunks(const kda_dims* d, const int32_t* cu_seqlens,
+                              const int32_t* chunk_indices,
+                              const int64_t* chunk_offsets, int64_t max_chunks,
+                              const void* qkv, const float* conv_w,
+                              void* conv_state, float* rec_state,
+                              const float* g, const float* beta,
+                              const void* gate, const float* norm_w,
+                              const int32_t* state_idx, void* out,
+                              void* workspace, uint64_t workspace_bytes,
+                              void* hip_stream) {
+  return prefill_chunks_impl(d, cu_seqlens, chunk_indices, chunk_offsets,
+                             max_chunks, qkv, conv_w, conv_state, rec_state, g,
+                             beta, nullptr, gate, norm_w, state_idx, out,
+                             workspace, workspace_bytes, hip_stream);
+}
+
+kda_status kda_prefill_chunks_raw_gates(
+    const kda_dims* d, const int32_t* cu_seqlens, const int32_t* chunk_indices,
+    const int64_t* chunk_offsets, int64_t max_chunks, const void* qkv,
+    const float* conv_w, void* conv_state, float* rec_state,
+    const kda_gate_inputs* gates, const void* gate, const float* norm_w,
+    const int32_t* state_idx, void* out, void* workspace,
+    uint64_t workspace_bytes, void* hip_stream) {
+  if (!gates) return KDA_ERR_INVALID_ARG;
+  return prefill_chunks_impl(d, cu_seqlens, chunk_indices, chunk_offsets,
+                             max_chunks, qkv, conv_w, conv_state, rec_state,
+                             nullptr, nullptr, gates, gate, norm_w, state_idx,
+                             out, workspace, workspace_bytes, hip_stream);
 }
 
 kda_status kda_chunk_metadata(const int32_t* cu_seqlens, int32_t num_seqs,

@@ -47,6 +47,13 @@ class Dims(ctypes.Structure):
 _lib = None
 
 
+class GateInputs(ctypes.Structure):
+    """``kda_gate_inputs``: raw gate operands of the prefill entry points."""
+    _fields_ = [("conv_bias", ctypes.c_void_p), ("raw_g", ctypes.c_void_p),
+                ("raw_beta", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float)]
+
+
 def lib() -> ctypes.CDLL:
     """Load ``libkda_decode.so`` (built by ``__graft_entry__.build()``)."""
     global _lib
@@ -81,6 +88,14 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_chunks.argtypes = (
             [ctypes.POINTER(Dims), P, P, P, ctypes.c_int64] + [P] * 10 +
             [P, ctypes.c_uint64, P])
+        L.kda_prefill_chunked_raw_gates.restype = ctypes.c_int
+        L.kda_prefill_chunked_raw_gates.argtypes = (
+            [ctypes.POINTER(Dims)] + [P] * 5 + [ctypes.POINTER(GateInputs)]
+            + [P] * 5)
+        L.kda_prefill_chunks_raw_gates.restype = ctypes.c_int
+        L.kda_prefill_chunks_raw_gates.argtypes = (
+            [ctypes.POINTER(Dims), P, P, P, ctypes.c_int64] + [P] * 4 +
+            [ctypes.POINTER(GateInputs)] + [P] * 5 + [ctypes.c_uint64, P])
         L.kda_chunk_metadata.restype = ctypes.c_int
         L.kda_chunk_metadata.argtypes = [P, ctypes.c_int32, ctypes.c_int32,
                                          P, P, P]
@@ -264,15 +279,10 @@ def kda_decode_tokens(qkv, conv_w, conv_state, rec_state, g, beta, gate,
         raise KdaError(rc, status_string(rc))
 
 
-def kda_prefill(cu_seqlens, qkv, conv_w, conv_state, rec_state, g, beta,
-                gate, norm_w, state_idx, out, *, norm: bool = True,
-                eps: float = 1e-5, variants: int = 0, chunked: bool = False,
-                stream=None) -> None:
-    """Variable-length prefill: sequence n covers tokens cu_seqlens[n] ..
-    cu_seqlens[n+1]-1 of token-major qkv [tokens, 3C], g [tokens, H, 128],
-    beta [tokens, H], gate/out [tokens, C]; slot state_idx[n].  ``chunked``
-    selects kda_prefill_chunked (16-token chunks on the matrix cores)
-    instead of the token-by-token kda_prefill."""
+def _prefill_common(cu_seqlens, qkv, conv_w, conv_state, rec_state, gate,
+                    norm_w, state_idx, out, norm, variants):
+    """Checks the operands every prefill entry point shares; returns
+    (N, tokens, H, D, S)."""
     if rec_state.dim() != 4 or qkv.dim() != 2:
         raise ValueError("rec_state [S, H, 128, 128], qkv [tokens, 3C]")
     S, H, D, D2 = rec_state.shape
@@ -287,12 +297,41 @@ def kda_prefill(cu_seqlens, qkv, conv_w, conv_state, rec_state, g, beta,
                 else (S, 3 * C, CONV_WIDTH - 1))
     _check(conv_state, "conv_state", torch.bfloat16, cs_shape)
     _check(state_idx, "state_idx", torch.int32, (N,))
-    _check(g, "g", torch.float32, (tokens, H, D))
-    _check(beta, "beta", torch.float32, (tokens, H))
     _check(out, "out", torch.bfloat16, (tokens, C))
     if norm:
         _check(gate, "gate", torch.bfloat16, (tokens, C))
         _check(norm_w, "norm_w", torch.float32, (D,))
+    return N, tokens, H, D, S
+
+
+def _gate_inputs(tokens, H, D, conv_bias, raw_g, raw_beta, A_log, dt_bias,
+                 lower_bound) -> GateInputs:
+    C = H * D
+    _check(raw_g, "raw_g", torch.bfloat16, (tokens, H, D))
+    _check(raw_beta, "raw_beta", torch.bfloat16, (tokens, H))
+    _check(A_log, "A_log", torch.float32, (H,))
+    _check(dt_bias, "dt_bias", torch.float32, (C,))
+    if conv_bias is not None:
+        _check(conv_bias, "conv_bias", torch.float32, (3 * C,))
+    return GateInputs(_ptr(conv_bias), _ptr(raw_g), _ptr(raw_beta),
+                      _ptr(A_log), _ptr(dt_bias),
+                      float(lower_bound if lower_bound is not None else 0.0))
+
+
+def kda_prefill(cu_seqlens, qkv, conv_w, conv_state, rec_state, g, beta,
+                gate, norm_w, state_idx, out, *, norm: bool = True,
+                eps: float = 1e-5, variants: int = 0, chunked: bool = False,
+                stream=None) -> None:
+    """Variable-length prefill: sequence n covers tokens cu_seqlens[n] ..
+    cu_seqlens[n+1]-1 of token-major qkv [tokens, 3C], g [tokens, H, 128],
+    beta [tokens, H], gate/out [tokens, C]; slot state_idx[n].  ``chunked``
+    selects kda_prefill_chunked (16-token chunks on the matrix cores)
+    instead of the token-by-token kda_prefill."""
+    N, tokens, H, D, S = _prefill_common(cu_seqlens, qkv, conv_w, conv_state,
+                                         rec_state, gate, norm_w, state_idx,
+                                         out, norm, variants)
+    _check(g, "g", torch.float32, (tokens, H, D))
+    _check(beta, "beta", torch.float32, (tokens, H))
     dims = Dims(N, H, D, CONV_WIDTH, S,
                 (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
     with torch.cuda.device(qkv.device):
@@ -327,30 +366,12 @@ def kda_prefill_chunks(cu_seqlens, chunk_indices, chunk_offsets,
     parallel into ``workspace`` (a uint8 device tensor of at least
     prefill_chunks_workspace_bytes bytes), then each sequence's state
     through its chunks.  Other arguments as kda_prefill."""
-    if rec_state.dim() != 4 or qkv.dim() != 2:
-        raise ValueError("rec_state [S, H, 128, 128], qkv [tokens, 3C]")
-    S, H, D, D2 = rec_state.shape
-    C = H * D
-    N = state_idx.shape[0]
-    tokens = qkv.shape[0]
-    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
-    _check(chunk_offsets, "chunk_offsets", torch.int64, (N + 1,))
-    _check(chunk_indices, "chunk_indices", torch.int32,
-           (chunk_indices.shape[0], 2))
-    _check(workspace, "workspace", torch.uint8, (workspace.numel(),))
-    _check(rec_state, "rec_state", torch.float32, (S, H, D, D2))
-    _check(qkv, "qkv", torch.bfloat16, (tokens, 3 * C))
-    _check(conv_w, "conv_w", torch.float32, (3, CONV_WIDTH, C))
-    cs_shape = ((S, CONV_WIDTH - 1, 3 * C) if variants & KDA_CONV_TAP_MAJOR
-                else (S, 3 * C, CONV_WIDTH - 1))
-    _check(conv_state, "conv_state", torch.bfloat16, cs_shape)
-    _check(state_idx, "state_idx", torch.int32, (N,))
+    N, tokens, H, D, S = _prefill_common(cu_seqlens, qkv, conv_w, conv_state,
+                                         rec_state, gate, norm_w, state_idx,
+                                         out, norm, variants)
+    _check_chunk_table(N, chunk_indices, chunk_offsets, workspace)
     _check(g, "g", torch.float32, (tokens, H, D))
     _check(beta, "beta", torch.float32, (tokens, H))
-    _check(out, "out", torch.bfloat16, (tokens, C))
-    if norm:
-        _check(gate, "gate", torch.bfloat16, (tokens, C))
-        _check(norm_w, "norm_w", torch.float32, (D,))
     dims = Dims(N, H, D, CONV_WIDTH, S,
                 (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
     with torch.cuda.device(qkv.device):
@@ -358,6 +379,75 @@ def kda_prefill_chunks(cu_seqlens, chunk_indices, chunk_offsets,
             ctypes.byref(dims), _ptr(cu_seqlens), _ptr(chunk_indices),
             _ptr(chunk_offsets), int(max_chunks), _ptr(qkv), _ptr(conv_w),
             _ptr(conv_state), _ptr(rec_state), _ptr(g), _ptr(beta),
+            _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
+            _ptr(state_idx), _ptr(out), _ptr(workspace),
+            int(workspace.numel()), _stream(stream, qkv.device))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+
+
+def _check_chunk_table(N, chunk_indices, chunk_offsets, workspace):
+    _check(chunk_offsets, "chunk_offsets", torch.int64, (N + 1,))
+    _check(chunk_indices, "chunk_indices", torch.int32,
+           (chunk_indices.shape[0], 2))
+    _check(workspace, "workspace", torch.uint8, (workspace.numel(),))
+
+
+def kda_prefill_chunked_raw_gates(cu_seqlens, qkv, conv_w, conv_bias,
+                                  conv_state, rec_state, raw_g, raw_beta,
+                                  A_log, dt_bias, gate, norm_w, state_idx,
+                                  out, *, norm: bool = True,
+                                  eps: float = 1e-5,
+                                  lower_bound: float | None = None,
+                                  variants: int = 0, stream=None) -> None:
+    """kda_prefill_chunked with the gate activation fused: raw_g bf16
+    [tokens, H, 128], raw_beta bf16 [tokens, H], A_log fp32 [H], dt_bias
+    fp32 [C], conv_bias fp32 [3C] or None; ``lower_bound`` (< 0) selects
+    the bounded gate.  Other arguments as kda_prefill."""
+    N, tokens, H, D, S = _prefill_common(cu_seqlens, qkv, conv_w, conv_state,
+                                         rec_state, gate, norm_w, state_idx,
+                                         out, norm, variants)
+    gi = _gate_inputs(tokens, H, D, conv_bias, raw_g, raw_beta, A_log,
+                      dt_bias, lower_bound)
+    flags = (KDA_OUTPUT_NORM if norm else 0) | int(variants)
+    if lower_bound is not None:
+        flags |= KDA_BOUNDED_GATE
+    dims = Dims(N, H, D, CONV_WIDTH, S, flags, float(eps))
+    with torch.cuda.device(qkv.device):
+        rc = lib().kda_prefill_chunked_raw_gates(
+            ctypes.byref(dims), _ptr(cu_seqlens), _ptr(qkv), _ptr(conv_w),
+            _ptr(conv_state), _ptr(rec_state), ctypes.byref(gi),
+            _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
+            _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+
+
+def kda_prefill_chunks_raw_gates(cu_seqlens, chunk_indices, chunk_offsets,
+                                 max_chunks: int, qkv, conv_w, conv_bias,
+                                 conv_state, rec_state, raw_g, raw_beta,
+                                 A_log, dt_bias, gate, norm_w, state_idx, out,
+                                 workspace, *, norm: bool = True,
+                                 eps: float = 1e-5,
+                                 lower_bound: float | None = None,
+                                 variants: int = 0, stream=None) -> None:
+    """kda_prefill_chunks with the gate activation fused (raw gate operands
+    as kda_prefill_chunked_raw_gates)."""
+    N, tokens, H, D, S = _prefill_common(cu_seqlens, qkv, conv_w, conv_state,
+                                         rec_state, gate, norm_w, state_idx,
+                                         out, norm, variants)
+    _check_chunk_table(N, chunk_indices, chunk_offsets, workspace)
+    gi = _gate_inputs(tokens, H, D, conv_bias, raw_g, raw_beta, A_log,
+                      dt_bias, lower_bound)
+    flags = (KDA_OUTPUT_NORM if norm else 0) | int(variants)
+    if lower_bound is not None:
+        flags |= KDA_BOUNDED_GATE
+    dims = Dims(N, H, D, CONV_WIDTH, S, flags, float(eps))
+    with torch.cuda.device(qkv.device):
+        rc = lib().kda_prefill_chunks_raw_gates(
+            ctypes.byref(dims), _ptr(cu_seqlens), _ptr(chunk_indices),
+            _ptr(chunk_offsets), int(max_chunks), _ptr(qkv), _ptr(conv_w),
+            _ptr(conv_state), _ptr(rec_state), ctypes.byref(gi),
             _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
             _ptr(state_idx), _ptr(out), _ptr(workspace),
             int(workspace.numel()), _stream(stream, qkv.device))

@@ -202,7 +202,7 @@ def small(name: str, batch: int, heads: int, num_slots: int, seed: int,
                     seed=seed, **kw)
 
 
-_BF16_KEYS = ("qkv", "conv_state", "gate")
+_BF16_KEYS = ("qkv", "conv_state", "gate", "raw_g", "raw_beta")
 
 
 def to_torch(inp: dict, device="cuda") -> dict:

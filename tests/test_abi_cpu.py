@@ -241,3 +241,48 @@ def test_prefill_and_metadata_argument_checks():
     assert L.kda_chunk_metadata(FAKE, 3, 64, None, FAKE, None) == 1
     assert L.kda_chunk_metadata(FAKE, 0, 64, None, FAKE, None) == 4
     assert L.kda_chunk_metadata(FAKE, 3, 64, FAKE + 8, FAKE, None) == 3
+
+
+@no_gpu
+def test_prefill_raw_gates_argument_checks():
+    L = kda.lib()
+    d = dims()
+    gi = kda.GateInputs(FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
+    gp = ctypes.byref(gi)
+    # cu, qkv, conv_w, cs, rs | gates | gate, norm_w, idx, out, stream
+    head, tail = [FAKE] * 5, [FAKE] * 4 + [None]
+    fn = L.kda_prefill_chunked_raw_gates
+    assert fn(ctypes.byref(d), *head, gp, *tail) == 4
+    assert fn(ctypes.byref(d), *head, None, *tail) == 1       # no gates
+    assert fn(ctypes.byref(dims(batch=0)), *head, gp, *tail) == 0
+    bounded = dims(flags=0x21)
+    assert fn(ctypes.byref(bounded), *head, gp, *tail) == 1   # bound 0.0
+    gb = kda.GateInputs(FAKE, FAKE, FAKE, FAKE, FAKE, -2.0)
+    assert fn(ctypes.byref(bounded), *head, ctypes.byref(gb), *tail) == 4
+    gn = kda.GateInputs(None, FAKE, FAKE, FAKE, FAKE, 0.0)    # no conv bias
+    assert fn(ctypes.byref(d), *head, ctypes.byref(gn), *tail) == 4
+    for field in ("raw_g", "raw_beta", "A_log", "dt_bias"):
+        g2 = kda.GateInputs(FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
+        setattr(g2, field, None)
+        assert fn(ctypes.byref(d), *head, ctypes.byref(g2), *tail) == 1
+        setattr(g2, field, FAKE + 2)
+        assert fn(ctypes.byref(d), *head, ctypes.byref(g2), *tail) == 3
+    ga = kda.GateInputs(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 0.0)
+    assert fn(ctypes.byref(d), *head, ctypes.byref(ga), *tail) == 3
+    # two-pass: cu, indices, offsets, max | qkv, conv_w, cs, rs | gates |
+    # gate, norm_w, idx, out, ws | bytes, stream
+    need = L.kda_prefill_chunks_workspace_bytes(ctypes.byref(d), 5)
+    fc = L.kda_prefill_chunks_raw_gates
+    pre, mid = [FAKE, FAKE, FAKE, 5], [FAKE] * 4
+    post = [FAKE] * 5 + [need, None]
+    assert fc(ctypes.byref(d), *pre, *mid, gp, *post) == 4
+    assert fc(ctypes.byref(d), *pre, *mid, None, *post) == 1
+    assert fc(ctypes.byref(bounded), *pre, *mid, gp, *post) == 1
+    short = post[:5] + [need - 1, None]
+    assert fc(ctypes.byref(d), *pre, *mid, gp, *short) == 1
+    g2 = kda.GateInputs(FAKE, None, FAKE, FAKE, FAKE, 0.0)
+    assert fc(ctypes.byref(d), *pre, *mid, ctypes.byref(g2), *post) == 1
+    assert fc(ctypes.byref(dims(batch=0)), *pre, *mid, gp, *post) == 0
+    # the plain entry points still reject the bounded-gate flag
+    p = [FAKE] * 12
+    assert L.kda_prefill_chunked(ctypes.byref(bounded), *p[:11], None) == 1

@@ -204,3 +204,110 @@ def test_two_pass_table_larger_than_workspace_is_skipped():
     ref = O.prefill(inp, cu, heads=H, eps=w.eps)
     P.check_output(got[:40], ref["y"][:40], np.full(40, inp["state_idx"][0]),
                    w.num_slots, H)
+
+
+# ---- raw gates: the gate activation fused into the chunk kernels ---------
+
+def add_prefill_raw_gates(inp, H, seed, g_mean=0.0, bias=True):
+    """Per-token raw gate operands (bf16 raw_g / raw_beta, A_log, dt_bias)
+    and optionally a conv bias.  g_mean shifts raw_g: 0 gives per-token
+    decays of several units (chunks on the exact path), -3 small ones (the
+    factored matrix-core path)."""
+    rng = np.random.default_rng(seed)
+    tokens, D = inp["qkv"].shape[0], 128
+    inp = dict(inp)
+    inp.update(
+        raw_g=synth.to_bf16_bits(
+            rng.normal(g_mean, 1.0, (tokens, H, D)).astype(np.float32)),
+        raw_beta=synth.to_bf16_bits(
+            rng.normal(0, 1, (tokens, H)).astype(np.float32)),
+        A_log=rng.normal(0, 0.5, H).astype(np.float32),
+        dt_bias=rng.normal(0, 0.5, H * D).astype(np.float32))
+    if bias:
+        inp["conv_bias"] = rng.normal(0, 0.3, 3 * H * D).astype(np.float32)
+    return inp
+
+
+def run_raw(path, w, inp, cu, variants=0, lower_bound=None):
+    t = synth.to_torch(inp, DEV)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    tokens = inp["qkv"].shape[0]
+    out = torch.full((tokens, w.channels), float("nan"), dtype=torch.bfloat16,
+                     device=DEV)
+    norm = w.norm
+    common = dict(norm=norm, eps=w.eps, lower_bound=lower_bound,
+                  variants=variants)
+    gate = t["gate"] if norm else None
+    norm_w = t["norm_w"] if norm else None
+    if path == "two_pass":
+        idx, off = kda.chunk_metadata(cu_d, kda.PREFILL_CHUNK,
+                                      cu_seqlens_host=torch.from_numpy(cu))
+        max_chunks = int(idx.shape[0])
+        ws = torch.empty(max(kda.prefill_chunks_workspace_bytes(
+            w.heads, max_chunks), 16), dtype=torch.uint8, device=DEV)
+        kda.kda_prefill_chunks_raw_gates(
+            cu_d, idx, off, max_chunks, t["qkv"], t["conv_w"],
+            t.get("conv_bias"), t["conv_state"], t["rec_state"], t["raw_g"],
+            t["raw_beta"], t["A_log"], t["dt_bias"], gate, norm_w,
+            t["state_idx"], out, ws, **common)
+    else:
+        kda.kda_prefill_chunked_raw_gates(
+            cu_d, t["qkv"], t["conv_w"], t.get("conv_bias"), t["conv_state"],
+            t["rec_state"], t["raw_g"], t["raw_beta"], t["A_log"],
+            t["dt_bias"], gate, norm_w, t["state_idx"], out, **common)
+    torch.cuda.synchronize()
+    return {"out": synth.bf16_bits(out),
+            "conv_state": synth.bf16_bits(t["conv_state"]),
+            "rec_state": t["rec_state"].cpu().numpy()}
+
+
+RAW_CASES = [
+    # name, lens, H, norm, null, flags, g_mean, bias, lower_bound
+    ("softplus_bias", [19, 0, 5, 48, 33, 1], 24, True, (2,), 0, 0.0, True,
+     None),
+    ("softplus_small_decay", [40, 16, 70], 12, True, (), 0, -3.0, True, None),
+    ("bounded_l2_nonorm", [17, 33, 0, 64], 48, False, (3,), O.QK_L2NORM,
+     0.0, False, -5.0),
+]
+
+
+@pytest.mark.parametrize("case", RAW_CASES, ids=[c[0] for c in RAW_CASES])
+def test_chunked_raw_gates_parity(case, path):
+    """Raw gates (the activation inside the chunk kernels) against the
+    oracle's raw-gate prefill: the single-token raw-gate step per token."""
+    name, lens, H, norm, null, flags, g_mean, bias, lb = case
+    w, inp, cu = prefill_case(230 + H, lens, H, norm=norm, null=null)
+    inp = add_prefill_raw_gates(inp, H, 240 + H, g_mean=g_mean, bias=bias)
+    if lb is not None:
+        inp["lower_bound"] = lb
+        flags |= O.BOUNDED_GATE
+    print(f"[chunked raw] {name} lens={lens} H={H} flags={flags:#x}",
+          flush=True)
+    ref = O.prefill(inp, cu, heads=H, norm=norm, eps=w.eps, flags=flags)
+    got = run_raw(path, w, inp, cu, variants=flags & ~O.BOUNDED_GATE,
+                  lower_bound=lb)
+    st = check_prefill(w, inp, cu, got, ref)
+    print(f"[chunked raw] {name} {st}", flush=True)
+
+
+def test_chunked_raw_gates_match_activated_gates():
+    """Fused activation against the plain chunked call fed the same gates
+    activated on the host in float64: equal within rounding."""
+    lens, H = [50, 7, 33], 24
+    w, inp, cu = prefill_case(250, lens, H)
+    inp = add_prefill_raw_gates(inp, H, 251, g_mean=-2.0, bias=False)
+    tokens, D = inp["qkv"].shape[0], 128
+    g = np.empty((tokens, H, D), np.float32)
+    beta = np.empty((tokens, H), np.float32)
+    for t in range(tokens):
+        for h in range(H):
+            gg, bb = O.raw_gates_stage(inp["raw_g"][t, h], inp["A_log"][h],
+                                       inp["dt_bias"][h * D:(h + 1) * D],
+                                       int(inp["raw_beta"][t, h]))
+            g[t, h], beta[t, h] = gg, bb
+    raw = run_raw("fused", w, inp, cu)
+    plain = run_prefill(w, dict(inp, g=g, beta=beta), cu, chunked=True)
+    assert np.array_equal(raw["conv_state"], plain["conv_state"])
+    d = np.abs(raw["rec_state"] - plain["rec_state"]).max()
+    print(f"[raw vs activated] state {d:.3g}", flush=True)
+    assert d <= 1e-4 * max(1.0, np.abs(plain["rec_state"]).max())
