@@ -307,8 +307,9 @@ def bench_prefill(args, np, torch, kda, synth):
     """Variable-length prefill: 16 sequences with seeded lengths (1..4096,
     log-uniform), 48 heads, q/k L2-normalised, fresh states.  A step is one
     kda_prefill_chunked call over the batch (16-token chunks on the matrix
-    cores); the token-by-token kda_prefill and the chunk metadata kernel
-    are timed beside it."""
+    cores); the token-by-token kda_prefill, the two-pass kda_prefill_chunks
+    (with its chunk metadata), the raw-gate entry point and the chunk
+    metadata kernel are timed beside it."""
     import oracle
 
     H, N = 48, 16
@@ -356,6 +357,55 @@ def bench_prefill(args, np, torch, kda, synth):
     wall, kern = timed(K, True)
     step(False)
     _, kern_seq = timed(max(K // 4, 1), False)
+
+    def event_time(fn, k):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / k
+
+    host = torch.from_numpy(cu)
+    max_chunks = int(((lens + 15) // 16).sum())
+    ws = torch.empty(kda.prefill_chunks_workspace_bytes(H, max_chunks),
+                     dtype=torch.uint8, device=dev)
+
+    def two_pass():
+        idx, off = kda.chunk_metadata(cu_d, kda.PREFILL_CHUNK,
+                                      cu_seqlens_host=host, stream=stream)
+        kda.kda_prefill_chunks(cu_d, idx, off, max_chunks, t["qkv"],
+                               t["conv_w"], t["conv_state"], t["rec_state"],
+                               t["g"], t["beta"], t["gate"], t["norm_w"],
+                               t["state_idx"], out, ws, eps=w.eps,
+                               variants=flags, stream=stream)
+
+    # raw gates (the activation fused into the chunk kernel): raw_g ~
+    # N(-3, 1) (per-token decays of a few hundredths to a few tenths),
+    # raw_beta ~ N(0, 1), A_log, dt_bias ~ N(0, 0.5), conv bias ~ N(0, 0.3)
+    rr = np.random.default_rng([7, 3])
+    rg = synth.to_torch({
+        "raw_g": synth.to_bf16_bits(
+            rr.normal(-3, 1, (total, H, 128)).astype(np.float32)),
+        "raw_beta": synth.to_bf16_bits(
+            rr.normal(0, 1, (total, H)).astype(np.float32)),
+        "A_log": rr.normal(0, 0.5, H).astype(np.float32),
+        "dt_bias": rr.normal(0, 0.5, H * 128).astype(np.float32),
+        "conv_bias": rr.normal(0, 0.3, 3 * H * 128).astype(np.float32)}, dev)
+
+    def raw_gates():
+        kda.kda_prefill_chunked_raw_gates(
+            cu_d, t["qkv"], t["conv_w"], rg["conv_bias"], t["conv_state"],
+            t["rec_state"], rg["raw_g"], rg["raw_beta"], rg["A_log"],
+            rg["dt_bias"], t["gate"], t["norm_w"], t["state_idx"], out,
+            eps=w.eps, variants=flags, stream=stream)
+
+    kern_two = event_time(two_pass, max(K // 2, 1))
+    kern_raw = event_time(raw_gates, max(K // 2, 1))
     updates = total * H
     # matrix-core work of the chunked form per (16-token chunk, head): K~S,
     # Q~S and the state update (3 x 2*16*128*128), the A and B products and
@@ -369,7 +419,6 @@ def bench_prefill(args, np, torch, kda, synth):
     per_tok = (3 * 128 * 2 + 128 * 4 + 4 + 128 * 2 + 128 * 2) * H
     nbytes = N * H * (2 * 128 * 128 * 4 + 2 * 2304) + total * per_tok
     # chunk metadata beside it
-    host = torch.from_numpy(cu)
     kda.chunk_metadata(cu_d, 64, cu_seqlens_host=host)
     torch.cuda.synchronize()
     m0 = torch.cuda.Event(enable_timing=True)
@@ -430,6 +479,8 @@ def bench_prefill(args, np, torch, kda, synth):
                   "hbm_GBs": round(nbytes / kern / 1e9, 1),
                   "sequential_kernel_us": round(kern_seq * 1e6, 2),
                   "speedup_vs_sequential": round(kern_seq / kern, 2),
+                  "two_pass_us": round(kern_two * 1e6, 2),
+                  "raw_gates_us": round(kern_raw * 1e6, 2),
                   "chunk_metadata_us": round(meta_us, 2)},
     }
     print(json.dumps(line), flush=True)
