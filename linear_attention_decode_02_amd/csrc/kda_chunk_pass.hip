@@ -20,13 +20,23 @@
 // (chunk, head) into the caller's workspace, laid out as the second pass
 // reads them (rows padded against LDS bank conflicts).
 //
-// Pass 2, kda_chunk_state_kernel: one 256-thread workgroup per (sequence,
-// head) carries the 128 x 128 state through the sequence's chunks in MFMA
-// accumulator registers (32 value columns per wave): K~S and Q~S, the
-// deltas T beta (V - K~S), the outputs Q~S + B Delta, the state update
-// e^{G_last} S + K^^T Delta, then the gated RMSNorm.  The next chunk's
-// record streams into LDS (global_load_lds) while the current one is
-// processed, so its serial chain holds only the state's matrix work.
+// Pass 2, kda_chunk_state_kernel: one wave per 16-column block of the
+// state (the value columns evolve independently: the delta rule couples
+// keys, not values), kStateWaves waves per workgroup and kSplits = 8 /
+// kStateWaves workgroups per (sequence, head).  A wave holds its 128 x 16
+// block in MFMA accumulator registers through the sequence's chunks: K~S and
+// Q~S, the deltas T beta (V - K~S), the outputs Q~S + B Delta (into the
+// record's output rows, before the norm) and the state update
+// e^{G_last} S + K^^T Delta.  The next chunk's record streams into LDS
+// (global_load_lds) while the current one is processed.  Eight waves in one
+// workgroup (two per SIMD) measured fastest: one wave per SIMD issues at
+// most one fp32 MFMA per 32 cycles, two waves share a SIMD at one per 24, so
+// splitting a (sequence, head) over more compute units with fewer waves each
+// gained nothing.  The workgroups of one (sequence, head) share
+// blockIdx % 8, i.e. one XCD and its L2, when kSplits > 1.
+//
+// Pass 3, kda_chunk_out_kernel: one workgroup per (chunk, head) applies the
+// gated RMSNorm, which needs all 128 columns of a token, and writes bf16.
 
 #include <hip/hip_runtime.h>
 
@@ -56,8 +66,20 @@ constexpr int kRecGam = kRecKh + kC * kLd;    // e^{G_last} [kD]
 constexpr int kRecBeta = kRecGam + kD;        // beta [kC]
 constexpr int kRecT = kRecBeta + kC;          // T    [kC][kTd]
 constexpr int kRecB = kRecT + kC * kTd;       // B    [kC][kTd]
-constexpr int kRecFloats = kRecB + kC * kTd;
-static_assert(kRecFloats % 4 == 0, "16-byte records");
+constexpr int kRecO = kRecB + kC * kTd;       // O (pass 2) [kC][kD]
+constexpr int kRecStaged = kRecO;             // what pass 2 copies to LDS
+constexpr int kRecFloats = kRecO + kC * kD;
+static_assert(kRecFloats % 4 == 0 && kRecStaged % 4 == 0, "16-byte records");
+constexpr int kStateWaves = 8;                // 16 value columns per wave
+constexpr int kSplits = kD / (16 * kStateWaves);
+constexpr int kBufs = 3;                      // records in flight in LDS
+// LDS-direct copy instructions per wave per record (the fewest any wave of
+// the workgroup issues: the last wave's count)
+constexpr int kStageBytes = kRecStaged * 4;
+constexpr int kDmaMin =
+    (kStageBytes - (kStateWaves - 1) * 1024 + kStateWaves * 1024 - 1) /
+    (kStateWaves * 1024);
+static_assert(kDmaMin >= 1 && kDmaMin < 64, "vmcnt range");
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
@@ -121,6 +143,12 @@ __device__ __forceinline__ void load_lds16(const void* src, void* dst) {
 }
 // s_waitcnt (gfx9 fields): vmcnt 0, the other counters at their maximum
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// vmcnt N (bits 3:0 and 15:14), expcnt and lgkmcnt at their maximum
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Sequence n's token range; false for an empty sequence.
 __device__ __forceinline__ bool seq_range(const KdaPassArgs& p, int n,
@@ -403,127 +431,93 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
 
 // ---- pass 2 -----------------------------------------------------------------
 
-struct alignas(16) StateSmem {
-  float rec[2][kRecFloats];  // the current and the next chunk's record
-  float o[kC][kLd];          // outputs of the chunk before the norm
-  float nw[kD];
-};
-
-template <bool kNorm>
-__global__ __launch_bounds__(kThreads) void kda_chunk_state_kernel(
+__global__ __launch_bounds__(64 * kStateWaves) void kda_chunk_state_kernel(
     KdaPassArgs p) {
-  __shared__ StateSmem sm;
+  __shared__ alignas(16) float rec[kBufs][kRecStaged];  // records in flight
   const int tid = threadIdx.x;
-  const int pw = tid >> 6;  // value columns 32pw .. 32pw+31
+  const int wave = tid >> 6;
   const int lane = tid & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;
   const int H = p.heads;
   const int C = H * kD;
   const int C3 = 3 * C;
-  const int n = static_cast<int>(blockIdx.x) / H;
-  const int h = static_cast<int>(blockIdx.x) % H;
+  // blockIdx = ((unit / 8) * kSplits + split) * 8 + unit % 8
+  const int64_t b = blockIdx.x;
+  const int split = static_cast<int>((b >> 3) % kSplits);
+  const int64_t unit = ((b >> 3) / kSplits) * 8 + (b & 7);
+  if (unit >= static_cast<int64_t>(p.num_seqs) * H) return;
+  const int n = static_cast<int>(unit / H);
+  const int h = static_cast<int>(unit % H);
   int32_t tb;
   int len;
   if (!seq_range(p, n, tb, len)) return;
   const int32_t slot = p.state_idx[n];
-  const int64_t col0 = static_cast<int64_t>(h) * kD;
+  if (slot <= 0 || slot >= p.num_slots) return;  // pass 3 writes the zeros
   const int nchunks = (len + kC - 1) / kC;
   const int64_t q0 = p.chunk_offsets[n];
-  if (slot <= 0 || slot >= p.num_slots) {
-    // null slot: +0.0 outputs, no state traffic
-    uint32_t* o32 = reinterpret_cast<uint32_t*>(p.out);
-    for (int64_t idx = tid; idx < static_cast<int64_t>(len) * (kD / 2);
-         idx += kThreads) {
-      const int64_t t = idx / (kD / 2);
-      o32[((tb + t) * C + col0) / 2 + idx % (kD / 2)] = 0u;
-    }
-    return;
-  }
   // records beyond the workspace: a table inconsistent with max_chunks
   if (q0 < 0 || q0 + nchunks > p.max_chunks) return;
-  const uint32_t flags = p.flags;
-  const bool gate_silu = (flags & KDA_GATE_SILU) != 0;
+  const int col = 16 * (split * kStateWaves + wave) + c;  // this lane's column
+  const int64_t col0 = static_cast<int64_t>(h) * kD;
 
-  float* st = p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD) +
-              32 * pw + c;
-  f4 S[2][8];
+  float* st =
+      p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD) + col;
+  f4 S[8];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[cb][kb][r] = st[(16 * kb + 4 * gq + r) * kD + 16 * cb];
-  if (kNorm && tid < kD) sm.nw[tid] = p.norm_w[tid];
-  const int ot = tid >> 4;      // output token of this lane
-  const int oc = 8 * (tid & 15);  // and its 8 columns
+    for (int r = 0; r < 4; ++r) S[kb][r] = st[(16 * kb + 4 * gq + r) * kD];
 
-  // chunk ci's record into buffer ci & 1: 16 bytes per lane, spread over
-  // the four waves
+  // chunk ci's record into buffer ci % kBufs: 16 bytes per lane, spread
+  // over the waves (wave w issues kDmaMin or more copy instructions)
   auto stage = [&](int ci) {
     const char* src = reinterpret_cast<const char*>(
         p.workspace + ((q0 + ci) * H + h) * kRecFloats);
-    char* dst = reinterpret_cast<char*>(&sm.rec[ci & 1][0]);
-    constexpr int kBytes = kRecFloats * 4;
-    for (int off = pw * 1024; off < kBytes; off += 4096) {
-      if (off + 16 * lane < kBytes) load_lds16(src + off + 16 * lane, dst + off);
+    char* dst = reinterpret_cast<char*>(&rec[ci % kBufs][0]);
+    for (int off = wave * 1024; off < kStageBytes;
+         off += kStateWaves * 1024) {
+      if (off + 16 * lane < kStageBytes)
+        load_lds16(src + off + 16 * lane, dst + off);
     }
   };
-  stage(0);
+  for (int i = 0; i < kBufs - 1 && i < nchunks; ++i) stage(i);
   wait_vmem();
   __syncthreads();
 
   for (int ci = 0; ci < nchunks; ++ci) {
-    if (ci + 1 < nchunks) stage(ci + 1);
-    const float* R = sm.rec[ci & 1];
+    // the buffer of chunk ci + kBufs - 1 was last read in chunk ci - 1,
+    // before the barrier that ended it
+    if (ci + kBufs - 1 < nchunks) stage(ci + kBufs - 1);
+    const float* R = rec[ci % kBufs];
     const int nv = len - ci * kC < kC ? len - ci * kC : kC;
-    u4 gate_raw = {0u, 0u, 0u, 0u};
-    if (kNorm) {
-      const int rr = ot < nv - 1 ? ot : nv - 1;
-      gate_raw = *reinterpret_cast<const u4*>(
-          p.gate + (tb + static_cast<int64_t>(ci) * kC + rr) * C + col0 + oc);
-    }
-    // K~ S and Q~ S
-    f4 ks[2], o[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      ks[cb] = f4{0.f, 0.f, 0.f, 0.f};
-      o[cb] = f4{0.f, 0.f, 0.f, 0.f};
-    }
+    // K~ S and Q~ S for this wave's 16 columns
+    f4 ks = {0.f, 0.f, 0.f, 0.f};
+    f4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
       const f4 ak = ld4(&R[kRecKt + c * kLd + 16 * kb + 4 * gq]);
       const f4 aq = ld4(&R[kRecQt + c * kLd + 16 * kb + 4 * gq]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          ks[cb] = mfma(ak[j], S[cb][kb][j], ks[cb]);
-          o[cb] = mfma(aq[j], S[cb][kb][j], o[cb]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        ks = mfma(ak[j], S[kb][j], ks);
+        o = mfma(aq[j], S[kb][j], o);
+      }
     }
     // Delta = T beta (V - K~ S);  O += B Delta
     const f4 at = ld4(&R[kRecT + c * kTd + 4 * gq]);
     const f4 ab = ld4(&R[kRecB + c * kTd + 4 * gq]);
-    f4 dl[2];
+    f4 br;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int col = 32 * pw + 16 * cb + c;
-      f4 br;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * gq + r;
-        br[r] = R[kRecBeta + t] * (R[kRecV + t * kLd + col] - ks[cb][r]);
-      }
-      dl[cb] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dl[cb] = mfma(at[j], br[j], dl[cb]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[cb] = mfma(ab[j], dl[cb][j], o[cb]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.o[4 * gq + r][col] = o[cb][r];
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * gq + r;
+      br[r] = R[kRecBeta + t] * (R[kRecV + t * kLd + col] - ks[r]);
     }
+    f4 dl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dl = mfma(at[j], br[j], dl);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o = mfma(ab[j], dl[j], o);
     // S <- e^{G_last} S + K^^T Delta; A operand K^[token 4gq + j][key
     // 16kb + c] (rows of K^, one dword per token)
 #pragma unroll
@@ -533,57 +527,35 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_state_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         ah[j] = R[kRecKh + (4 * gq + j) * kLd + 16 * kb + c];
+      S[kb] *= gm;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        S[cb][kb] *= gm;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          S[cb][kb] = mfma(ah[j], dl[cb][j], S[cb][kb]);
-      }
+      for (int j = 0; j < 4; ++j) S[kb] = mfma(ah[j], dl[j], S[kb]);
     }
-    __syncthreads();
-    // gated RMSNorm and bf16 outputs: token ot, columns oc .. oc+7
-    {
-      const f4 v0 = ld4(&sm.o[ot][oc]);
-      const f4 v1 = ld4(&sm.o[ot][oc + 4]);
-      float yv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      if (kNorm) {
-        float ss = 0.0f;
+    // the next record is in LDS (this wave's part): with a younger record
+    // in flight, vector memory loads return in order, so at most kDmaMin
+    // outstanding operations means the older copies have all landed
+    if (kBufs > 2 && ci + kBufs - 1 < nchunks)
+      wait_vmcnt<kDmaMin>();
+    else
+      wait_vmem();
+    __syncthreads();  // ... and every other wave's; this buffer is free
+    // outputs before the norm into the record's O rows (valid tokens),
+    // issued after the wait: vmcnt counts stores too, so stores issued
+    // before it would hold every chunk until they are acknowledged
+    float* O = p.workspace + ((q0 + ci) * H + h) * kRecFloats + kRecO + col;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss += yv[j] * yv[j];
-        ss = row_sum16(ss);
-        const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t w2 = gate_raw[j >> 1];
-          const float gv = (j & 1) ? bf16_hi(w2) : bf16_lo(w2);
-          const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
-          yv[j] = ((yv[j] * rs) * sm.nw[oc + j]) * ga;
-        }
-      }
-      if (ot < nv) {
-        const u4 pk = {pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3]),
-                       pack_bf16(yv[4], yv[5]), pack_bf16(yv[6], yv[7])};
-        *reinterpret_cast<u4*>(
-            p.out + (tb + static_cast<int64_t>(ci) * kC + ot) * C + col0 +
-            oc) = pk;
-      }
-    }
-    wait_vmem();      // the next record is in LDS (this wave's part)
-    __syncthreads();  // ... and every other wave's; sm.o is free again
+    for (int r = 0; r < 4; ++r)
+      if (4 * gq + r < nv) O[(4 * gq + r) * kD] = o[r];
   }
 
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        st[(16 * kb + 4 * gq + r) * kD + 16 * cb] = S[cb][kb][r];
+    for (int r = 0; r < 4; ++r) st[(16 * kb + 4 * gq + r) * kD] = S[kb][r];
   // conv window: the last W-1 inputs of (stored window ++ tokens)
-  if ((flags & KDA_NO_CONV_UPDATE) == 0) {
-    const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
-    for (int i = tid; i < 3 * kD; i += kThreads) {
+  if (split == 0 && (p.flags & KDA_NO_CONV_UPDATE) == 0) {
+    const bool tap_major = (p.flags & KDA_CONV_TAP_MAJOR) != 0;
+    for (int i = tid; i < 3 * kD; i += 64 * kStateWaves) {
       const int64_t ch = (i >> 7) * static_cast<int64_t>(C) + col0 + (i & 127);
       auto at = [&](int e) -> int64_t {
         return tap_major
@@ -603,6 +575,71 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_state_kernel(
   }
 }
 
+// ---- pass 3 -----------------------------------------------------------------
+
+template <bool kNorm>
+__global__ __launch_bounds__(kThreads) void kda_chunk_out_kernel(
+    KdaPassArgs p) {
+  const int tid = threadIdx.x;
+  const int H = p.heads;
+  const int C = H * kD;
+  const int64_t q = blockIdx.x / H;
+  const int h = static_cast<int>(blockIdx.x % H);
+  const int64_t total = p.chunk_offsets[p.num_seqs];
+  if (q >= total || q >= p.max_chunks) return;
+  const int n = p.chunk_indices[2 * q];
+  const int ci = p.chunk_indices[2 * q + 1];
+  if (n < 0 || n >= p.num_seqs || ci < 0) return;
+  int32_t tb;
+  int len;
+  if (!seq_range(p, n, tb, len) || ci * kC >= len) return;
+  // the state pass skipped this sequence: leave its outputs alone
+  const int64_t q0 = p.chunk_offsets[n];
+  if (q0 < 0 || q0 + (len + kC - 1) / kC > p.max_chunks) return;
+  const int nv = len - ci * kC < kC ? len - ci * kC : kC;
+  const int ot = tid >> 4;        // token of the chunk
+  const int oc = 8 * (tid & 15);  // and 8 of its columns
+  const int64_t col0 = static_cast<int64_t>(h) * kD;
+  u4* dst = reinterpret_cast<u4*>(
+      p.out + (tb + static_cast<int64_t>(ci) * kC + ot) * C + col0 + oc);
+  const int32_t slot = p.state_idx[n];
+  if (slot <= 0 || slot >= p.num_slots) {  // null row: +0.0
+    if (ot < nv) *dst = u4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const float* O =
+      p.workspace + (q * H + h) * kRecFloats + kRecO + ot * kD + oc;
+  // rows past the end of the sequence read the last valid row (not stored)
+  const int rr = ot < nv ? 0 : (nv - 1 - ot) * kD;
+  const f4 v0 = ld4(O + rr);
+  const f4 v1 = ld4(O + rr + 4);
+  float yv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  if (kNorm) {
+    const bool gate_silu = (p.flags & KDA_GATE_SILU) != 0;
+    const int tr = ot < nv ? ot : nv - 1;
+    const u4 gate_raw = *reinterpret_cast<const u4*>(
+        p.gate + (tb + static_cast<int64_t>(ci) * kC + tr) * C + col0 + oc);
+    const f4 w0 = ld4(p.norm_w + oc);
+    const f4 w1 = ld4(p.norm_w + oc + 4);
+    const float nw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += yv[j] * yv[j];
+    ss = row_sum16(ss);
+    const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w2 = gate_raw[j >> 1];
+      const float gv = (j & 1) ? bf16_hi(w2) : bf16_lo(w2);
+      const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
+      yv[j] = ((yv[j] * rs) * nw[j]) * ga;
+    }
+  }
+  if (ot < nv)
+    *dst = u4{pack_bf16(yv[0], yv[1]), pack_bf16(yv[2], yv[3]),
+              pack_bf16(yv[4], yv[5]), pack_bf16(yv[6], yv[7])};
+}
+
 }  // namespace
 
 uint64_t kda_pass_record_bytes() {
@@ -610,17 +647,22 @@ uint64_t kda_pass_record_bytes() {
 }
 
 hipError_t kda_chunk_pass_launch(const KdaPassArgs& args, hipStream_t stream) {
-  const unsigned prep_blocks =
+  const unsigned chunk_blocks =
       static_cast<unsigned>(args.max_chunks * args.heads);
-  if (prep_blocks > 0)
-    hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3(prep_blocks),
+  if (chunk_blocks > 0)
+    hipLaunchKernelGGL(kda_chunk_prep_kernel, dim3(chunk_blocks),
                        dim3(kThreads), 0, stream, args);
-  const dim3 grid(static_cast<unsigned>(args.num_seqs * args.heads));
-  if (args.flags & KDA_OUTPUT_NORM)
-    hipLaunchKernelGGL(kda_chunk_state_kernel<true>, grid, dim3(kThreads), 0,
-                       stream, args);
-  else
-    hipLaunchKernelGGL(kda_chunk_state_kernel<false>, grid, dim3(kThreads), 0,
-                       stream, args);
+  const int64_t units = static_cast<int64_t>(args.num_seqs) * args.heads;
+  const dim3 grid(static_cast<unsigned>((units + 7) / 8 * 8 * kSplits));
+  hipLaunchKernelGGL(kda_chunk_state_kernel, grid, dim3(64 * kStateWaves), 0,
+                     stream, args);
+  if (chunk_blocks > 0) {
+    if (args.flags & KDA_OUTPUT_NORM)
+      hipLaunchKernelGGL(kda_chunk_out_kernel<true>, dim3(chunk_blocks),
+                         dim3(kThreads), 0, stream, args);
+    else
+      hipLaunchKernelGGL(kda_chunk_out_kernel<false>, dim3(chunk_blocks),
+                         dim3(kThreads), 0, stream, args);
+  }
   return hipGetLastError();
 }

@@ -1141,7 +1141,8 @@ kda_status prefill_chunks_impl(
   kda_status st = check_prefill_gates(d, gi);
   if (st != KDA_OK) return st;
   if (max_chunks < 0 ||
-      max_chunks * static_cast<int64_t>(d->num_heads) > INT32_MAX)
+      max_chunks * static_cast<int64_t>(d->num_heads) > INT32_MAX ||
+      static_cast<int64_t>(d->batch) * d->num_heads * 8 > INT32_MAX)
     return KDA_ERR_INVALID_ARG;
   if (d->batch == 0) return KDA_OK;
   if (!cu_seqlens || !chunk_offsets ||

@@ -221,7 +221,7 @@ def test_prefill_and_metadata_argument_checks():
         assert fn(ctypes.byref(dims(batch=0)), *p[:11], None) == 0
     # kda_prefill_chunks: cu, indices, offsets, max, 10 tensors, ws, bytes
     need = L.kda_prefill_chunks_workspace_bytes(ctypes.byref(d), 5)
-    assert need == 5 * 12 * 36928
+    assert need == 5 * 12 * 45120
     assert L.kda_prefill_chunks_workspace_bytes(ctypes.byref(d), -1) == 0
     args = [FAKE, FAKE, FAKE, 5] + [FAKE] * 10 + [FAKE, need, None]
     assert L.kda_prefill_chunks(ctypes.byref(d), *args) == 4
