@@ -483,19 +483,49 @@ void kda_decode_kernel(Params p) {
 // Token-major buffers (qkv [tokens, 3C], g [tokens, H, D], beta
 // [tokens, H], gate and out [tokens, C]); row n covers tokens
 // n*T_fixed .. +T_fixed-1, or cu_seqlens[n] .. cu_seqlens[n+1]-1 when
-// p.cu_seqlens is set (variable-length prefill).  Three barriers per
-// token; the next token's small inputs are fetched while the current one
-// is processed.
+// p.cu_seqlens is set (variable-length prefill).
+//
+// Two barriers per token, software-pipelined one token deep: waves 4..7
+// compute token t+1's inputs (conv + SiLU of q, k, v; exp(g)) while waves
+// 0..3 finish token t's column sums, so the token chain holds only
+//   decay + partial sums | barrier | column sums (and next inputs) |
+//   barrier | rank-1 update + output.
+// Each input wave fetches its next token's small inputs one token ahead.
+
+// finish_columns with the token's v row taken from `v` (double-buffered by
+// token parity: the next token's v is written while this one is read).
+__device__ __forceinline__ void finish_columns_v(Lds& L, int tid, float beta,
+                                                 const float* v) {
+  if (tid < 2 * kD) {
+    const int which = tid / kD;
+    const int j = tid % kD;
+    float acc = L.red[0][which][j];
+#pragma unroll
+    for (int r = 1; r < 2 * kWaves; ++r) acc += L.red[r][which][j];
+    if (which == 0)
+      L.delta[j] = beta * (v[j] - acc);
+    else
+      L.p[j] = acc;
+    if (tid == 0) {
+      float t = L.qk[0];
+#pragma unroll
+      for (int r = 1; r < 2 * kWaves; ++r) t += L.qk[r];
+      L.qk_total = t;
+    }
+  }
+}
+
 template <bool kNorm>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void kda_decode_tokens_kernel(Params p, int T_fixed) {
   __shared__ Lds L;
   __shared__ f2 s_w[3][kW][kD / 2];   // conv taps, per part and lane
   __shared__ float s_norm_w[kD];
-  // {exp(g), k, q} rows by token parity: the update of token t re-reads k
-  // while token t+1's rows are being written into the other buffer
+  // {exp(g), k, q} rows and v by token parity: token t+1's rows are
+  // written while token t's are read
   __shared__ f4 s_akq[2][kD];
-  // conv window words of waves 0..2, kept in LDS across the token loop
+  __shared__ float s_v[2][kD];
+  // conv window words of input waves 4..6, kept in LDS across the tokens
   __shared__ uint32_t s_win[3][3][kD / 2];
 
   const int tid = threadIdx.x;
@@ -530,8 +560,11 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
 
   const uint32_t flags = p.flags;
   const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
+  // input waves 4..7: role 0 q, 1 k, 2 v (conv + SiLU), 3 exp(g)
+  const bool input_wave = wave >= 4 && wave < 8;
+  const int role = wave - 4;
   const int i0 = 2 * lane;
-  const int part = wave < 3 ? wave : 2;
+  const int part = input_wave && role < 3 ? role : 2;
   // per-lane 32-bit offsets from per-token uniform bases
   const uint32_t c = part * C + h * kD + i0;         // into a qkv token row
   const uint32_t gi = h * kD + i0;                   // into a g token row
@@ -539,9 +572,14 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
   const uint16_t* qkv_row = p.qkv + row_tok * 3 * C;
   const float* g_row = p.g + row_tok * H * kD;
   const float* beta_row = p.beta + row_tok * H;
-  uint32_t x2 = *at_bytes<const uint32_t>(uniform_gptr(qkv_row), 2 * c);
-  f2 g2 = *at_bytes<const f2>(uniform_gptr(g_row), 4 * gi);
-  float beta = beta_row[h];
+  // small inputs of the token an input wave computes next
+  uint32_t x2 = 0u;
+  f2 g2 = {0.f, 0.f};
+  if (input_wave) {
+    x2 = *at_bytes<const uint32_t>(uniform_gptr(qkv_row), 2 * c);
+    g2 = *at_bytes<const f2>(uniform_gptr(g_row), 4 * gi);
+  }
+  float beta = beta_row[h];  // of the token waves 0..3 finish next
   // output gate words of lanes 0..31 (wave 0 loads them; lanes 32..63
   // mirror 0..31)
   u2 gate_w = {0u, 0u};
@@ -552,19 +590,17 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
   const uint32_t cs_off = (tap_major ? c : c * (kW - 1)) / 2;  // in words
   const uint32_t cs_step = tap_major ? (3 * C) / 2 : 1;
   const gptr<uint32_t> cs_g = uniform_gptr(cs_slot);
-  if (wave < 3) {
-    s_win[0][wave][lane] = *at_bytes<uint32_t>(cs_g, 4 * cs_off);
-    s_win[1][wave][lane] = *at_bytes<uint32_t>(cs_g, 4 * (cs_off + cs_step));
-    s_win[2][wave][lane] =
+  const bool conv_wave = input_wave && role < 3;
+  if (conv_wave) {
+    s_win[0][role][lane] = *at_bytes<uint32_t>(cs_g, 4 * cs_off);
+    s_win[1][role][lane] = *at_bytes<uint32_t>(cs_g, 4 * (cs_off + cs_step));
+    s_win[2][role][lane] =
         *at_bytes<uint32_t>(cs_g, 4 * (cs_off + 2 * cs_step));
-  }
-  // conv taps and norm weights go to LDS once (read per token: fewer live
-  // VGPRs across the token loop)
-  if (wave < 3) {
+    // conv taps to LDS once (read per token: fewer live VGPRs)
 #pragma unroll
     for (int t = 0; t < kW; ++t)
-      s_w[wave][t][lane] = *reinterpret_cast<const f2*>(
-          p.conv_w + (wave * kW + t) * C + h * kD + i0);
+      s_w[role][t][lane] = *reinterpret_cast<const f2*>(
+          p.conv_w + (role * kW + t) * C + h * kD + i0);
   } else if (wave == 3 && kNorm) {
     *reinterpret_cast<f2*>(&s_norm_w[i0]) =
         *reinterpret_cast<const f2*>(p.norm_w + i0);
@@ -581,7 +617,56 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
   for (int m = 0; m < kRowsPerThread; ++m)
     s[m] = __builtin_nontemporal_load(tile_at(st, lane_off, m));
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();   // s_w, s_norm_w visible
+  __syncthreads();   // s_w, s_win, s_norm_w visible
+
+  // Input waves: token tt's q/k/v/exp(g) into the buffers of its parity,
+  // the conv window advanced in LDS, then the small inputs of token tn
+  // fetched for the next call.
+  auto inputs = [&](int tt, int tn) {
+    int tid_t = tid;
+    asm volatile("" : "+v"(tid_t));
+    const int lane_t = tid_t & 63;
+    const int role_t = (tid_t >> 6) - 4;
+    const int part_t = role_t < 3 ? role_t : 2;
+    const int i0_t = 2 * lane_t;
+    f2 w_t[kW];
+#pragma unroll
+    for (int tap = 0; tap < kW; ++tap) w_t[tap] = s_w[part_t][tap][lane_t];
+    uint32_t cw0 = 0, cw1 = 0, cw2 = 0;
+    if (role_t < 3) {
+      cw0 = s_win[0][role_t][lane_t];
+      cw1 = s_win[1][role_t][lane_t];
+      cw2 = s_win[2][role_t][lane_t];
+    }
+    float y0, y1;
+    token_inputs(flags, role_t, cw0, cw1, cw2, x2, w_t, f2{0.f, 0.f}, false,
+                 g2, y0, y1);
+    // successive calls with the update off all see the stored window
+    if (role_t < 3 && !(flags & KDA_NO_CONV_UPDATE)) {
+      shift_window(tap_major, cw0, cw1, cw2, x2);
+      s_win[0][role_t][lane_t] = cw0;
+      s_win[1][role_t][lane_t] = cw1;
+      s_win[2][role_t][lane_t] = cw2;
+    }
+    if (role_t == 2) {
+      *reinterpret_cast<f2*>(&s_v[tt & 1][i0_t]) = f2{y0, y1};
+    } else {
+      // q -> .z, k -> .y, exp(g) -> .x
+      const int comp = role_t == 0 ? 2 : (role_t == 1 ? 1 : 0);
+      float* base = reinterpret_cast<float*>(s_akq[tt & 1]);
+      base[i0_t * 4 + comp] = y0;
+      base[(i0_t + 1) * 4 + comp] = y1;
+    }
+    const uint32_t c_t = part_t * C + h * kD + i0_t;
+    const uint32_t gi_t = h * kD + i0_t;
+    x2 = *at_bytes<const uint32_t>(
+        uniform_gptr(qkv_row + static_cast<int64_t>(tn) * 3 * C), 2 * c_t);
+    g2 = *at_bytes<const f2>(
+        uniform_gptr(g_row + static_cast<int64_t>(tn) * H * kD), 4 * gi_t);
+  };
+
+  if (input_wave) inputs(0, T > 1 ? 1 : 0);
+  __syncthreads();   // token 0's inputs
 
   for (int t = 0; t < T; ++t) {
     // Lane-derived offsets are recomputed every token from an opaque copy
@@ -591,58 +676,22 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
     asm volatile("" : "+v"(tid_t));
     const int wave_t = tid_t >> 6;
     const int lane_t = tid_t & 63;
-    const int i0_t = 2 * lane_t;
-    const int part_t = wave_t < 3 ? wave_t : 2;
     const int col4_t = tid_t & 31;
     const int rgrp_t = tid_t >> 5;
-    const uint32_t c_t = part_t * C + h * kD + i0_t;
-    const uint32_t gi_t = h * kD + i0_t;
     const uint32_t oc_t = h * kD + 4 * col4_t;
 
-    f4* akq_t = s_akq[t & 1];
-    if (wave_t < 4) {   // per-token inputs: waves 0..3 only (uniform branch)
-      f2 w_t[kW];
-#pragma unroll
-      for (int tap = 0; tap < kW; ++tap) w_t[tap] = s_w[part_t][tap][lane_t];
-      // each lane of waves 0..2 owns its window words
-      uint32_t cw0 = 0, cw1 = 0, cw2 = 0;
-      if (wave_t < 3) {
-        cw0 = s_win[0][wave_t][lane_t];
-        cw1 = s_win[1][wave_t][lane_t];
-        cw2 = s_win[2][wave_t][lane_t];
-      }
-      float y0, y1;
-      token_inputs(flags, wave_t, cw0, cw1, cw2, x2, w_t, f2{0.f, 0.f}, false,
-                   g2, y0, y1);
-      // successive calls with the update off all see the stored window
-      if (wave_t < 3 && !(flags & KDA_NO_CONV_UPDATE)) {
-        shift_window(tap_major, cw0, cw1, cw2, x2);
-        s_win[0][wave_t][lane_t] = cw0;
-        s_win[1][wave_t][lane_t] = cw1;
-        s_win[2][wave_t][lane_t] = cw2;
-      }
-      store_token_inputs(L, wave_t, i0_t, y0, y1, akq_t);
-    }
-    __syncthreads();
+    const f4* akq_t = s_akq[t & 1];
     float k_unused[kRowsPerThread];
     decay_and_partials<true>(L, s, k_unused, rgrp_t, wave_t, lane_t, col4_t,
                              akq_t);
     __syncthreads();
-
-    // fetch the next token's small inputs; they are used one iteration
-    // later (issued after the decay phase, the register peak)
-    const int tn = t + 1 < T ? t + 1 : t;
-    const uint32_t x2_next = *at_bytes<const uint32_t>(
-        uniform_gptr(qkv_row + static_cast<int64_t>(tn) * 3 * C), 2 * c_t);
-    const f2 g2_next = *at_bytes<const f2>(
-        uniform_gptr(g_row + static_cast<int64_t>(tn) * H * kD), 4 * gi_t);
-    const float beta_next = beta_row[static_cast<int64_t>(tn) * H + h];
-    u2 gate_next = {0u, 0u};
-    if (kNorm && wave_t == 0)
-      gate_next = *at_bytes<const u2>(
-          uniform_gptr(p.gate + (row_tok + tn) * C), 2 * oc_t);
-
-    finish_columns(L, tid_t, beta);
+    if (wave_t < 4) {
+      finish_columns_v(L, tid_t, beta, s_v[t & 1]);
+      const int tn = t + 1 < T ? t + 1 : t;
+      beta = beta_row[static_cast<int64_t>(tn) * H + h];
+    } else if (wave_t < 8 && t + 1 < T) {
+      inputs(t + 1, t + 2 < T ? t + 2 : t + 1);
+    }
     __syncthreads();
     const f4 delta = *reinterpret_cast<const f4*>(&L.delta[4 * col4_t]);
 #pragma unroll
@@ -653,21 +702,20 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
                          at_bytes<uint16_t>(
                              uniform_gptr(p.out + (row_tok + t) * C), 2 * oc_t));
     }
-    x2 = x2_next;
-    g2 = g2_next;
-    beta = beta_next;
-    gate_w = gate_next;
+    if (kNorm && wave_t == 0 && t + 1 < T)
+      gate_w = *at_bytes<const u2>(
+          uniform_gptr(p.gate + (row_tok + t + 1) * C), 2 * oc_t);
   }
 
   // ---- write back: state tile once, conv window once ----------------------
 #pragma unroll
   for (int m = 0; m < kRowsPerThread; ++m)
     __builtin_nontemporal_store(s[m], tile_at(st, lane_off, m));
-  if (wave < 3 && !(flags & KDA_NO_CONV_UPDATE)) {
-    *at_bytes<uint32_t>(cs_g, 4 * cs_off) = s_win[0][wave][lane];
-    *at_bytes<uint32_t>(cs_g, 4 * (cs_off + cs_step)) = s_win[1][wave][lane];
+  if (conv_wave && !(flags & KDA_NO_CONV_UPDATE)) {
+    *at_bytes<uint32_t>(cs_g, 4 * cs_off) = s_win[0][role][lane];
+    *at_bytes<uint32_t>(cs_g, 4 * (cs_off + cs_step)) = s_win[1][role][lane];
     *at_bytes<uint32_t>(cs_g, 4 * (cs_off + 2 * cs_step)) =
-        s_win[2][wave][lane];
+        s_win[2][role][lane];
   }
 }
 
@@ -799,9 +847,10 @@ Params base_params(const kda_dims* d, const void* qkv, const float* conv_w,
 
 // From this many tokens per row on, kda_decode_tokens runs the chunked
 // (matrix-core) kernel: measured on MI355X with 256 rows x 48 heads, the
-// token-by-token kernel takes 1073 us at T = 16 against 934 us chunked
-// (1911 against 1224 at T = 32), and is faster below 16.
-constexpr int32_t kChunkedMinTokens = 16;
+// token-by-token kernel takes 836 / 989 / 1126 / 1414 us at T = 16 / 20 /
+// 24 / 32 against 848 / 1109 / 1101 / 1097 us chunked (a chunk is 16
+// tokens, so 17..32 tokens cost two).
+constexpr int32_t kChunkedMinTokens = 24;
 
 KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
                             int32_t tokens_per_row, const void* qkv,

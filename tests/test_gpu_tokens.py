@@ -146,17 +146,17 @@ def test_tokens_b256_h48_full_size():
 
 
 CHUNKED_CASES = [
-    ("plain", 0, True, 16), ("nonorm", 0, False, 17),
+    ("plain", 0, True, 24), ("nonorm", 0, False, 25),
     ("tap_major", O.CONV_TAP_MAJOR, True, 33),
-    ("l2_silu", O.QK_L2NORM | O.GATE_SILU, True, 16),
-    ("no_conv_update", O.NO_CONV_UPDATE, True, 20),
+    ("l2_silu", O.QK_L2NORM | O.GATE_SILU, True, 24),
+    ("no_conv_update", O.NO_CONV_UPDATE, True, 40),
 ]
 
 
 @pytest.mark.parametrize("name,flags,norm,T", CHUNKED_CASES,
                          ids=[c[0] for c in CHUNKED_CASES])
-def test_tokens_from_16_take_the_chunked_form(name, flags, norm, T):
-    """From 16 tokens per row the call runs the chunked matrix-core form;
+def test_tokens_from_24_take_the_chunked_form(name, flags, norm, T):
+    """From 24 tokens per row the call runs the chunked matrix-core form;
     it must still equal T successive single-token steps (the oracle)."""
     H = 24
     w = synth.small(f"tc_{name}", batch=9, heads=H, num_slots=14,
@@ -177,10 +177,10 @@ def test_tokens_from_16_take_the_chunked_form(name, flags, norm, T):
     print(f"[tokens chunked] {name}: {st}", flush=True)
 
 
-def test_tokens_15_and_16_agree_with_single_calls():
+def test_tokens_23_and_24_agree_with_single_calls():
     """Either side of the switch to the chunked form, against T single-token
     kernel calls on the same inputs."""
-    for T in (15, 16):
+    for T in (23, 24):
         w = synth.small(f"tsw{T}", batch=12, heads=48, num_slots=20,
                         seed=170 + T, null_every=5, conv_w_sigma=0.05)
         inp = synth.make_tokens(w, T)
@@ -197,22 +197,23 @@ def test_tokens_15_and_16_agree_with_single_calls():
                            inp["state_idx"], w.num_slots, w.heads)
 
 
-def test_tokens_b256_h48_16_tokens_full_size():
+@pytest.mark.parametrize("T", [16, 24])
+def test_tokens_b256_h48_full_size(T):
     """The batch-256, 48-head workload (32 null rows) with 16 tokens per
-    row: the chunked form at full size, every element against the oracle.
+    row (token by token) and 24 (the chunked form) at full size, every
+    element against the oracle.
     q/k are L2-normalised (unit keys, beta < 1: each update contracts the
-    state along k).  Without it these inputs give beta |k|^2 near 40, and 16
-    chained updates amplify fp32 rounding order by that factor per token,
-    which no bar meaningful for single steps survives."""
+    state along k).  Without it these inputs give beta |k|^2 near 40, and
+    16 or more chained updates amplify fp32 rounding order by that factor
+    per token, which no bar meaningful for single steps survives."""
     w = synth.B256_H48
-    T = 16
     inp = synth.make_tokens(w, T)
     ref = O.decode_tokens(inp, heads=w.heads, tokens=T, norm=True, eps=w.eps,
                           flags=O.QK_L2NORM)
     got = run_tokens(w, inp, T, variants=O.QK_L2NORM)
     st = check_tokens(w, inp, got, ref, T)
     assert np.all(got["out"][-32:] == 0)
-    print(f"[tokens b256 T=16] {st}", flush=True)
+    print(f"[tokens b256 T={T}] {st}", flush=True)
 
 
 def test_tokens_argument_checks():
