@@ -311,3 +311,62 @@ def test_chunked_raw_gates_match_activated_gates():
     d = np.abs(raw["rec_state"] - plain["rec_state"]).max()
     print(f"[raw vs activated] state {d:.3g}", flush=True)
     assert d <= 1e-4 * max(1.0, np.abs(plain["rec_state"]).max())
+
+
+@pytest.mark.parametrize("path", ["fused", "two_pass"])
+def test_chunked_graph_replay_matches_eager(path):
+    """One chunked prefill call captured in a HIP graph and replayed three
+    times, with eager work and synchronisation between the replays: every
+    replay equals the same number of eager calls bit for bit (the call
+    updates its pools in place).  Neither path records a memset."""
+    lens, H = [40, 0, 17, 5], 24
+    w, inp, cu = prefill_case(260, lens, H, null=(3,))
+    te = synth.to_torch(inp, DEV)
+    tg = synth.to_torch(inp, DEV)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    idx, off = kda.chunk_metadata(cu_d, kda.PREFILL_CHUNK,
+                                  cu_seqlens_host=torch.from_numpy(cu))
+    max_chunks = int(idx.shape[0])
+    tokens = inp["qkv"].shape[0]
+    out_e = torch.zeros(tokens, w.channels, dtype=torch.bfloat16, device=DEV)
+    out_g = torch.zeros_like(out_e)
+    ws_e = torch.empty(kda.prefill_chunks_workspace_bytes(H, max_chunks),
+                       dtype=torch.uint8, device=DEV)
+    ws_g = torch.empty_like(ws_e)
+
+    def call(t, out, ws):
+        if path == "fused":
+            kda.kda_prefill(cu_d, t["qkv"], t["conv_w"], t["conv_state"],
+                            t["rec_state"], t["g"], t["beta"], t["gate"],
+                            t["norm_w"], t["state_idx"], out, eps=w.eps,
+                            chunked=True)
+        else:
+            kda.kda_prefill_chunks(cu_d, idx, off, max_chunks, t["qkv"],
+                                   t["conv_w"], t["conv_state"],
+                                   t["rec_state"], t["g"], t["beta"],
+                                   t["gate"], t["norm_w"], t["state_idx"],
+                                   out, ws, eps=w.eps)
+
+    warm = synth.to_torch(inp, DEV)
+    call(warm, torch.empty_like(out_e), torch.empty_like(ws_e))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cs0, rs0 = tg["conv_state"].clone(), tg["rec_state"].clone()
+    with torch.cuda.graph(graph):
+        call(tg, out_g, ws_g)
+    tg["conv_state"].copy_(cs0)
+    tg["rec_state"].copy_(rs0)
+    torch.cuda.synchronize()
+    for r in range(3):
+        call(te, out_e, ws_e)
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 20, device=DEV).sum()   # eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert scratch.isfinite()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), r
+        assert torch.equal(tg["conv_state"].view(torch.int16),
+                           te["conv_state"].view(torch.int16)), r
+        assert torch.equal(tg["rec_state"].view(torch.int32),
+                           te["rec_state"].view(torch.int32)), r
+        print(f"[chunked graph {path}] replay {r} matches eager", flush=True)
