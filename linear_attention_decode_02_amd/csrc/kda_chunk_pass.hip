@@ -162,18 +162,26 @@ __device__ __forceinline__ bool seq_range(const KdaPassArgs& p, int n,
 // ---- pass 1 -----------------------------------------------------------------
 
 struct PrepSmem {
-  float kt[kC][kLd];   // Gram inputs on the factored path
-  float qt[kC][kLd];
+  // Gram inputs: K~ and Q~ on the factored path, or raw q and the
+  // cumulative log2 decay on the exact path (one or the other per chunk)
+  union {
+    struct {
+      float kt[kC][kLd];
+      float qt[kC][kLd];
+    } f;
+    struct {
+      float qraw[kC][kLd];
+      float graw[kC][kLd];
+    } x;
+  } g;
   float ki[kC][kLd];   // k e^{-G}; raw k on the exact path
-  float qraw[kC][kLd];  // exact path
-  float graw[kC][kLd];  // exact path: cumulative log2 decay
   float part[4][kC][kC];
   float LT[kC][kTd];   // LT[s][t] = beta_t A_ts (s < t)
   float beta[kC];
   int unsafe;
 };
 
-__global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void kda_chunk_prep_kernel(
     KdaPassArgs p) {
   __shared__ alignas(16) PrepSmem sm;
   const int tid = threadIdx.x;
@@ -360,16 +368,16 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
         f2{y[u][2][0], y[u][2][1]};
     *reinterpret_cast<f2*>(&rec[kRecKh + t * kLd + 2 * lane]) =
         f2{y[u][1][0] * exp2_(G.x - Gu[u].x), y[u][1][1] * exp2_(G.y - Gu[u].y)};
-    *reinterpret_cast<f2*>(&sm.qt[t][2 * lane]) = qv;
-    *reinterpret_cast<f2*>(&sm.kt[t][2 * lane]) = kv;
     if (!unsafe) {
+      *reinterpret_cast<f2*>(&sm.g.f.qt[t][2 * lane]) = qv;
+      *reinterpret_cast<f2*>(&sm.g.f.kt[t][2 * lane]) = kv;
       *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) =
           f2{y[u][1][0] * exp2_(-Gu[u].x), y[u][1][1] * exp2_(-Gu[u].y)};
     } else {
       *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) = f2{y[u][1][0], y[u][1][1]};
-      *reinterpret_cast<f2*>(&sm.qraw[t][2 * lane]) =
+      *reinterpret_cast<f2*>(&sm.g.x.qraw[t][2 * lane]) =
           f2{y[u][0][0], y[u][0][1]};
-      *reinterpret_cast<f2*>(&sm.graw[t][2 * lane]) = Gu[u];
+      *reinterpret_cast<f2*>(&sm.g.x.graw[t][2 * lane]) = Gu[u];
     }
   }
   if (pw == 0)
@@ -382,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
   const int t16 = tid >> 4;  // (t, s) of threads 0..255
   const int s16 = tid & 15;
   if (!unsafe) {
-    const float(*src)[kLd] = pw < 2 ? sm.kt : sm.qt;
+    const float(*src)[kLd] = pw < 2 ? sm.g.f.kt : sm.g.f.qt;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -404,9 +412,9 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_prep_kernel(
     if (s16 <= t16) {
       for (int i = 0; i < kD; ++i) {
         const float ks =
-            sm.ki[s16][i] * exp2_(sm.graw[t16][i] - sm.graw[s16][i]);
+            sm.ki[s16][i] * exp2_(sm.g.x.graw[t16][i] - sm.g.x.graw[s16][i]);
         a += sm.ki[t16][i] * ks;
-        b += sm.qraw[t16][i] * ks;
+        b += sm.g.x.qraw[t16][i] * ks;
       }
     }
     sm.LT[s16][t16] = s16 < t16 ? sm.beta[t16] * a : 0.0f;
