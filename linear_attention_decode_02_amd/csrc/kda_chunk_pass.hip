@@ -185,7 +185,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     KdaPassArgs p) {
   __shared__ alignas(16) PrepSmem sm;
   const int tid = threadIdx.x;
-  const int pw = tid >> 6;  // this wave's tokens: 4pw .. 4pw+3
+  // this wave's tokens: 4pw .. 4pw+3 (scalar: wave-uniform offsets stay on
+  // the scalar unit)
+  const int pw = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(64 * kStateWaves) void kda_chunk_state_kernel(
     KdaPassArgs p) {
   __shared__ alignas(16) float rec[kBufs][kRecStaged];  // records in flight
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
   const int lane = tid & 63;
   const int c = lane & 15;
   const int gq = lane >> 4;

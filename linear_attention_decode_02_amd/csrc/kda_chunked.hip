@@ -208,7 +208,9 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   constexpr bool kRaw = kGate != kGateInput;
   __shared__ Smem sm;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index in a scalar register: role tests and role-derived offsets
+  // stay on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c = lane & 15;   // MFMA column / A-operand row
   const int gq = lane >> 4;  // MFMA row group

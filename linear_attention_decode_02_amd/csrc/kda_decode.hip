@@ -529,7 +529,7 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
   __shared__ uint32_t s_win[3][3][kD / 2];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
   const int lane = tid & 63;
   const int unit = blockIdx.x;
   const int H = p.heads;
