@@ -370,3 +370,14 @@ def test_chunked_graph_replay_matches_eager(path):
         assert torch.equal(tg["rec_state"].view(torch.int32),
                            te["rec_state"].view(torch.int32)), r
         print(f"[chunked graph {path}] replay {r} matches eager", flush=True)
+
+
+def test_chunked_prefill_max_heads_long_sequence(path):
+    """96 heads (the largest head count) with a 4096-token sequence (256
+    chunks) beside short ones, q/k L2-normalised, fresh states: every
+    output and state element against the oracle, through both paths."""
+    lens = [4096, 3, 700, 0]
+    w, inp, cu = prefill_case(270, lens, 96, zero_state=True,
+                              conv_w_sigma=0.5, null=(3,))
+    run_and_check(w, inp, cu, 96, flags=O.QK_L2NORM, label="H96 4096",
+                  path=path)

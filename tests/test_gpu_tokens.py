@@ -232,3 +232,19 @@ def test_tokens_argument_checks():
     assert L.kda_decode_tokens(ctypes.byref(d), 1025, *ptrs, s) == 1
     d.flags = 0x21
     assert L.kda_decode_tokens(ctypes.byref(d), 2, *ptrs, s) == 1
+
+
+def test_tokens_maximum_T():
+    """T = 1024, the largest count the entry point accepts (64 chunks of
+    the matrix-core form), on a small batch with a null row, against 1024
+    oracle steps.  q/k L2-normalised, so the long chain stays contractive
+    and the single-step bars apply."""
+    T = 1024
+    w = synth.small("tmax", batch=3, heads=12, num_slots=6, seed=180,
+                    null_every=3, conv_w_sigma=0.5)
+    inp = synth.make_tokens(w, T)
+    ref = O.decode_tokens(inp, heads=w.heads, tokens=T, norm=True, eps=w.eps,
+                          flags=O.QK_L2NORM)
+    got = run_tokens(w, inp, T, variants=O.QK_L2NORM)
+    st = check_tokens(w, inp, got, ref, T)
+    print(f"[tokens T=1024] {st}", flush=True)
