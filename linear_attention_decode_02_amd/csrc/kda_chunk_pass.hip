@@ -27,8 +27,9 @@
 // block in MFMA accumulator registers through the sequence's chunks: K~S and
 // Q~S, the deltas T beta (V - K~S), the outputs Q~S + B Delta (into the
 // record's output rows, before the norm) and the state update
-// e^{G_last} S + K^^T Delta.  The next chunk's record streams into LDS
-// (global_load_lds) while the current one is processed.  Eight waves in one
+// e^{G_last} S + K^^T Delta.  The next chunks' records stream into LDS
+// (global_load_lds, kBufs records in flight) while the current one is
+// processed.  Eight waves in one
 // workgroup (two per SIMD) measured fastest: one wave per SIMD issues at
 // most one fp32 MFMA per 32 cycles, two waves share a SIMD at one per 24, so
 // splitting a (sequence, head) over more compute units with fewer waves each
