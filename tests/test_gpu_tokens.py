@@ -105,6 +105,36 @@ def test_tokens_match_successive_single_calls(T):
                        inp["state_idx"], w.num_slots, w.heads)
 
 
+
+def test_tokens_decay_extremes():
+    """Decays across the whole range within one multi-token call: per
+    element -1e-4 (10 %), -8 (20 %), -30 (5 %), -100 (5 %, exp underflows
+    to zero or a subnormal) or -softplus(N(0,1)).  Over 12 tokens a key row
+    keeps nearly all of its state or forgets it entirely; the result must
+    equal the oracle and T single-token calls."""
+    T = 12
+    w = synth.small("tdecay", batch=9, heads=24, num_slots=14, seed=77,
+                    null_every=4, conv_w_sigma=0.05)
+    inp = synth.make_tokens(w, T)
+    rng = np.random.default_rng(78)
+    u = rng.random(inp["g"].shape)
+    g = inp["g"].copy()
+    g[u < 0.4] = -100.0
+    g[u < 0.35] = -30.0
+    g[u < 0.30] = -8.0
+    g[u < 0.10] = -1e-4
+    inp["g"] = np.ascontiguousarray(g.astype(np.float32))
+    ref = O.decode_tokens(inp, heads=w.heads, tokens=T, norm=True, eps=w.eps)
+    got = run_tokens(w, inp, T)
+    st = check_tokens(w, inp, got, ref, T)
+    single = run_single_calls(w, inp, T)
+    assert np.array_equal(got["conv_state"], single["conv_state"])
+    d_rs = np.abs(got["rec_state"] - single["rec_state"]).max()
+    print(f"[tokens decay] {st} vs single calls: state maxdiff {d_rs:.3g}",
+          flush=True)
+    assert d_rs <= 1e-5
+
+
 CASES = [
     ("plain", 0, True), ("nonorm", 0, False),
     ("tap_major", O.CONV_TAP_MAJOR, True),
