@@ -487,32 +487,64 @@ void kda_decode_kernel(Params p) {
 //
 // Two barriers per token, software-pipelined one token deep: waves 4..7
 // compute token t+1's inputs (conv + SiLU of q, k, v; exp(g)) while waves
-// 0..3 finish token t's column sums, so the token chain holds only
-//   decay + partial sums | barrier | column sums (and next inputs) |
-//   barrier | rank-1 update + output.
+// 0..3 finish token t's column sums, wave 9 its q.k, and wave 8 emits token
+// t-1's output (readout + gated RMSNorm), so the token chain holds only
+//   decay + partial sums | barrier | column sums (next inputs, previous
+//   output) | barrier | rank-1 update.
 // Each input wave fetches its next token's small inputs one token ahead.
 
-// finish_columns with the token's v row taken from `v` (double-buffered by
-// token parity: the next token's v is written while this one is read).
-__device__ __forceinline__ void finish_columns_v(Lds& L, int tid, float beta,
-                                                 const float* v) {
-  if (tid < 2 * kD) {
-    const int which = tid / kD;
-    const int j = tid % kD;
-    float acc = L.red[0][which][j];
+// finish_columns with the token's v row taken from `v` and delta and p
+// written to dp[0] and dp[1] (double-buffered by token parity: the next
+// token's are written while this one's are read).  Two interleaved
+// accumulators halve the dependent-add chain.
+__device__ __forceinline__ void finish_columns_v(const Lds& L, int tid,
+                                                 float beta, const float* v,
+                                                 float (*dp)[kD]) {
+  const int which = tid / kD;
+  const int j = tid % kD;
+  float a0 = L.red[0][which][j], a1 = L.red[1][which][j];
 #pragma unroll
-    for (int r = 1; r < 2 * kWaves; ++r) acc += L.red[r][which][j];
-    if (which == 0)
-      L.delta[j] = beta * (v[j] - acc);
-    else
-      L.p[j] = acc;
-    if (tid == 0) {
-      float t = L.qk[0];
-#pragma unroll
-      for (int r = 1; r < 2 * kWaves; ++r) t += L.qk[r];
-      L.qk_total = t;
-    }
+  for (int r = 2; r < 2 * kWaves; r += 2) {
+    a0 += L.red[r][which][j];
+    a1 += L.red[r + 1][which][j];
   }
+  const float acc = a0 + a1;
+  dp[which][j] = which == 0 ? beta * (v[j] - acc) : acc;
+}
+
+// q.k of one token from the 32 half-wave partials, by one whole wave
+// (lanes 0..31 read one partial each; DPP row sums, then two lane reads).
+__device__ __forceinline__ void finish_qk(const Lds& L, int lane, float* qk) {
+  const float rows = sum16(lane < 2 * kWaves ? L.qk[lane] : 0.0f);
+  const float t = lane_value(rows, 0) + lane_value(rows, 16);
+  if (lane == 0) *qk = t;
+}
+
+// Readout and gated RMSNorm of one finished token from its delta, p and q.k
+// rows, by 32 lanes of one wave (four columns each; lanes 32..63 idle).
+template <bool kNorm>
+__device__ __forceinline__ void emit_token_output(
+    const float (*dp)[kD], float qk_total, const float* norm_w,
+    uint32_t flags, float eps, int col4, u2 gb, gptr<uint16_t> out4) {
+  const f4 delta = *reinterpret_cast<const f4*>(&dp[0][4 * col4]);
+  const f4 o = *reinterpret_cast<const f4*>(&dp[1][4 * col4]) +
+               qk_total * delta;
+  f4 y = o;
+  if (kNorm) {
+    const float rows = sum16(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
+    const float ss = lane_value(rows, 0) + lane_value(rows, 16);
+    const float r = rsqrtf(ss * (1.0f / kD) + eps);
+    const f4 w = *reinterpret_cast<const f4*>(norm_w + 4 * col4);
+    const f4 gv = {bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
+    f4 ga = {sigmoidf_(gv.x), sigmoidf_(gv.y), sigmoidf_(gv.z),
+             sigmoidf_(gv.w)};
+    if (flags & KDA_GATE_SILU) ga *= gv;
+    y = o * r * w * ga;
+  }
+  u2 ob;
+  ob.x = pack_bf16x2(y.x, y.y);
+  ob.y = pack_bf16x2(y.z, y.w);
+  *reinterpret_cast<gptr<u2>>(out4) = ob;
 }
 
 template <bool kNorm>
@@ -525,6 +557,10 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
   // written while token t's are read
   __shared__ f4 s_akq[2][kD];
   __shared__ float s_v[2][kD];
+  // finished delta and p rows and q.k by token parity: token t-1's are
+  // read by the output wave while token t's are written
+  __shared__ float s_dp[2][2][kD];
+  __shared__ float s_qk[2];
   // conv window words of input waves 4..6, kept in LDS across the tokens
   __shared__ uint32_t s_win[3][3][kD / 2];
 
@@ -580,10 +616,11 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
     g2 = *at_bytes<const f2>(uniform_gptr(g_row), 4 * gi);
   }
   float beta = beta_row[h];  // of the token waves 0..3 finish next
-  // output gate words of lanes 0..31 (wave 0 loads them; lanes 32..63
-  // mirror 0..31)
+  // output gate words of lanes 0..31 of the output wave (wave 8, which
+  // emits token t-1 while token t's column sums are finished)
+  constexpr int kOutWave = 8;
   u2 gate_w = {0u, 0u};
-  if (kNorm && wave == 0)
+  if (kNorm && wave == kOutWave)
     gate_w = *at_bytes<const u2>(uniform_gptr(p.gate + row_tok * C), 2 * oc);
   uint32_t* cs_slot = reinterpret_cast<uint32_t*>(
       p.conv_state + static_cast<int64_t>(slot) * 3 * C * (kW - 1));
@@ -686,26 +723,38 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
                              akq_t);
     __syncthreads();
     if (wave_t < 4) {
-      finish_columns_v(L, tid_t, beta, s_v[t & 1]);
+      finish_columns_v(L, tid_t, beta, s_v[t & 1], s_dp[t & 1]);
       const int tn = t + 1 < T ? t + 1 : t;
       beta = beta_row[static_cast<int64_t>(tn) * H + h];
-    } else if (wave_t < 8 && t + 1 < T) {
-      inputs(t + 1, t + 2 < T ? t + 2 : t + 1);
+    } else if (wave_t < 8) {
+      if (t + 1 < T) inputs(t + 1, t + 2 < T ? t + 2 : t + 1);
+    } else if (wave_t == kOutWave + 1) {
+      finish_qk(L, lane_t, &s_qk[t & 1]);
+    } else if (wave_t == kOutWave && t > 0) {
+      // output of the previous token, off the token chain
+      if (lane_t < 32)
+        emit_token_output<kNorm>(
+            s_dp[(t - 1) & 1], s_qk[(t - 1) & 1], s_norm_w, flags, p.eps,
+            col4_t, gate_w,
+            at_bytes<uint16_t>(uniform_gptr(p.out + (row_tok + t - 1) * C),
+                               2 * oc_t));
+      if (kNorm)
+        gate_w = *at_bytes<const u2>(
+            uniform_gptr(p.gate + (row_tok + t) * C), 2 * oc_t);
     }
     __syncthreads();
-    const f4 delta = *reinterpret_cast<const f4*>(&L.delta[4 * col4_t]);
+    const f4 delta = *reinterpret_cast<const f4*>(&s_dp[t & 1][0][4 * col4_t]);
 #pragma unroll
     for (int m = 0; m < kRowsPerThread; ++m)
       s[m] += akq_t[rgrp_t + kRowStride * m].y * delta;
-    if (tid_t < 32) {
-      emit_output<kNorm>(L, s_norm_w, flags, p.eps, col4_t, delta, gate_w,
-                         at_bytes<uint16_t>(
-                             uniform_gptr(p.out + (row_tok + t) * C), 2 * oc_t));
-    }
-    if (kNorm && wave_t == 0 && t + 1 < T)
-      gate_w = *at_bytes<const u2>(
-          uniform_gptr(p.gate + (row_tok + t + 1) * C), 2 * oc_t);
   }
+  // output of the last token (its rows are final after the last barrier)
+  if (wave == kOutWave && lane < 32)
+    emit_token_output<kNorm>(
+        s_dp[(T - 1) & 1], s_qk[(T - 1) & 1], s_norm_w, flags, p.eps,
+        lane, gate_w,
+        at_bytes<uint16_t>(uniform_gptr(p.out + (row_tok + T - 1) * C),
+                           2 * (h * kD + 4 * lane)));
 
   // ---- write back: state tile once, conv window once ----------------------
 #pragma unroll
