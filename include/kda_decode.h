@@ -169,7 +169,7 @@ kda_status kda_decode_raw_gates(const kda_dims* dims, const void* qkv,
  * Other buffers, flags (KDA_BOUNDED_GATE excluded), rules and status codes
  * as kda_decode; T outside 1..1024 is KDA_ERR_INVALID_ARG.  With
  * KDA_NO_CONV_UPDATE every token sees the stored conv window, as T
- * successive calls with that flag would.  From T = 24 on, the call runs
+ * successive calls with that flag would.  From T = 29 on, the call runs
  * the chunked matrix-core form of kda_prefill_chunked (each row one
  * sequence of T tokens): equal up to rounding, and faster there; g must
  * then be finite.
