@@ -97,6 +97,9 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="measure the variable-length prefill instead "
                          "(16 sequences, 48 heads, L2-normalised q/k)")
+    ap.add_argument("--serving", action="store_true",
+                    help="per-call latency of kda_decode at serving batch "
+                         "sizes (1..256 rows, 12 and 48 heads, graph replay)")
     ap.add_argument("--tokens", type=int, default=1,
                     help="decode tokens per row and call (> 1: the "
                          "multi-token entry point, state kept on chip)")
@@ -124,6 +127,8 @@ def main():
 
     if args.prefill:
         return bench_prefill(args, np, torch, kda, synth)
+    if args.serving:
+        return bench_serving(args, np, torch, kda, synth)
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -302,6 +307,76 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_serving(args, np, torch, kda, synth, copies=8, calls=64):
+    """Per-call latency of kda_decode at the batch sizes of serving: 1..256
+    rows at 12 heads (the TP8 share of 96) and 48 heads, norm on, every row
+    live.  Each point is a graph of ``calls`` calls rotating ``copies``
+    copies of the state pools (no reuse through the last-level cache),
+    replayed 5 times; the median replay divided by ``calls``."""
+    dev = torch.device("cuda:0")
+    points = []
+    for H in (12, 48):
+        for B in (1, 8, 16, 24, 32, 64, 128, 256):
+            w = synth.small(f"serving_b{B}_h{H}", batch=B, heads=H,
+                            num_slots=B + 1, seed=5)
+            t = synth.to_torch(synth.make_inputs(w), dev)
+            out = torch.empty(B, w.channels, dtype=torch.bfloat16,
+                              device=dev)
+            pools = [(t["conv_state"].clone(), t["rec_state"].clone())
+                     for _ in range(copies)]
+
+            def call(i):
+                cs, rs = pools[i % copies]
+                kda.kda_decode(t["qkv"], t["conv_w"], cs, rs, t["g"],
+                               t["beta"], t["gate"], t["norm_w"],
+                               t["state_idx"], out, norm=True, eps=w.eps)
+
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                for i in range(copies):
+                    call(i)
+            torch.cuda.current_stream(dev).wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(calls):
+                    call(i)
+            g.replay()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / calls)
+            us = float(np.median(ts))
+            nbytes = kda.decode_bytes(B, H, B, True)
+            points.append({"batch": B, "heads": H, "us_per_call": round(us, 2),
+                           "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+            print(f"[serving] H={H} B={B}: {us:.2f} us", file=sys.stderr,
+                  flush=True)
+            del g, pools, t
+    c16 = next(p for p in points if p["batch"] == 16 and p["heads"] == 12)
+    line = {
+        "metric": "KDA decode latency per call at serving batch sizes",
+        "value": c16["us_per_call"], "unit": "us", "n_gpus": 1,
+        "steps": calls, "warmup": copies, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "serving_b16_h12 (value); sweep in extra",
+                   "head_dim": 128, "conv_width": 4, "output_norm": True,
+                   "parallelism": "single-gpu"},
+        "roofline": None, "cpu_baseline": None,
+        "extra": {"points": points, "pool_copies": copies,
+                  "calls_per_graph": calls},
     }
     print(json.dumps(line), flush=True)
 
