@@ -10,8 +10,6 @@ import subprocess
 import sys
 import tempfile
 
-import pytest
-
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kda_oracle.cpp")
 
