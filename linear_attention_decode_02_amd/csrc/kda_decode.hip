@@ -707,8 +707,9 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
 
   for (int t = 0; t < T; ++t) {
     // Lane-derived offsets are recomputed every token from an opaque copy
-    // of the thread id: cheaper than keeping a dozen of them live across
-    // the loop (they would not fit the 64-VGPR budget otherwise).
+    // of the thread id (a dozen of them kept live across the loop would
+    // not fit the 64-VGPR budget); the state rows' key-row group and column
+    // block stay live (rgrp, col4: measured ~1 % faster than recomputing).
     int tid_t = tid;
     asm volatile("" : "+v"(tid_t));
     const int wave_t = tid_t >> 6;
@@ -719,8 +720,7 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
 
     const f4* akq_t = s_akq[t & 1];
     float k_unused[kRowsPerThread];
-    decay_and_partials<true>(L, s, k_unused, rgrp_t, wave_t, lane_t, col4_t,
-                             akq_t);
+    decay_and_partials<true>(L, s, k_unused, rgrp, wave, lane, col4, akq_t);
     __syncthreads();
     if (wave_t < 4) {
       finish_columns_v(L, tid_t, beta, s_v[t & 1], s_dp[t & 1]);
@@ -743,10 +743,10 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
             uniform_gptr(p.gate + (row_tok + t) * C), 2 * oc_t);
     }
     __syncthreads();
-    const f4 delta = *reinterpret_cast<const f4*>(&s_dp[t & 1][0][4 * col4_t]);
+    const f4 delta = *reinterpret_cast<const f4*>(&s_dp[t & 1][0][4 * col4]);
 #pragma unroll
     for (int m = 0; m < kRowsPerThread; ++m)
-      s[m] += akq_t[rgrp_t + kRowStride * m].y * delta;
+      s[m] += akq_t[rgrp + kRowStride * m].y * delta;
   }
   // output of the last token (its rows are final after the last barrier)
   if (wave == kOutWave && lane < 32)
