@@ -715,7 +715,6 @@ void kda_decode_tokens_kernel(Params p, int T_fixed) {
     const int wave_t = tid_t >> 6;
     const int lane_t = tid_t & 63;
     const int col4_t = tid_t & 31;
-    const int rgrp_t = tid_t >> 5;
     const uint32_t oc_t = h * kD + 4 * col4_t;
 
     const f4* akq_t = s_akq[t & 1];
