@@ -43,3 +43,20 @@ def test_recorded_traffic_matches_this_kernel():
     t = bench.recorded_traffic("b256_h48_pool512_null32")
     assert t is not None and abs(t / 1478831616 - 1) < 0.01
     assert bench.recorded_traffic("b64_h24_pool128") is None
+
+
+def test_cpu_baseline_reports_threads_model_and_single_thread_rate():
+    """The oracle baseline object carries the fields the bench line states:
+    rate, unit, the threads used, kind, the sample, and a one-thread rate."""
+    from linear_attention_decode_02_amd import synth
+
+    w = synth.small("cpu_fields", batch=3, heads=12, num_slots=6, seed=1,
+                    null_every=3)
+    inp = synth.make_inputs(w)
+    units = w.units(inp["state_idx"])
+    r = bench.cpu_baseline(w, inp, 0.2, 1000, units)
+    assert r["kind"] == "oracle" and r["unit"] == "updates/s"
+    assert r["value"] > 0 and 1 <= r["cores"] <= 16
+    assert f"({units} updates)" in r["sample"]
+    st = r["single_thread"]
+    assert st["value"] > 0 and st["calls"] >= 1
