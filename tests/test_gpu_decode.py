@@ -336,3 +336,54 @@ def test_state_stream_probe_modes(waves):
     kda.state_stream_probe(y, waves, scale=3.0, mode=kda.PROBE_WRITE)
     torch.cuda.synchronize()
     assert torch.all(y == 3.0)
+
+
+def _bf16_bits(x: float) -> int:
+    """bf16 bit pattern of a value that bf16 holds exactly."""
+    return int(np.array([x], dtype=np.float32).view(np.uint32)[0] >> 16)
+
+
+DEGENERATE = ["no_update_no_decay", "zero_inputs", "zero_key",
+              "decay_underflow", "zero_state", "gate_saturated"]
+
+
+@pytest.mark.parametrize("case", DEGENERATE)
+def test_degenerate_inputs(case):
+    """Degenerate cases of the step, against the oracle, with exact checks
+    where the method fixes the result exactly:
+    - g = 0 and beta = 0: every touched state comes back bit-identical;
+    - all inputs and conv states zero: q = k = v = 0, every live output is
+      +-0 (the RMS of a zero vector is 0: the norm's bar is exact);
+    - zero keys: no update along any key, S' = diag(exp g) S;
+    - g = -100: exp underflows, the old state is forgotten;
+    - zero state: S' = beta k v^T;
+    - output gates at +-30: sigmoid saturates at 1 and ~1e-13."""
+    C = 12 * 128
+    w = synth.small(f"degen_{case}", batch=8, heads=12, num_slots=12,
+                    seed=90 + DEGENERATE.index(case), null_every=4)
+    inp = synth.make_inputs(w)
+    if case == "no_update_no_decay":
+        inp["g"][:] = 0.0
+        inp["beta"][:] = 0.0
+    elif case == "zero_inputs":
+        inp["qkv"][:] = 0
+        inp["conv_state"][:] = 0
+    elif case == "zero_key":
+        inp["qkv"][:, C:2 * C] = 0
+        inp["conv_state"][:, C:2 * C, :] = 0
+    elif case == "decay_underflow":
+        inp["g"][:] = -100.0
+    elif case == "zero_state":
+        inp["rec_state"][:] = 0.0
+    elif case == "gate_saturated":
+        inp["gate"][:, 0::2] = _bf16_bits(30.0)
+        inp["gate"][:, 1::2] = _bf16_bits(-30.0)
+    got, ref = parity(w, inp, label=f"degenerate {case}")
+    live = inp["state_idx"][(inp["state_idx"] > 0)
+                            & (inp["state_idx"] < w.num_slots)]
+    if case == "no_update_no_decay":
+        assert np.array_equal(got["rec_state"][live].view(np.uint32),
+                              inp["rec_state"][live].view(np.uint32))
+    if case == "zero_inputs":
+        y = P.bf16_to_f32(got["out"])
+        assert np.all(y == 0.0)
