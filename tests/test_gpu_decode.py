@@ -387,3 +387,37 @@ def test_degenerate_inputs(case):
     if case == "zero_inputs":
         y = P.bf16_to_f32(got["out"])
         assert np.all(y == 0.0)
+
+
+def test_nan_stays_in_its_unit():
+    """A NaN decay input reaches one (row, head): it propagates through that
+    unit's column sums into its whole state tile and its outputs, as in the
+    oracle, and changes nothing in any other unit or slot."""
+    w = synth.small("nan_unit", batch=6, heads=12, num_slots=10, seed=97,
+                    null_every=5)
+    inp = synth.make_inputs(w)
+    r, h = 2, 3
+    assert inp["state_idx"][r] > 0
+    inp["g"][r, h, 5] = np.nan
+    got = P.run_gpu(w, inp, DEV)
+    ref = P.run_oracle(w, inp)
+    s = inp["state_idx"][r]
+    for res in (got, ref):
+        assert np.all(np.isnan(res["rec_state"][s, h]))
+    assert np.all(np.isnan(P.bf16_to_f32(got["out"]).reshape(
+        w.batch, w.heads, -1)[r, h]))
+    assert np.all(np.isnan(np.asarray(ref["y"]).reshape(
+        w.batch, w.heads, -1)[r, h]))
+    # everything else: the usual bars, with the NaN unit set aside
+    got_rs, ref_rs = got["rec_state"].copy(), ref["rec_state"].copy()
+    got_rs[s, h] = inp["rec_state"][s, h]
+    ref_rs[s, h] = inp["rec_state"][s, h]
+    P.check_states(got["conv_state"], got_rs, ref["conv_state"], ref_rs,
+                   inp["conv_state"], inp["rec_state"], inp["state_idx"],
+                   w.num_slots)
+    out = got["out"].reshape(w.batch, w.heads, -1).copy()
+    y = np.asarray(ref["y"], np.float32).reshape(w.batch, w.heads, -1).copy()
+    out[r, h] = 0
+    y[r, h] = 0.0
+    P.check_output(out.reshape(w.batch, -1), y.reshape(w.batch, -1),
+                   inp["state_idx"], w.num_slots, w.heads)
