@@ -421,3 +421,73 @@ def test_nan_stays_in_its_unit():
     y[r, h] = 0.0
     P.check_output(out.reshape(w.batch, -1), y.reshape(w.batch, -1),
                    inp["state_idx"], w.num_slots, w.heads)
+
+
+@pytest.mark.parametrize("T", [1, 3, 30])
+def test_pool_beyond_4gib_with_rows_in_its_last_slots(T):
+    """64-bit state addressing: a 1,100-slot, 96-head pool (6.9 GB of
+    recurrent state) whose live rows sit in its last 64 slots, at byte
+    offsets past 6.3 GB, through the single-token kernel (T = 1), the
+    token-by-token multi-token kernel (T = 3) and the chunked form (T = 30,
+    q/k L2-normalised as in every long chain).  The rows' inputs and the
+    touched slots' contents come from a seeded 65-slot problem that the
+    oracle solves; every other slot of the large pool is filled on the GPU
+    and must come back unchanged."""
+    import oracle as O
+
+    H, S_big = 96, 1100
+    small = synth.small("pool_4g_rows", batch=64, heads=H, num_slots=65,
+                        seed=99, null_every=9)
+    flags = O.QK_L2NORM if T >= 29 else 0
+    if T == 1:
+        inp = synth.make_inputs(small)
+        ref = P.run_oracle(small, inp)
+    else:
+        inp = synth.make_tokens(small, T)
+        ref = O.decode_tokens(inp, heads=H, tokens=T, norm=True,
+                              eps=small.eps, flags=flags)
+    t = synth.to_torch(inp, DEV)
+    base = S_big - small.num_slots          # small slot s -> base + s
+    gen = torch.Generator(device=DEV).manual_seed(99)
+    rs_big = torch.randn((S_big, H, 128, 128), generator=gen, device=DEV)
+    cs_big = torch.randint(-30000, 30000, (S_big, 3 * H * 128, 3),
+                           generator=gen, device=DEV,
+                           dtype=torch.int16).view(torch.bfloat16)
+    rs_big[base:] = t["rec_state"]
+    cs_big[base:] = t["conv_state"]
+    rs_before = rs_big[:base].clone()
+    cs_before = cs_big[:base].clone()
+    idx = inp["state_idx"]
+    live = (idx > 0) & (idx < small.num_slots)
+    big_idx = torch.from_numpy(np.where(live, idx + base, 0).astype(
+        np.int32)).to(DEV)
+    assert (S_big - 1) * H * 128 * 128 * 4 > 6.3e9
+    shape = (small.batch, small.channels) if T == 1 else \
+        (small.batch, T, small.channels)
+    out = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    if T == 1:
+        kda.kda_decode(t["qkv"], t["conv_w"], cs_big, rs_big, t["g"],
+                       t["beta"], t["gate"], t["norm_w"], big_idx, out,
+                       norm=True, eps=small.eps)
+    else:
+        kda.kda_decode_tokens(t["qkv"], t["conv_w"], cs_big, rs_big, t["g"],
+                              t["beta"], t["gate"], t["norm_w"], big_idx, out,
+                              norm=True, eps=small.eps, variants=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(rs_big[:base].view(torch.int32),
+                       rs_before.view(torch.int32)), \
+        "a slot no row names changed"
+    assert torch.equal(cs_big[:base].view(torch.int16),
+                       cs_before.view(torch.int16))
+    del rs_before, cs_before
+    got_rs = rs_big[base:].cpu().numpy()
+    got_cs = synth.bf16_bits(cs_big[base:])
+    st = P.check_states(got_cs, got_rs, ref["conv_state"], ref["rec_state"],
+                        inp["conv_state"], inp["rec_state"], idx,
+                        small.num_slots, scaled=T > 1)
+    out_bits = synth.bf16_bits(out)
+    for tok in range(T):
+        o = out_bits if T == 1 else out_bits[:, tok]
+        y = ref["y"] if T == 1 else ref["y"][:, tok]
+        st.update(P.check_output(o, y, idx, small.num_slots, H))
+    print(f"[pool > 4 GiB, T={T}] {st}", flush=True)
