@@ -381,3 +381,17 @@ def test_chunked_prefill_max_heads_long_sequence(path):
                               conv_w_sigma=0.5, null=(3,))
     run_and_check(w, inp, cu, 96, flags=O.QK_L2NORM, label="H96 4096",
                   path=path)
+
+
+def test_two_pass_workspace_beyond_4gib():
+    """64-bit record addressing in the two-pass prefill: a 16,400-token
+    sequence at 96 heads (1,026 chunks with the short one) needs a 4.44 GB
+    workspace, so its last records lie past 4 GiB.  q/k L2-normalised,
+    fresh states; every output and state element against the oracle."""
+    lens = [16400, 5, 0]
+    w, inp, cu = prefill_case(290, lens, 96, zero_state=True,
+                              conv_w_sigma=0.5, null=(2,))
+    chunks = sum(-(-n // kda.PREFILL_CHUNK) for n in lens)
+    assert kda.prefill_chunks_workspace_bytes(96, chunks) > 4 * 2 ** 30
+    run_and_check(w, inp, cu, 96, flags=O.QK_L2NORM, label="H96 16400",
+                  path="two_pass")
