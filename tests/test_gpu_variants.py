@@ -173,3 +173,35 @@ def test_b256_h48_full_size_kda_configuration():
     got, _ = run_gpu(w, inp, O.QK_L2NORM, raw=True, lower_bound=-5.0)
     st = check(w, inp, got, ref, inp["conv_state"], inp["rec_state"], 0)
     print(f"[b256 kda config] {st}", flush=True)
+
+
+@pytest.mark.parametrize("bounded", [False, True], ids=["softplus", "bounded"])
+def test_raw_gates_across_their_regimes(bounded):
+    """Raw gates spread over [-40, 40] so that every branch of the gate
+    activation is taken: softplus in its linear range (z > 20, decays down
+    to exp(-a z) ~ 0), its exponential tail (z < -17, decay ~ 1) and in
+    between; the bounded form saturating at its lower bound and at 0;
+    sigmoid(raw_beta) saturating at 0 and 1.  A_log per head in {-2, 0, 1}
+    (rates e^-2, 1, e), no dt bias."""
+    H, B = 24, 9
+    rng = np.random.default_rng(123 + bounded)
+    w = synth.small(f"raw_regimes_{int(bounded)}", batch=B, heads=H,
+                    num_slots=B + 3, seed=124, null_every=4)
+    inp = synth.make_inputs(w)
+    D = w.head_dim
+    inp.update(
+        raw_g=synth.to_bf16_bits(
+            rng.uniform(-40, 40, (B, H, D)).astype(np.float32)),
+        raw_beta=synth.to_bf16_bits(
+            rng.uniform(-30, 30, (B, H)).astype(np.float32)),
+        A_log=np.array([-2.0, 0.0, 1.0] * (H // 3), np.float32),
+        dt_bias=np.zeros(H * D, np.float32))
+    flags = O.BOUNDED_GATE if bounded else 0
+    lb = -5.0 if bounded else None
+    inp["lower_bound"] = lb if bounded else 0.0
+    print(f"[raw regimes] bounded={bounded}", flush=True)
+    ref = O.decode(inp, heads=H, norm=True, eps=w.eps, dtype="f32",
+                   flags=flags)
+    got, _ = run_gpu(w, inp, 0, raw=True, lower_bound=lb)
+    st = check(w, inp, got, ref, inp["conv_state"], inp["rec_state"], flags)
+    print(f"[raw regimes] bounded={bounded}: {st}", flush=True)
