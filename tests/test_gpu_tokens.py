@@ -279,3 +279,50 @@ def test_tokens_maximum_T():
     got = run_tokens(w, inp, T, variants=O.QK_L2NORM)
     st = check_tokens(w, inp, got, ref, T)
     print(f"[tokens T=1024] {st}", flush=True)
+
+
+@pytest.mark.parametrize("T", [4, 30])
+def test_tokens_graph_replay_matches_eager(T):
+    """kda_decode_tokens captured in a HIP graph (T = 4 token by token,
+    T = 30 the chunked form) and replayed three times with eager work and
+    synchronisation in between: each replay equals the same eager call bit
+    for bit (pools updated in place, so every replay advances the state)."""
+    w = synth.small(f"tgraph{T}", batch=10, heads=24, num_slots=16,
+                    seed=190 + T, null_every=4, conv_w_sigma=0.05)
+    inp = synth.make_tokens(w, T)
+    flags = O.QK_L2NORM if T >= 29 else 0
+    te = synth.to_torch(inp, DEV)        # eager copy
+    tg = synth.to_torch(inp, DEV)        # graph copy
+    out_e = torch.empty(w.batch, T, w.channels, dtype=torch.bfloat16,
+                        device=DEV)
+    out_g = torch.empty_like(out_e)
+
+    def call(t, out):
+        kda.kda_decode_tokens(t["qkv"], t["conv_w"], t["conv_state"],
+                              t["rec_state"], t["g"], t["beta"], t["gate"],
+                              t["norm_w"], t["state_idx"], out, norm=True,
+                              eps=w.eps, variants=flags)
+
+    warm = synth.to_torch(inp, DEV)
+    call(warm, torch.empty_like(out_e))   # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cs0, rs0 = tg["conv_state"].clone(), tg["rec_state"].clone()
+    with torch.cuda.graph(graph):
+        call(tg, out_g)
+    tg["conv_state"].copy_(cs0)
+    tg["rec_state"].copy_(rs0)
+    torch.cuda.synchronize()
+    for r in range(3):
+        call(te, out_e)
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 20, device=DEV).sum()   # eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert scratch.isfinite()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), r
+        assert torch.equal(tg["conv_state"].view(torch.int16),
+                           te["conv_state"].view(torch.int16)), r
+        assert torch.equal(tg["rec_state"].view(torch.int32),
+                           te["rec_state"].view(torch.int32)), r
+        print(f"[tokens graph T={T}] replay {r} matches eager", flush=True)
