@@ -491,3 +491,62 @@ def test_pool_beyond_4gib_with_rows_in_its_last_slots(T):
         y = ref["y"] if T == 1 else ref["y"][:, tok]
         st.update(P.check_output(o, y, idx, small.num_slots, H))
     print(f"[pool > 4 GiB, T={T}] {st}", flush=True)
+
+
+def test_concurrent_threads_and_streams_match_serial_calls():
+    """Four host threads, each on its own stream (default priority) with its
+    own pools, issue five decode calls each at the same time; the library
+    keeps no per-call state, so every thread's pools and last output equal
+    the same five calls run one after another, bit for bit."""
+    import threading
+
+    w = synth.small("threads", batch=16, heads=24, num_slots=24, seed=57,
+                    null_every=5)
+    inputs = [synth.make_inputs(dataclasses.replace(w, seed=57 + i))
+              for i in range(4)]
+
+    def five_calls(t, out, stream=None):
+        for _ in range(5):
+            kda.kda_decode(t["qkv"], t["conv_w"], t["conv_state"],
+                           t["rec_state"], t["g"], t["beta"], t["gate"],
+                           t["norm_w"], t["state_idx"], out, norm=True,
+                           eps=w.eps, stream=stream)
+
+    serial = []
+    for inp in inputs:
+        t = synth.to_torch(inp, DEV)
+        out = torch.empty(w.batch, w.channels, dtype=torch.bfloat16,
+                          device=DEV)
+        five_calls(t, out)
+        torch.cuda.synchronize()
+        serial.append((t, out))
+
+    par = [(synth.to_torch(inp, DEV),
+            torch.empty(w.batch, w.channels, dtype=torch.bfloat16,
+                        device=DEV)) for inp in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(DEV) for _ in inputs]
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                five_calls(par[i][0], par[i][1], stream=streams[i])
+            streams[i].synchronize()
+        except Exception as e:           # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, ((ts, os_), (tp, op)) in enumerate(zip(serial, par)):
+        assert torch.equal(op.view(torch.int16), os_.view(torch.int16)), i
+        assert torch.equal(tp["rec_state"].view(torch.int32),
+                           ts["rec_state"].view(torch.int32)), i
+        assert torch.equal(tp["conv_state"].view(torch.int16),
+                           ts["conv_state"].view(torch.int16)), i
+    print("[threads] 4 threads x 5 calls match serial calls", flush=True)
