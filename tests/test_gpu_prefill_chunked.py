@@ -395,3 +395,37 @@ def test_two_pass_workspace_beyond_4gib():
     assert kda.prefill_chunks_workspace_bytes(96, chunks) > 4 * 2 ** 30
     run_and_check(w, inp, cu, 96, flags=O.QK_L2NORM, label="H96 16400",
                   path="two_pass")
+
+
+def test_zero_sequences_is_a_noop():
+    """A prefill batch with no sequences (cu_seqlens = [0], no tokens)
+    through the token-by-token, fused chunked and two-pass entry points:
+    each returns without error and leaves both pools untouched."""
+    H = 24
+    w = synth.small("pf0", batch=1, heads=H, num_slots=4, seed=300)
+    base = synth.make_inputs(w)
+    t = synth.to_torch(base, DEV)
+    C = H * 128
+    cu = torch.zeros(1, dtype=torch.int32, device=DEV)
+    idx0 = torch.zeros(0, dtype=torch.int32, device=DEV)
+    qkv = torch.zeros(0, 3 * C, dtype=torch.bfloat16, device=DEV)
+    g = torch.zeros(0, H, 128, dtype=torch.float32, device=DEV)
+    beta = torch.zeros(0, H, dtype=torch.float32, device=DEV)
+    gate = torch.zeros(0, C, dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros(0, C, dtype=torch.bfloat16, device=DEV)
+    cs0, rs0 = t["conv_state"].clone(), t["rec_state"].clone()
+    for chunked in (False, True):
+        kda.kda_prefill(cu, qkv, t["conv_w"], t["conv_state"], t["rec_state"],
+                        g, beta, gate, t["norm_w"], idx0, out, norm=True,
+                        eps=w.eps, chunked=chunked)
+    ci, co = kda.chunk_metadata(cu, kda.PREFILL_CHUNK,
+                                cu_seqlens_host=torch.zeros(1, dtype=torch.int32))
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    kda.kda_prefill_chunks(cu, ci, co, 0, qkv, t["conv_w"], t["conv_state"],
+                           t["rec_state"], g, beta, gate, t["norm_w"], idx0,
+                           out, ws, norm=True, eps=w.eps)
+    torch.cuda.synchronize()
+    assert int(co[0]) == 0
+    assert torch.equal(t["conv_state"].view(torch.int16),
+                       cs0.view(torch.int16))
+    assert torch.equal(t["rec_state"].view(torch.int32), rs0.view(torch.int32))
