@@ -325,7 +325,8 @@ def prefill(inp: dict, cu_seqlens, *, heads: int, head_dim: int = 128,
     """Variable-length prefill on host arrays: the tokens of sequence n
     (cu_seqlens[n] .. cu_seqlens[n+1]-1 of the token-major qkv [tokens, 3C],
     g [tokens, H, D], beta [tokens, H], gate [tokens, C]) run through the
-    single-token step in order on slot state_idx[n].  fp32.  Optional
+    single-token step in order on slot state_idx[n] (a pair with
+    cu_seqlens[n+1] < cu_seqlens[n] is an empty sequence).  fp32.  Optional
     ``inp`` entries as in ``decode``, token-major: "conv_bias" [3C], and the
     raw gates "raw_g" [tokens, H, D] / "raw_beta" [tokens, H] / "A_log" /
     "dt_bias" / "lower_bound" (then "g" and "beta" are not read)."""
@@ -334,7 +335,10 @@ def prefill(inp: dict, cu_seqlens, *, heads: int, head_dim: int = 128,
     C = heads * head_dim
     qkv = np.ascontiguousarray(inp["qkv"], dtype=np.uint16)
     tokens = qkv.shape[0]
-    assert qkv.shape == (tokens, 3 * C) and int(cu[-1]) <= tokens
+    assert qkv.shape == (tokens, 3 * C)
+    # a decreasing pair is an empty sequence; every other one lies in range
+    live = cu[1:] > cu[:-1]
+    assert np.all(cu[:-1][live] >= 0) and np.all(cu[1:][live] <= tokens)
     cs = np.array(inp["conv_state"], dtype=np.uint16, order="C", copy=True)
     rs = np.array(inp["rec_state"], dtype=np.float32, order="C", copy=True)
     S = cs.shape[0]

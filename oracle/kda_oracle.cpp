@@ -328,7 +328,12 @@ int decode(const Dims* d, const uint16_t* qkv, const float* conv_w,
 // Sequence n covers tokens cu[n] .. cu[n+1]-1 of the token-major inputs
 // (qkv [tokens, 3C], g [tokens, H, D], beta [tokens, H], gate [tokens, C],
 // out [tokens, C]) and uses slot state_idx[n]; the result is that of one
-// single-token step per token, in order.  Sequences are independent.
+// single-token step per token, in order.  Sequences are independent.  The
+// prefill page gives a variable-length batch by its offsets but no rule for
+// offsets that go down; a pair with cu[n+1] < cu[n] is read as a sequence
+// of no tokens, like an equal pair: no output, no state touched (the same
+// reading as the chunk bookkeeping, where a negative length counts as
+// empty).
 template <typename T>
 int prefill(const Dims* d, const int32_t* cu, const uint16_t* qkv,
             const float* conv_w, uint16_t* conv_state, T* rec_state,
@@ -341,9 +346,8 @@ int prefill(const Dims* d, const int32_t* cu, const uint16_t* qkv,
   const int64_t H = d->num_heads, D = d->head_dim;
   const int64_t C = H * D;
   for (int64_t n = 0; n < N; ++n) {
-    if (cu[n + 1] < cu[n]) return ORC_ERR_INVALID_ARG;
-    const int64_t len = cu[n + 1] - cu[n];
-    if (len == 0) continue;
+    const int64_t len = static_cast<int64_t>(cu[n + 1]) - cu[n];
+    if (len <= 0) continue;
     const int32_t slot = state_idx[n];
     for (int64_t t = 0; t < len; ++t) {
       const int64_t tok = cu[n] + t;
@@ -446,7 +450,8 @@ int kda_oracle_decode_ext_f64(const kda_oracle_dims* d, const uint16_t* qkv,
 }
 
 // Variable-length prefill (see prefill() above); dims->batch = number of
-// sequences, cu_seqlens [batch + 1] token offsets (non-decreasing).
+// sequences, cu_seqlens [batch + 1] token offsets (a decreasing pair is an
+// empty sequence).
 int kda_oracle_prefill_f32(const kda_oracle_dims* d, const int32_t* cu_seqlens,
                            const uint16_t* qkv, const float* conv_w,
                            uint16_t* conv_state, float* rec_state,

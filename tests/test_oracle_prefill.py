@@ -123,6 +123,36 @@ def test_prefill_empty_sequence_and_null_slot_leave_state():
     assert np.all(got["out"] == 0)
 
 
+def test_prefill_decreasing_pair_is_an_empty_sequence():
+    """Offsets [20, 40, 3, 20, 0]: sequences 1 (40 -> 3) and 3 (20 -> 0)
+    go down, which reads as no tokens.  The batch must equal sequences 0
+    (tokens 20..39) and 2 (tokens 3..19) run as batches of their own; the
+    slots of the decreasing pairs stay bit-identical and tokens 0..2,
+    which no sequence covers, get no output."""
+    H = 12
+    w, inp, _ = _tokens_case(6, [20, 20], H, extra_slots=5)
+    inp["state_idx"] = np.array([4, 2, 6, 1], np.int32)
+    cu = np.array([20, 40, 3, 20, 0], np.int32)
+    got = O.prefill(inp, cu, heads=H)
+    a = O.prefill(dict(inp, state_idx=np.array([4], np.int32)),
+                  np.array([20, 40], np.int32), heads=H)
+    b = O.prefill(dict(inp, state_idx=np.array([6], np.int32),
+                       conv_state=a["conv_state"], rec_state=a["rec_state"]),
+                  np.array([3, 20], np.int32), heads=H)
+    assert np.array_equal(got["rec_state"], b["rec_state"])
+    assert np.array_equal(got["conv_state"], b["conv_state"])
+    assert np.array_equal(got["out"][20:40], a["out"][20:40])
+    assert np.array_equal(got["out"][3:20], b["out"][3:20])
+    assert np.all(got["out"][:3] == 0)
+    for s in (2, 1):
+        assert np.array_equal(got["rec_state"][s], inp["rec_state"][s])
+        assert np.array_equal(got["conv_state"][s], inp["conv_state"][s])
+    # the chunk bookkeeping counts both pairs as empty
+    idx, off = O.chunk_metadata(cu, 16)
+    assert off.tolist() == [0, 2, 2, 4, 4]
+    assert idx.tolist() == [[0, 0], [0, 1], [2, 0], [2, 1]]
+
+
 def _add_raw_gates(inp, H, D, seed, bias=True):
     """Raw gate operands for every token (bf16 raw_g / raw_beta, A_log,
     dt_bias) and optionally a conv bias."""

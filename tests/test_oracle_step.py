@@ -168,9 +168,19 @@ def test_heads_are_independent(oracle_mod):
     assert not np.array_equal(a["out"][:, ~cols], b["out"][:, ~cols])
 
 
-@pytest.mark.parametrize("wl", [synth.TINY, synth.B64_H24])
-def test_fp32_matches_fp64(oracle_mod, wl):
-    """P12: the fp32 oracle agrees with the fp64 one on the small workloads."""
+@pytest.mark.parametrize("wl,out_rtol", [(synth.TINY, 1e-3),
+                                         (synth.B64_H24, 1e-3),
+                                         (synth.B256_H48, 2e-3)],
+                         ids=["tiny", "b64_h24", "b256_h48"])
+def test_fp32_matches_fp64(oracle_mod, wl, out_rtol):
+    """P12: the fp32 oracle agrees with the fp64 one on the tiny, b64/h24
+    and b256/h48 (full size, 32 null rows) workloads: state within 1e-5,
+    outputs within 1e-3 relative (floor 1e-2 of the unit's rms).  At
+    b256/h48 two of its 1,376,256 outputs reach 1.37e-3: near-zero elements
+    (|y| ~ 0.002 rms) whose fp32 readout sums 128 products that nearly
+    cancel, so the rounding of those products is large next to the result.
+    There the bar is 2e-3, still ten times inside the 2e-2 bar the oracle
+    holds the GPU path to."""
     inp = synth.make_inputs(wl)
     a = run(oracle_mod, wl, inp, dtype="f32")
     b = run(oracle_mod, wl, inp, dtype="f64")
@@ -179,7 +189,7 @@ def test_fp32_matches_fp64(oracle_mod, wl):
     assert np.array_equal(a["conv_state"], b["conv_state"])
     yr = b["y"].reshape(wl.batch, wl.heads, -1)
     rms = np.sqrt(np.mean(yr ** 2, axis=-1, keepdims=True))
-    bound = 1e-3 * np.maximum(np.abs(yr), 1e-2 * rms)
+    bound = out_rtol * np.maximum(np.abs(yr), 1e-2 * rms)
     assert np.all(np.abs(a["y"].reshape(yr.shape) - yr) <= bound)
 
 
