@@ -171,8 +171,9 @@ kda_status kda_decode_raw_gates(const kda_dims* dims, const void* qkv,
  * KDA_NO_CONV_UPDATE every token sees the stored conv window, as T
  * successive calls with that flag would.  From T = 29 on, the call runs
  * the chunked matrix-core form of kda_prefill_chunked (each row one
- * sequence of T tokens): equal up to rounding, and faster there; g must
- * then be finite.
+ * sequence of T tokens): equal up to rounding, and faster there.  The
+ * contract on g does not change with T: any g <= 0 down to -inf is
+ * accepted on both sides (-inf forgets the key row, as exp(-inf) = 0).
  */
 kda_status kda_decode_tokens(const kda_dims* dims, int32_t tokens,
                              const void* qkv, const float* conv_w,
@@ -211,9 +212,12 @@ kda_status kda_prefill(const kda_dims* dims, const int32_t* cu_seqlens,
  * state follow from Delta by matrix products.  In exact arithmetic this is
  * the token-by-token recurrence; in fp32 it differs only by rounding.  One
  * workgroup per (sequence, head) carries the state across the sequence's
- * chunks.  g must be finite; chunks whose cumulative decay exceeds 80 in
- * magnitude in any channel take an exact per-entry path.  Arguments, flags,
- * rules and status codes as kda_prefill.
+ * chunks.  Chunks whose cumulative decay exceeds 80 in magnitude in any
+ * channel take an exact per-entry path; a token's decay below -200 log2
+ * units (e^g = 0 in fp32), -inf included, is taken as -200 log2 units,
+ * which leaves every decay factor of the chunk exactly as it would be
+ * (zero) for g <= 0.  Arguments, flags, rules and status codes as
+ * kda_prefill.
  */
 kda_status kda_prefill_chunked(const kda_dims* dims, const int32_t* cu_seqlens,
                                const void* qkv, const float* conv_w,

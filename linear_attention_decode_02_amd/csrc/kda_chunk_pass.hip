@@ -296,6 +296,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
               kLog2e;
     }
   }
+#pragma unroll
+  for (int t = 0; t < kC; ++t) gl[t] = kda_decay_floor2(gl[t]);
   f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
   f2 G = {0.f, 0.f};
   float gmax = 0.0f;
@@ -577,8 +579,9 @@ __global__ __launch_bounds__(64 * kStateWaves) void kda_chunk_state_kernel(
 #pragma unroll
       for (int e = 0; e < kW - 1; ++e) {
         const int idx = len - (kW - 1) + e;
-        nwin[e] = idx >= 0 ? p.qkv[(tb + idx) * C3 + ch]
-                           : p.conv_state[at(e + len)];
+        nwin[e] = idx >= 0
+                      ? p.qkv[(static_cast<int64_t>(tb) + idx) * C3 + ch]
+                      : p.conv_state[at(e + len)];
       }
 #pragma unroll
       for (int e = 0; e < kW - 1; ++e) p.conv_state[at(e)] = nwin[e];

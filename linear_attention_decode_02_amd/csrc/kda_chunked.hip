@@ -219,10 +219,12 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   const int C3 = 3 * C;
   const int n = static_cast<int>(blockIdx.x) / H;
   const int h = static_cast<int>(blockIdx.x) % H;
-  const int32_t tb = p.cu_seqlens ? p.cu_seqlens[n] : n * p.tokens_per_row;
-  const int32_t te =
+  // token offsets in 64 bits: tb * 3C passes 2^31 from 58,255 tokens at
+  // 96 heads
+  const int64_t tb = p.cu_seqlens ? p.cu_seqlens[n] : n * p.tokens_per_row;
+  const int64_t te =
       p.cu_seqlens ? p.cu_seqlens[n + 1] : (n + 1) * p.tokens_per_row;
-  const int len = te > tb ? te - tb : 0;
+  const int len = te > tb ? static_cast<int>(te - tb) : 0;
   if (len == 0) return;
   const int32_t slot = p.state_idx[n];
   const int64_t col0 = static_cast<int64_t>(h) * kD;
@@ -393,6 +395,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     for (int t = 0; t < kC; ++t) {
       gl[t] = *reinterpret_cast<const f2*>(&sm.gst[ci & 1][t][2 * lane]);
       if (!kRaw) gl[t] *= kLog2e;
+      gl[t] = kda_decay_floor2(gl[t]);
     }
     const float bt = lane < 4 ? sm.bst[ci & 1][4 * pw + lane] : 0.0f;
     // the staging buffers are free again: request the next chunk

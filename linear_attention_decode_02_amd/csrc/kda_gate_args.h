@@ -35,3 +35,16 @@ __device__ __forceinline__ float kda_gate2_from_raw(float z, float a_rate,
       z > 20.0f ? z2 : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(z2));
   return -(a_rate * sp2);
 }
+
+// Floor of a per-token log2 decay.  2^x is exactly 0 in fp32 for every
+// x <= -200, so clamping there leaves every decay factor of the chunk form
+// unchanged for non-positive decays: a factor e^{G_t - G_s} whose span
+// holds a clamped token has exponent <= -200 either way.  It keeps the
+// cumulative sums finite, so that g = -inf (full forgetting) gives zeros
+// instead of -inf - -inf = NaN.  NaN passes through (the comparison is
+// false).
+typedef float kda_f2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ kda_f2 kda_decay_floor2(kda_f2 g2) {
+  return kda_f2{g2.x < -200.0f ? -200.0f : g2.x,
+                g2.y < -200.0f ? -200.0f : g2.y};
+}

@@ -58,36 +58,23 @@ def test_b256_h48_null32_full_size():
     assert np.array_equal(got["conv_state"][0], inp["conv_state"][0])
 
 
-def test_b512_h96_nonorm_full_size_sampled():
+def test_b512_h96_nonorm_full_size():
     """Full-size batch-512, 96-head, norm-off call with the stressed decay
-    mix.  Every conv state is checked bit for bit against its closed form
-    (old taps shifted, token appended) and every untouched slot for
-    identity; the oracle recomputes 48 sampled rows."""
+    mix, every row against the oracle: conv state bit-exact over the whole
+    pool, untouched slots bit-identical, state within 1e-3, outputs within
+    2e-2.  The conv state is also checked against its closed form (old
+    taps shifted, token appended)."""
     w = synth.B512_H96
     inp = synth.make_inputs(w)
     g = inp["g"]
     print(f"[b512] g fractions near-zero {np.mean(g == np.float32(-1e-4)):.3f}"
           f" strong {np.mean(g == -8.0):.3f}", flush=True)
-    got = P.run_gpu(w, inp, DEV)
+    got, _ = parity(w, inp)
     idx = inp["state_idx"]
     cs_exp = inp["conv_state"].copy()
     cs_exp[idx, :, :2] = inp["conv_state"][idx, :, 1:]
     cs_exp[idx, :, 2] = inp["qkv"]
     assert np.array_equal(got["conv_state"], cs_exp)
-    untouched = np.setdiff1d(np.arange(w.num_slots), idx)
-    assert np.array_equal(got["rec_state"][untouched].view(np.uint32),
-                          inp["rec_state"][untouched].view(np.uint32))
-    y = P.bf16_to_f32(got["out"])
-    assert np.all(np.isfinite(y))
-    rows = np.sort(np.random.default_rng(0).choice(w.batch, 48, replace=False))
-    sub, keep = P.sub_problem(inp, rows, w.num_slots)
-    ref = P.run_oracle(dataclasses.replace(w, batch=rows.size,
-                                           num_slots=keep.size), sub)
-    err = np.abs(got["rec_state"][keep[1:]] - ref["rec_state"][1:]).max()
-    assert err <= P.STATE_TOL, err
-    st = P.check_output(got["out"][rows], ref["y"], sub["state_idx"],
-                        keep.size, w.heads)
-    print(f"[b512] state err {err:.2e} {st}", flush=True)
 
 
 @pytest.mark.parametrize("H", synth.SUPPORTED_HEADS)

@@ -45,6 +45,23 @@ def test_chunk_metadata_bit_exact(case):
     print(f"[metadata] {len(lens)} seqs, {ref_idx.shape[0]} chunks", flush=True)
 
 
+def test_chunk_metadata_decreasing_offsets():
+    """Offsets that go down count as empty sequences (a negative length),
+    and offsets need not start at 0: bit-exact against the oracle's
+    bookkeeping."""
+    for cu, bt in (([20, 40, 3, 20, 0], 16),
+                   ([100, 5000, 0, 64, 64, 10, 4000], 64)):
+        cu = np.asarray(cu, np.int32)
+        ref_idx, ref_off = O.chunk_metadata(cu, bt)
+        idx, off = kda.chunk_metadata(torch.from_numpy(cu).to(DEV), bt,
+                                      cu_seqlens_host=torch.from_numpy(cu))
+        torch.cuda.synchronize()
+        assert np.array_equal(off.cpu().numpy(), ref_off)
+        assert np.array_equal(idx.cpu().numpy(), ref_idx)
+        print(f"[metadata decreasing] {cu.tolist()}: {ref_off.tolist()}",
+              flush=True)
+
+
 def prefill_case(seed, lens, H, S=None, norm=True, null=(), zero_state=False,
                  conv_w_sigma=0.05):
     """Token-major inputs.  Small conv weights by default: long chains of
@@ -91,16 +108,26 @@ def run_prefill(w, inp, cu, variants=0, chunked=False):
             "rec_state": t["rec_state"].cpu().numpy()}
 
 
-def check_prefill(w, inp, cu, got, ref):
+def check_prefill(w, inp, cu, got, ref, scaled=False):
+    """Parity of a prefill call under the absolute 1e-3 state bar (every
+    prefill case here is contractive: small conv weights or L2-normalised
+    keys); ``scaled`` would make it relative to each unit's state magnitude
+    for an expansive case.  Offsets may go down (an empty sequence): only
+    tokens that a non-empty sequence covers are compared."""
+    lens = np.diff(cu)
     st = P.check_states(got["conv_state"], got["rec_state"], ref["conv_state"],
                         ref["rec_state"], inp["conv_state"], inp["rec_state"],
-                        np.where(np.diff(cu) > 0, inp["state_idx"], 0),
-                        w.num_slots, scaled=True)
-    # per-token rows: map each token to its sequence's slot for the checks
-    seq_of = np.repeat(np.arange(cu.size - 1), np.diff(cu))
-    tok_idx = inp["state_idx"][seq_of]
-    st.update(P.check_output(got["out"], ref["y"], tok_idx, w.num_slots,
-                             w.heads))
+                        np.where(lens > 0, inp["state_idx"], 0),
+                        w.num_slots, scaled=scaled)
+    # per-token rows: each covered token with its sequence's slot
+    live = np.flatnonzero(lens > 0)
+    toks = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in live]
+                          ) if live.size else np.zeros(0, np.int64)
+    tok_idx = np.concatenate([np.full(lens[n], inp["state_idx"][n])
+                              for n in live]) if live.size else \
+        np.zeros(0, np.int32)
+    st.update(P.check_output(got["out"][toks], ref["y"][toks], tok_idx,
+                             w.num_slots, w.heads))
     return st
 
 
@@ -149,3 +176,25 @@ def test_prefill_equals_multi_token_decode_for_equal_lengths():
     assert np.array_equal(a["out"], synth.bf16_bits(out).reshape(N * T, -1))
     assert np.array_equal(a["rec_state"].view(np.uint32),
                           t["rec_state"].cpu().numpy().view(np.uint32))
+
+
+def decreasing_case(H, seed):
+    """Offsets [20, 40, 3, 20, 0] over 40 tokens: sequence 0 covers tokens
+    20..39, sequence 2 tokens 3..19; sequences 1 and 3 go down (empty) and
+    tokens 0..2 belong to no sequence."""
+    w, inp, _ = prefill_case(seed, [20, 20], H, S=8)
+    inp["state_idx"] = np.array([4, 2, 6, 1], np.int32)
+    return w, inp, np.array([20, 40, 3, 20, 0], np.int32)
+
+
+def test_prefill_decreasing_offsets():
+    """The token-by-token prefill with decreasing offset pairs, against the
+    oracle; the slots of the empty sequences stay bit-identical (checked in
+    check_prefill) and tokens no sequence covers keep their old output."""
+    H = 24
+    w, inp, cu = decreasing_case(H, 330)
+    ref = O.prefill(inp, cu, heads=H, eps=w.eps)
+    got = run_prefill(w, inp, cu)
+    st = check_prefill(w, inp, cu, got, ref)
+    assert np.all(np.isnan(P.bf16_to_f32(got["out"][:3])))
+    print(f"[prefill decreasing] {st}", flush=True)

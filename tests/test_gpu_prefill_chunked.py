@@ -15,7 +15,8 @@ import oracle as O
 from linear_attention_decode_02_amd import kda, synth
 
 import _parity as P
-from test_gpu_prefill import check_prefill, prefill_case, run_prefill
+from test_gpu_prefill import (check_prefill, decreasing_case, prefill_case,
+                              run_prefill)
 
 DEV = "cuda:0"
 
@@ -429,3 +430,72 @@ def test_zero_sequences_is_a_noop():
     assert torch.equal(t["conv_state"].view(torch.int16),
                        cs0.view(torch.int16))
     assert torch.equal(t["rec_state"].view(torch.int32), rs0.view(torch.int32))
+
+
+def test_chunked_decreasing_offsets(path):
+    """Decreasing offset pairs (empty sequences) and offsets that do not
+    start at 0, through both chunked paths, against the oracle; tokens no
+    sequence covers keep their old output."""
+    H = 24
+    w, inp, cu = decreasing_case(H, 331)
+    got, _ = run_and_check(w, inp, cu, H, label="decreasing", path=path)
+    assert np.all(np.isnan(P.bf16_to_f32(got["out"][:3])))
+
+
+def test_token_offsets_past_int32_products(path):
+    """64-bit token offsets: 96 heads and a 300-token sequence whose first
+    token is token 176,000 of the token-major buffers, so token x 3C and
+    token x C pass 2^31 elements (qkv 13.0 GB, g 8.7 GB, gate and out
+    4.3 GB each on the device).  Only the sequence's rows are filled (with
+    the seeded inputs of a 300-token case); the kernels read no other row.
+    The token-by-token prefill and the chunked path each run on the
+    sequence, against the oracle on the same 300 tokens; conv state bit
+    for bit."""
+    H, L, T0 = 96, 300, 176_000
+    w, inp, cu0 = prefill_case(340, [L], H, S=3, zero_state=True,
+                               conv_w_sigma=0.5)
+    flags = O.QK_L2NORM
+    ref = O.prefill(inp, cu0, heads=H, eps=w.eps, flags=flags)
+    C = H * 128
+    assert T0 * C > 2 ** 31       # hence T0 * 3C too
+    total = T0 + L
+    t = synth.to_torch(inp, DEV)
+    big = {"qkv": torch.empty(total, 3 * C, dtype=torch.bfloat16, device=DEV),
+           "g": torch.empty(total, H, 128, dtype=torch.float32, device=DEV),
+           "beta": torch.empty(total, H, dtype=torch.float32, device=DEV),
+           "gate": torch.empty(total, C, dtype=torch.bfloat16, device=DEV)}
+    for k, b in big.items():
+        b[T0:].copy_(t[k])
+    cu = torch.tensor([T0, total], dtype=torch.int32, device=DEV)
+    cu_h = cu.cpu()
+    cs0, rs0 = t["conv_state"].clone(), t["rec_state"].clone()
+    for which in ("token", path):
+        t["conv_state"].copy_(cs0)
+        t["rec_state"].copy_(rs0)
+        out = torch.full((total, C), float("nan"), dtype=torch.bfloat16,
+                         device=DEV)
+        if which == "two_pass":
+            idx, off = kda.chunk_metadata(cu, kda.PREFILL_CHUNK,
+                                          cu_seqlens_host=cu_h)
+            mc = int(idx.shape[0])
+            ws = torch.empty(kda.prefill_chunks_workspace_bytes(H, mc),
+                             dtype=torch.uint8, device=DEV)
+            kda.kda_prefill_chunks(cu, idx, off, mc, big["qkv"], t["conv_w"],
+                                   t["conv_state"], t["rec_state"], big["g"],
+                                   big["beta"], big["gate"], t["norm_w"],
+                                   t["state_idx"], out, ws, eps=w.eps,
+                                   variants=flags)
+        else:
+            kda.kda_prefill(cu, big["qkv"], t["conv_w"], t["conv_state"],
+                            t["rec_state"], big["g"], big["beta"],
+                            big["gate"], t["norm_w"], t["state_idx"], out,
+                            eps=w.eps, variants=flags,
+                            chunked=which == "fused")
+        torch.cuda.synchronize()
+        got = {"out": synth.bf16_bits(out[T0:]),
+               "conv_state": synth.bf16_bits(t["conv_state"]),
+               "rec_state": t["rec_state"].cpu().numpy()}
+        assert bool(torch.isnan(out[:T0:997].float()).all())   # untouched
+        st = check_prefill(w, inp, cu0, got, ref)
+        print(f"[offsets past 2^31] {which}: {st}", flush=True)
+        del out

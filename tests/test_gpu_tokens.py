@@ -57,7 +57,12 @@ def run_single_calls(w, inp, T, variants=0):
             "rec_state": t["rec_state"].cpu().numpy()}
 
 
-def check_tokens(w, inp, got, ref, T, flags=0):
+def check_tokens(w, inp, got, ref, T, flags=0, scaled=False):
+    """Parity of a multi-token call.  The state bar is the absolute 1e-3;
+    ``scaled`` makes it 1e-3 relative to each unit's largest state
+    magnitude, for the expansive regime only (beta |k|^2 > 2: raw keys from
+    the reference conv weights, where each token multiplies the state, and
+    its fp32 rounding, by up to |1 - beta |k|^2| ~ 20)."""
     cs_got, cs_ref, cs_in = got["conv_state"], ref["conv_state"], \
         inp["conv_state"]
     if flags & O.CONV_TAP_MAJOR:
@@ -65,7 +70,7 @@ def check_tokens(w, inp, got, ref, T, flags=0):
                                  for a in (cs_got, cs_ref, cs_in))
     st = P.check_states(cs_got, got["rec_state"], cs_ref, ref["rec_state"],
                         cs_in, inp["rec_state"], inp["state_idx"],
-                        w.num_slots, scaled=True)
+                        w.num_slots, scaled=scaled)
     for t in range(T):
         st_t = P.check_output(got["out"][:, t], ref["y"][:, t],
                               inp["state_idx"], w.num_slots, w.heads)
@@ -157,20 +162,25 @@ def test_tokens_parity_with_oracle(name, flags, norm, H, T):
     ref = O.decode_tokens(inp, heads=H, tokens=T, norm=norm, eps=w.eps,
                           flags=flags)
     got = run_tokens(w, inp, T, variants=flags)
-    st = check_tokens(w, inp, got, ref, T, flags)
+    # reference conv weights: raw keys are expansive, L2-normalised ones
+    # contractive
+    st = check_tokens(w, inp, got, ref, T, flags,
+                      scaled=not flags & O.QK_L2NORM)
     if flags & O.NO_CONV_UPDATE:
         assert np.array_equal(got["conv_state"], inp["conv_state"])
     print(f"[tokens] {name}: {st}", flush=True)
 
 
 def test_tokens_b256_h48_full_size():
-    """The batch-256, 48-head workload (32 null rows) with 4 tokens per row."""
+    """The batch-256, 48-head workload (32 null rows) with 4 tokens per row.
+    Raw keys from the reference conv weights: the expansive regime, so the
+    state bar is relative to each unit's state magnitude."""
     w = synth.B256_H48
     T = 4
     inp = synth.make_tokens(w, T)
     ref = O.decode_tokens(inp, heads=w.heads, tokens=T, norm=True, eps=w.eps)
     got = run_tokens(w, inp, T)
-    st = check_tokens(w, inp, got, ref, T)
+    st = check_tokens(w, inp, got, ref, T, scaled=True)
     assert np.all(got["out"][-32:] == 0)
     print(f"[tokens b256] {st}", flush=True)
 
@@ -326,3 +336,65 @@ def test_tokens_graph_replay_matches_eager(T):
         assert torch.equal(tg["rec_state"].view(torch.int32),
                            te["rec_state"].view(torch.int32)), r
         print(f"[tokens graph T={T}] replay {r} matches eager", flush=True)
+
+
+@pytest.mark.parametrize("T", [28, 29])
+def test_tokens_decay_contract_independent_of_T(T):
+    """The contract on g is the same on both sides of the switch to the
+    chunked form at 29 tokens: per element -inf (5 %, the key row is
+    forgotten), -1e30 (5 %), -100 (5 %, exp underflows), -1e-4 (5 %) or an
+    ordinary decay, against the oracle (exp(-inf) = 0 there)."""
+    w = synth.small(f"tginf{T}", batch=6, heads=24, num_slots=10,
+                    seed=310 + T, null_every=4, conv_w_sigma=0.05)
+    inp = synth.make_tokens(w, T)
+    u = np.random.default_rng(311).random(inp["g"].shape)
+    g = inp["g"].copy()
+    g[u < 0.20] = -1e-4
+    g[u < 0.15] = -100.0
+    g[u < 0.10] = -1e30
+    g[u < 0.05] = -np.inf
+    inp["g"] = np.ascontiguousarray(g.astype(np.float32))
+    ref = O.decode_tokens(inp, heads=w.heads, tokens=T, norm=True, eps=w.eps)
+    assert np.isfinite(ref["rec_state"]).all()
+    got = run_tokens(w, inp, T)
+    st = check_tokens(w, inp, got, ref, T)
+    print(f"[tokens decay contract T={T}] {st}", flush=True)
+
+
+def test_tokens_offsets_past_int32_products():
+    """64-bit token offsets in kda_decode_tokens: 64 rows x 1024 tokens at
+    96 heads, so row x T x 3C passes 2^31 elements from row 57 on (the
+    chunked form runs at this T).  Rows 0..59 are null (they read no input
+    and write zeros); rows 60..63 carry seeded inputs and are compared with
+    the oracle.  q/k L2-normalised (contractive)."""
+    B, T, H = 64, 1024, 96
+    C = H * 128
+    live = 4
+    small = synth.small("tbig", batch=live, heads=H, num_slots=live + 1,
+                        seed=320, conv_w_sigma=0.5)
+    inp = synth.make_tokens(small, T)
+    inp["state_idx"] = np.arange(1, live + 1, dtype=np.int32)
+    ref = O.decode_tokens(inp, heads=H, tokens=T, norm=True, eps=small.eps,
+                          flags=O.QK_L2NORM)
+    t = synth.to_torch(inp, DEV)
+    big = {"qkv": torch.empty(B, T, 3 * C, dtype=torch.bfloat16, device=DEV),
+           "g": torch.empty(B, T, H, 128, dtype=torch.float32, device=DEV),
+           "beta": torch.empty(B, T, H, dtype=torch.float32, device=DEV),
+           "gate": torch.empty(B, T, C, dtype=torch.bfloat16, device=DEV)}
+    for k, b in big.items():
+        b[B - live:].copy_(t[k])
+    idx = torch.zeros(B, dtype=torch.int32, device=DEV)
+    idx[B - live:] = t["state_idx"]
+    out = torch.full((B, T, C), float("nan"), dtype=torch.bfloat16,
+                     device=DEV)
+    kda.kda_decode_tokens(big["qkv"], t["conv_w"], t["conv_state"],
+                          t["rec_state"], big["g"], big["beta"], big["gate"],
+                          t["norm_w"], idx, out, norm=True, eps=small.eps,
+                          variants=O.QK_L2NORM)
+    torch.cuda.synchronize()
+    assert bool((out[:B - live].view(torch.int16) == 0).all())
+    got = {"out": synth.bf16_bits(out[B - live:]),
+           "conv_state": synth.bf16_bits(t["conv_state"]),
+           "rec_state": t["rec_state"].cpu().numpy()}
+    st = check_tokens(small, inp, got, ref, T)
+    print(f"[tokens offsets past 2^31] {st}", flush=True)
