@@ -270,6 +270,11 @@ def main():
 
     traffic = (recorded_traffic(w.name)
                if args.variant == "plain" and T == 1 else None)
+    if traffic is not None:
+        extra["traffic_source"] = (
+            "recorded: calibrated FETCH_SIZE + WRITE_SIZE counters of this "
+            "kernel source on this workload (" +
+            os.path.relpath(TRAFFIC_FILE, ROOT) + "), not read in this run")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -509,8 +514,7 @@ def bench_prefill(args, np, torch, kda, synth):
     meta_us = m0.elapsed_time(m1) * 1e3 / 100
     cpu = None
     if args.cpu_seconds > 0:
-        cores = min(os.cpu_count() or 1,
-                    int(os.environ.get("OMP_NUM_THREADS", "0")) or 16, 16)
+        cores, info = cpu_threads()
         # a bounded sample: the 4 shortest sequences, repeated
         order = np.argsort(lens)[:4]
         sub_lens = lens[order]
@@ -519,19 +523,20 @@ def bench_prefill(args, np, torch, kda, synth):
         sub = dict(inp, state_idx=inp["state_idx"][order].copy())
         for k in ("qkv", "g", "beta", "gate"):
             sub[k] = np.ascontiguousarray(inp[k][sel])
-        reps, c0 = 0, time.perf_counter()
-        while True:
-            oracle.prefill(sub, sub_cu, heads=H, eps=w.eps, nthreads=cores,
-                           flags=0x08)
-            reps += 1
-            el = time.perf_counter() - c0
-            if el >= args.cpu_seconds:
-                break
-        cpu = {"value": round(int(sub_lens.sum()) * H * reps / el, 1),
+        sub_updates = int(sub_lens.sum()) * H
+        runs = timed_runs(lambda: oracle.prefill(
+            sub, sub_cu, heads=H, eps=w.eps, nthreads=cores, flags=0x08),
+            args.cpu_seconds)
+        rates = sorted(sub_updates * r / el for r, el in runs)
+        cpu = {"value": round(float(np.median(rates)), 1),
                "unit": "token-head updates/s", "cores": cores,
                "kind": "oracle",
                "sample": f"4 shortest sequences ({int(sub_lens.sum())} "
-                         f"tokens) x {reps} calls, {el:.1f} s"}
+                         f"tokens), median of 3 runs of "
+                         f"{args.cpu_seconds / 3:.1f} s, {cores} threads, "
+                         f"{info['model']}",
+               "runs_updates_per_s": [round(r, 1) for r in rates],
+               "host": info}
     line = {
         "metric": "KDA prefill token-head updates/sec (variable length)",
         "value": round(updates * K / wall, 1), "unit": "updates/s",
@@ -674,51 +679,18 @@ def stream_ceiling(torch, kda, stream, w, live_rows, alg_bytes, kern_s,
             "serial_over_kernel": round(bound / kern_s, 4)}
 
 
-def cpu_baseline(w, inp, seconds, alg_bytes, units, flags=0, tokens=1):
-    """The CPU oracle (fp32, OpenMP over units) on the same batch, repeated
-    in place until ``seconds`` have passed."""
-    import numpy as np
-
-    import oracle
-
-    cores = min(os.cpu_count() or 1,
-                int(os.environ.get("OMP_NUM_THREADS", "0")) or 16, 16)
-    oracle.lib()
-    work = dict(inp, conv_state=inp["conv_state"].copy(),
-                rec_state=inp["rec_state"].copy())
-    print(f"[bench] cpu oracle on {cores} threads", file=sys.stderr,
-          flush=True)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        if tokens > 1:
-            oracle.decode_tokens(work, heads=w.heads, tokens=tokens,
-                                 norm=w.norm, eps=w.eps, dtype="f32",
-                                 nthreads=cores, flags=flags, inplace=True)
-        else:
-            oracle.decode(work, heads=w.heads, norm=w.norm, eps=w.eps,
-                          dtype="f32", nthreads=cores, inplace=True,
-                          flags=flags)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    # the same oracle on one thread, for about a fifth of the time
-    work1 = dict(inp, conv_state=inp["conv_state"].copy(),
-                 rec_state=inp["rec_state"].copy())
-    reps1, t1 = 0, time.perf_counter()
-    while True:
-        if tokens > 1:
-            oracle.decode_tokens(work1, heads=w.heads, tokens=tokens,
-                                 norm=w.norm, eps=w.eps, dtype="f32",
-                                 nthreads=1, flags=flags, inplace=True)
-        else:
-            oracle.decode(work1, heads=w.heads, norm=w.norm, eps=w.eps,
-                          dtype="f32", nthreads=1, inplace=True, flags=flags)
-        reps1 += 1
-        el1 = time.perf_counter() - t1
-        if el1 >= seconds / 5:
-            break
-    del work1
+def cpu_threads():
+    """Threads for the CPU oracle: every CPU this process may run on
+    (its affinity mask), capped by OMP_NUM_THREADS when that is set (the
+    GPU host allots each GPU's jobs a CPU share through it).  Returns the
+    count and the facts it came from."""
+    nproc = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = nproc
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = max(1, min(allowed, omp) if omp > 0 else allowed)
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -728,13 +700,69 @@ def cpu_baseline(w, inp, seconds, alg_bytes, units, flags=0, tokens=1):
                     break
     except OSError:
         pass
-    del np
-    return {"value": round(units * reps / el, 1), "unit": "updates/s",
+    return threads, {"nproc": nproc, "affinity_cpus": allowed,
+                     "omp_num_threads": omp or None, "model": model}
+
+
+def timed_runs(fn, seconds, runs=3):
+    """``runs`` timed runs of ``fn`` (each repeated until seconds / runs
+    have passed); returns [(calls, elapsed)] per run."""
+    res = []
+    for _ in range(runs):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds / runs:
+                break
+        res.append((reps, el))
+    return res
+
+
+def cpu_baseline(w, inp, seconds, alg_bytes, units, flags=0, tokens=1):
+    """The CPU oracle (fp32, OpenMP over units) on the same batch, in
+    place: the median rate of three runs of about seconds / 3 each on every
+    allotted core, and one run of about seconds / 5 on one thread."""
+    import numpy as np
+
+    import oracle
+
+    cores, info = cpu_threads()
+    oracle.lib()
+    print(f"[bench] cpu oracle on {cores} threads ({info})", file=sys.stderr,
+          flush=True)
+
+    def one_call(work, nthreads):
+        def fn():
+            if tokens > 1:
+                oracle.decode_tokens(work, heads=w.heads, tokens=tokens,
+                                     norm=w.norm, eps=w.eps, dtype="f32",
+                                     nthreads=nthreads, flags=flags,
+                                     inplace=True)
+            else:
+                oracle.decode(work, heads=w.heads, norm=w.norm, eps=w.eps,
+                              dtype="f32", nthreads=nthreads, inplace=True,
+                              flags=flags)
+        return fn
+
+    work = dict(inp, conv_state=inp["conv_state"].copy(),
+                rec_state=inp["rec_state"].copy())
+    runs = timed_runs(one_call(work, cores), seconds)
+    rates = sorted(units * r / el for r, el in runs)
+    rate = float(np.median(rates))
+    (reps1, el1), = timed_runs(one_call(work, 1), seconds / 5, runs=1)
+    del work
+    return {"value": round(rate, 1), "unit": "updates/s",
             "cores": cores, "kind": "oracle",
             "sample": (f"{'one layer of the ' if w.layers > 1 else ''}"
-                       f"full {w.name} batch ({units} updates) x {reps} calls "
-                       f"in place, {el:.1f} s, fp32, {model}"),
-            "GBs": round(alg_bytes * reps / el / 1e9, 2),
+                       f"full {w.name} batch ({units} updates) in place, "
+                       f"median of 3 runs of {seconds / 3:.1f} s "
+                       f"({', '.join(str(r) for r, _ in runs)} calls), fp32, "
+                       f"{cores} threads, {info['model']}"),
+            "runs_updates_per_s": [round(r, 1) for r in rates],
+            "host": info,
+            "GBs": round(alg_bytes * rate / units / 1e9, 2),
             "single_thread": {"value": round(units * reps1 / el1, 1),
                               "unit": "updates/s", "calls": reps1,
                               "seconds": round(el1, 1)}}

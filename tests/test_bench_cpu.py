@@ -47,16 +47,33 @@ def test_recorded_traffic_matches_this_kernel():
 
 def test_cpu_baseline_reports_threads_model_and_single_thread_rate():
     """The oracle baseline object carries the fields the bench line states:
-    rate, unit, the threads used, kind, the sample, and a one-thread rate."""
+    the median rate of three runs, unit, the threads used (every CPU the
+    process may run on, capped only by OMP_NUM_THREADS), the host facts,
+    kind, the sample, and a one-thread rate."""
     from linear_attention_decode_02_amd import synth
 
     w = synth.small("cpu_fields", batch=3, heads=12, num_slots=6, seed=1,
                     null_every=3)
     inp = synth.make_inputs(w)
     units = w.units(inp["state_idx"])
-    r = bench.cpu_baseline(w, inp, 0.2, 1000, units)
+    r = bench.cpu_baseline(w, inp, 0.3, 1000, units)
     assert r["kind"] == "oracle" and r["unit"] == "updates/s"
-    assert r["value"] > 0 and 1 <= r["cores"] <= 16
+    runs = r["runs_updates_per_s"]
+    assert len(runs) == 3 and r["value"] == runs[1] > 0
+    host = r["host"]
+    allowed = len(os.sched_getaffinity(0))
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    assert r["cores"] == (min(allowed, omp) if omp else allowed)
+    assert host["nproc"] == os.cpu_count()
+    assert host["affinity_cpus"] == allowed and host["model"]
     assert f"({units} updates)" in r["sample"]
     st = r["single_thread"]
     assert st["value"] > 0 and st["calls"] >= 1
+
+
+def test_cpu_threads_follow_omp_num_threads(monkeypatch):
+    allowed = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.cpu_threads()[0] == 1
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.cpu_threads()[0] == allowed
