@@ -59,7 +59,8 @@ typedef enum kda_status {
   KDA_ERR_UNSUPPORTED = 2, /* head count not in {12,24,48,96}, D != 128, W != 4 */
   KDA_ERR_MISALIGNED = 3,  /* a buffer pointer not 16-byte aligned           */
   KDA_ERR_DEVICE = 4,      /* no HIP device, or the current one is not gfx950 */
-  KDA_ERR_LAUNCH = 5       /* the kernel launch reported an error            */
+  KDA_ERR_LAUNCH = 5,      /* the kernel launch reported an error            */
+  KDA_ERR_TOO_LARGE = 6    /* request exceeds the library's static scratch  */
 } kda_status;
 
 /* flags (kda_dims.flags).  The page's kernel has template switches for
@@ -263,6 +264,34 @@ kda_status kda_prefill_chunks(const kda_dims* dims, const int32_t* cu_seqlens,
                               const int32_t* state_idx, void* out,
                               void* workspace, uint64_t workspace_bytes,
                               void* hip_stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * kda_prefill_chunks with its per-(chunk, head) records kept in a scratch
+ * array inside the library instead of a caller workspace.  The array is a
+ * file-scope device array of KDA_STATIC_SCRATCH_BYTES bytes, one per GPU,
+ * created when the library is loaded on that GPU and held until the process
+ * ends; the call allocates nothing and frees nothing.
+ *   max_chunks * H * kda_prefill_chunks_workspace_bytes(dims, 1) must be
+ *   at most KDA_STATIC_SCRATCH_BYTES (else KDA_ERR_TOO_LARGE, nothing
+ *   queued): e.g. 123 chunks of 16 tokens at 48 heads, 495 at 12.
+ * Every call on one GPU uses that GPU's array, which keeps the last call's
+ * records (the kernels read only what the same call wrote): calls that
+ * overlap on one GPU -- on two streams, from two threads, or a graph
+ * replay beside an eager call -- race on it and give undefined results.
+ * Arguments other than the workspace, flags, rules and status codes as
+ * kda_prefill_chunks; KDA_ERR_DEVICE also if the array cannot be located
+ * on the current device.
+ */
+#define KDA_STATIC_SCRATCH_BYTES (256ull << 20)
+kda_status kda_prefill_chunks_static(
+    const kda_dims* dims, const int32_t* cu_seqlens,
+    const int32_t* chunk_indices, const int64_t* chunk_offsets,
+    int64_t max_chunks, const void* qkv, const float* conv_w, void* conv_state,
+    float* rec_state, const float* g, const float* beta, const void* gate,
+    const float* norm_w, const int32_t* state_idx, void* out,
+    void* hip_stream);
 
 /*
  * Raw gate inputs of a prefill call, token-major (the chunk op of the page

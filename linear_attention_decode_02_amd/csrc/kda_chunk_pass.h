@@ -35,5 +35,10 @@ struct KdaPassArgs {
 // Bytes of one (chunk, head) record.
 uint64_t kda_pass_record_bytes();
 
+// Device address of the library's static record array on device `dev`
+// (KDA_STATIC_SCRATCH_BYTES bytes), looked up once per device with that
+// device current; null if the lookup failed.
+void* kda_pass_static_scratch(int dev);
+
 // Queues both passes on `stream`.
 hipError_t kda_chunk_pass_launch(const KdaPassArgs& args, hipStream_t stream);

@@ -43,11 +43,21 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kda_chunk_pass.h"
 #include "kda_decode.h"
 
 namespace {
+
+// Records of kda_prefill_chunks_static, for callers that cannot allocate:
+// one array per GPU, created when the library's code object is loaded on
+// that GPU and held until the process ends.  Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol): it
+// uses the device address that kda_pass_static_scratch looks up once per
+// device.
+constexpr uint64_t kStaticScratchBytes = KDA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 constexpr int kD = 128;
 constexpr int kW = 4;
@@ -658,6 +668,23 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_out_kernel(
 
 uint64_t kda_pass_record_bytes() {
   return static_cast<uint64_t>(kRecFloats) * sizeof(float);
+}
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+void* kda_pass_static_scratch(int dev) {
+  if (dev < 0 || dev >= kScratchDevices) return nullptr;
+  // once per device, with that device current (the caller's)
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess)
+      g_scratch_ptr[dev] = ptr;
+  });
+  return g_scratch_ptr[dev];
 }
 
 hipError_t kda_chunk_pass_launch(const KdaPassArgs& args, hipStream_t stream) {

@@ -1229,28 +1229,36 @@ uint64_t kda_prefill_chunks_workspace_bytes(const kda_dims* d,
 
 namespace {
 
+// With static_scratch the records go to the library's per-device array
+// (workspace and workspace_bytes are ignored); a request larger than the
+// array is KDA_ERR_TOO_LARGE.
 kda_status prefill_chunks_impl(
     const kda_dims* d, const int32_t* cu_seqlens, const int32_t* chunk_indices,
     const int64_t* chunk_offsets, int64_t max_chunks, const void* qkv,
     const float* conv_w, void* conv_state, float* rec_state, const float* g,
     const float* beta, const kda_gate_inputs* gi, const void* gate,
     const float* norm_w, const int32_t* state_idx, void* out, void* workspace,
-    uint64_t workspace_bytes, void* hip_stream) {
+    uint64_t workspace_bytes, void* hip_stream, bool static_scratch = false) {
   kda_status st = check_prefill_gates(d, gi);
   if (st != KDA_OK) return st;
   if (max_chunks < 0 ||
       max_chunks * static_cast<int64_t>(d->num_heads) > INT32_MAX ||
       static_cast<int64_t>(d->batch) * d->num_heads * 8 > INT32_MAX)
     return KDA_ERR_INVALID_ARG;
+  if (static_scratch &&
+      kda_prefill_chunks_workspace_bytes(d, max_chunks) >
+          KDA_STATIC_SCRATCH_BYTES)
+    return KDA_ERR_TOO_LARGE;
   if (d->batch == 0) return KDA_OK;
   if (!cu_seqlens || !chunk_offsets ||
-      (max_chunks > 0 && (!chunk_indices || !workspace)))
+      (max_chunks > 0 && (!chunk_indices || (!static_scratch && !workspace))))
     return KDA_ERR_INVALID_ARG;
-  if (workspace_bytes < kda_prefill_chunks_workspace_bytes(d, max_chunks))
+  if (!static_scratch &&
+      workspace_bytes < kda_prefill_chunks_workspace_bytes(d, max_chunks))
     return KDA_ERR_INVALID_ARG;
   if (!aligned16(cu_seqlens) || !aligned16(chunk_offsets) ||
       (chunk_indices && !aligned16(chunk_indices)) ||
-      (workspace && !aligned16(workspace)))
+      (!static_scratch && workspace && !aligned16(workspace)))
     return KDA_ERR_MISALIGNED;
   st = check_gate_ptrs(g, beta, gi);
   if (st != KDA_OK) return st;
@@ -1260,6 +1268,10 @@ kda_status prefill_chunks_impl(
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return KDA_ERR_DEVICE;
+  if (static_scratch) {
+    workspace = kda_pass_static_scratch(dev);
+    if (!workspace) return KDA_ERR_DEVICE;
+  }
   KdaPassArgs a{};
   a.qkv = static_cast<const uint16_t*>(qkv);
   a.conv_w = conv_w;
@@ -1304,6 +1316,18 @@ kda_status kda_prefill_chunks(const kda_dims* d, const int32_t* cu_seqlens,
                              max_chunks, qkv, conv_w, conv_state, rec_state, g,
                              beta, nullptr, gate, norm_w, state_idx, out,
                              workspace, workspace_bytes, hip_stream);
+}
+
+kda_status kda_prefill_chunks_static(
+    const kda_dims* d, const int32_t* cu_seqlens, const int32_t* chunk_indices,
+    const int64_t* chunk_offsets, int64_t max_chunks, const void* qkv,
+    const float* conv_w, void* conv_state, float* rec_state, const float* g,
+    const float* beta, const void* gate, const float* norm_w,
+    const int32_t* state_idx, void* out, void* hip_stream) {
+  return prefill_chunks_impl(d, cu_seqlens, chunk_indices, chunk_offsets,
+                             max_chunks, qkv, conv_w, conv_state, rec_state, g,
+                             beta, nullptr, gate, norm_w, state_idx, out,
+                             nullptr, 0, hip_stream, /*static_scratch=*/true);
 }
 
 kda_status kda_prefill_chunks_raw_gates(
@@ -1367,6 +1391,9 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_MISALIGNED: return "buffer not 16-byte aligned";
     case KDA_ERR_DEVICE: return "no gfx950 HIP device current";
     case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_TOO_LARGE:
+      return "request exceeds the library's static scratch "
+             "(KDA_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

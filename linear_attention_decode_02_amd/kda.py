@@ -28,7 +28,11 @@ HEAD_DIM = 128
 CONV_WIDTH = 4
 
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
-           3: "KDA_ERR_MISALIGNED", 4: "KDA_ERR_DEVICE", 5: "KDA_ERR_LAUNCH"}
+           3: "KDA_ERR_MISALIGNED", 4: "KDA_ERR_DEVICE", 5: "KDA_ERR_LAUNCH",
+           6: "KDA_ERR_TOO_LARGE"}
+KDA_ERR_TOO_LARGE = 6
+# bytes of the library's static record array (KDA_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 256 << 20
 
 
 class KdaError(RuntimeError):
@@ -88,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_chunks.argtypes = (
             [ctypes.POINTER(Dims), P, P, P, ctypes.c_int64] + [P] * 10 +
             [P, ctypes.c_uint64, P])
+        L.kda_prefill_chunks_static.restype = ctypes.c_int
+        L.kda_prefill_chunks_static.argtypes = (
+            [ctypes.POINTER(Dims), P, P, P, ctypes.c_int64] + [P] * 10 + [P])
         L.kda_prefill_chunked_raw_gates.restype = ctypes.c_int
         L.kda_prefill_chunked_raw_gates.argtypes = (
             [ctypes.POINTER(Dims)] + [P] * 5 + [ctypes.POINTER(GateInputs)]
@@ -382,6 +389,37 @@ def kda_prefill_chunks(cu_seqlens, chunk_indices, chunk_offsets,
             _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
             _ptr(state_idx), _ptr(out), _ptr(workspace),
             int(workspace.numel()), _stream(stream, qkv.device))
+    if rc != KDA_OK:
+        raise KdaError(rc, status_string(rc))
+
+
+def kda_prefill_chunks_static(cu_seqlens, chunk_indices, chunk_offsets,
+                              max_chunks: int, qkv, conv_w, conv_state,
+                              rec_state, g, beta, gate, norm_w, state_idx,
+                              out, *, norm: bool = True, eps: float = 1e-5,
+                              variants: int = 0, stream=None) -> None:
+    """kda_prefill_chunks without a workspace, for callers that cannot
+    allocate: the records go to the library's static per-GPU array
+    (max_chunks * H * record bytes <= STATIC_SCRATCH_BYTES, else
+    KdaError KDA_ERR_TOO_LARGE).  Calls that overlap on one GPU race on
+    that array.  Other arguments as kda_prefill_chunks."""
+    N, tokens, H, D, S = _prefill_common(cu_seqlens, qkv, conv_w, conv_state,
+                                         rec_state, gate, norm_w, state_idx,
+                                         out, norm, variants)
+    _check(chunk_offsets, "chunk_offsets", torch.int64, (N + 1,))
+    _check(chunk_indices, "chunk_indices", torch.int32,
+           (chunk_indices.shape[0], 2))
+    _check(g, "g", torch.float32, (tokens, H, D))
+    _check(beta, "beta", torch.float32, (tokens, H))
+    dims = Dims(N, H, D, CONV_WIDTH, S,
+                (KDA_OUTPUT_NORM if norm else 0) | int(variants), float(eps))
+    with torch.cuda.device(qkv.device):
+        rc = lib().kda_prefill_chunks_static(
+            ctypes.byref(dims), _ptr(cu_seqlens), _ptr(chunk_indices),
+            _ptr(chunk_offsets), int(max_chunks), _ptr(qkv), _ptr(conv_w),
+            _ptr(conv_state), _ptr(rec_state), _ptr(g), _ptr(beta),
+            _ptr(gate) if norm else None, _ptr(norm_w) if norm else None,
+            _ptr(state_idx), _ptr(out), _stream(stream, qkv.device))
     if rc != KDA_OK:
         raise KdaError(rc, status_string(rc))
 

@@ -36,8 +36,15 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, name), f"{name} declared but not exported"
 
 
+def test_static_scratch_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "kda_decode.h")).read()
+    m = re.search(r"#define KDA_STATIC_SCRATCH_BYTES \((\d+)ull << (\d+)\)",
+                  text)
+    assert m and int(m.group(1)) << int(m.group(2)) == kda.STATIC_SCRATCH_BYTES
+
+
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         s = kda.status_string(code)
         assert s and s != "unknown status"
     assert kda.status_string(99) == "unknown status"
@@ -234,6 +241,24 @@ def test_prefill_and_metadata_argument_checks():
     bad = list(args); bad[-3] = FAKE + 8                  # workspace align
     assert L.kda_prefill_chunks(ctypes.byref(d), *bad) == 3
     assert L.kda_prefill_chunks(ctypes.byref(dims(batch=0)), *args) == 0
+    # the static-scratch variant: no workspace arguments; a request past
+    # KDA_STATIC_SCRATCH_BYTES is refused before anything else is checked
+    sargs = [FAKE, FAKE, FAKE, 5] + [FAKE] * 10 + [None]
+    fs = L.kda_prefill_chunks_static
+    assert fs(ctypes.byref(d), *sargs) == 4
+    fit = kda.STATIC_SCRATCH_BYTES // (12 * 45120)
+    big = list(sargs); big[3] = fit
+    assert fs(ctypes.byref(d), *big) == 4
+    big[3] = fit + 1
+    assert fs(ctypes.byref(d), *big) == kda.KDA_ERR_TOO_LARGE
+    assert fs(ctypes.byref(dims(batch=0)), *big) == kda.KDA_ERR_TOO_LARGE
+    assert fs(ctypes.byref(dims(batch=0)), *sargs) == 0
+    bad = list(sargs); bad[3] = -1
+    assert fs(ctypes.byref(d), *bad) == 1
+    bad = list(sargs); bad[1] = None                      # chunk_indices
+    assert fs(ctypes.byref(d), *bad) == 1
+    bad = list(sargs); bad[2] = FAKE + 8                  # offsets align
+    assert fs(ctypes.byref(d), *bad) == 3
     assert L.kda_chunk_metadata(FAKE, 3, 64, FAKE, FAKE, None) == 4
     assert L.kda_chunk_metadata(FAKE, -1, 64, FAKE, FAKE, None) == 1
     assert L.kda_chunk_metadata(FAKE, 3, 0, FAKE, FAKE, None) == 1
