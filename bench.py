@@ -318,13 +318,13 @@ def main():
 
 def bench_serving(args, np, torch, kda, synth, copies=8, calls=64):
     """Per-call latency of kda_decode at the batch sizes of serving: 1..256
-    rows at 12 heads (the TP8 share of 96) and 48 heads, norm on, every row
-    live.  Each point is a graph of ``calls`` calls rotating ``copies``
+    rows at 12 heads (the TP8 share of 96), 24 and 48 heads, norm on, every
+    row live.  Each point is a graph of ``calls`` calls rotating ``copies``
     copies of the state pools (no reuse through the last-level cache),
     replayed 5 times; the median replay divided by ``calls``."""
     dev = torch.device("cuda:0")
     points = []
-    for H in (12, 48):
+    for H in (12, 24, 48):
         for B in (1, 8, 16, 24, 32, 64, 128, 256):
             w = synth.small(f"serving_b{B}_h{H}", batch=B, heads=H,
                             num_slots=B + 1, seed=5)
@@ -334,41 +334,69 @@ def bench_serving(args, np, torch, kda, synth, copies=8, calls=64):
             pools = [(t["conv_state"].clone(), t["rec_state"].clone())
                      for _ in range(copies)]
 
+            null_idx = torch.zeros_like(t["state_idx"])
+            tiles = [torch.ones(B * H, 128, 128, dtype=torch.float32,
+                                device=dev) for _ in range(copies)]
+
             def call(i):
                 cs, rs = pools[i % copies]
                 kda.kda_decode(t["qkv"], t["conv_w"], cs, rs, t["g"],
                                t["beta"], t["gate"], t["norm_w"],
                                t["state_idx"], out, norm=True, eps=w.eps)
 
-            side = torch.cuda.Stream(dev)
-            side.wait_stream(torch.cuda.current_stream(dev))
-            with torch.cuda.stream(side):
-                for i in range(copies):
-                    call(i)
-            torch.cuda.current_stream(dev).wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(calls):
-                    call(i)
-            g.replay()
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(5):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                g.replay()
-                e1.record()
+            def null_call(i):
+                # every row on the null slot: the launch and the zero
+                # outputs, no state traffic
+                cs, rs = pools[i % copies]
+                kda.kda_decode(t["qkv"], t["conv_w"], cs, rs, t["g"],
+                               t["beta"], t["gate"], t["norm_w"], null_idx,
+                               out, norm=True, eps=w.eps)
+
+            def rmw_call(i):
+                # the same state bytes read and rewritten with the kernel's
+                # tile mapping and nothing else (one 64 KiB tile per
+                # 1024-thread workgroup)
+                kda.state_stream_probe(tiles[i % copies], 16,
+                                       mode=kda.PROBE_RMW)
+
+            def graph_us(fn):
+                side = torch.cuda.Stream(dev)
+                side.wait_stream(torch.cuda.current_stream(dev))
+                with torch.cuda.stream(side):
+                    for i in range(copies):
+                        fn(i)
+                torch.cuda.current_stream(dev).wait_stream(side)
                 torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3 / calls)
-            us = float(np.median(ts))
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(calls):
+                        fn(i)
+                g.replay()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(5):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3 / calls)
+                del g
+                return float(np.median(ts))
+
+            us = graph_us(call)
+            us_null = graph_us(null_call)
+            us_rmw = graph_us(rmw_call)
             nbytes = kda.decode_bytes(B, H, B, True)
             points.append({"batch": B, "heads": H, "us_per_call": round(us, 2),
-                           "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)})
-            print(f"[serving] H={H} B={B}: {us:.2f} us", file=sys.stderr,
-                  flush=True)
-            del g, pools, t
+                           "GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                           "null_rows_us": round(us_null, 2),
+                           "state_rmw_us": round(us_rmw, 2)})
+            print(f"[serving] H={H} B={B}: {us:.2f} us (all rows null "
+                  f"{us_null:.2f}, bare state read-modify-write {us_rmw:.2f})",
+                  file=sys.stderr, flush=True)
+            del pools, t, tiles
     c16 = next(p for p in points if p["batch"] == 16 and p["heads"] == 12)
     line = {
         "metric": "KDA decode latency per call at serving batch sizes",
@@ -381,7 +409,11 @@ def bench_serving(args, np, torch, kda, synth, copies=8, calls=64):
                    "parallelism": "single-gpu"},
         "roofline": None, "cpu_baseline": None,
         "extra": {"points": points, "pool_copies": copies,
-                  "calls_per_graph": calls},
+                  "calls_per_graph": calls,
+                  "null_rows_us": "the same call with every row on the null "
+                                  "slot (launch + zero outputs)",
+                  "state_rmw_us": "kda_state_stream_probe read-modify-write "
+                                  "of the call's B*H state tiles, 16 waves"},
     }
     print(json.dumps(line), flush=True)
 
