@@ -311,13 +311,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
   f2 G = {0.f, 0.f};
   float gmax = 0.0f;
+  // in groups of the 4 tokens a wave owns: the wave keeps its own group's
+  // prefixes under a wave-uniform branch (no per-token select)
 #pragma unroll
-  for (int t = 0; t < kC; ++t) {
-    if (t < nv) G += gl[t];
-    gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+  for (int grp = 0; grp < 4; ++grp) {
+    f2 Gt[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (t == 4 * pw + u) Gu[u] = G;
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * grp + u;
+      if (t < nv) G += gl[t];
+      gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+      Gt[u] = G;
+    }
+    if (grp == pw) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Gu[u] = Gt[u];
+    }
   }
   // NaN counts as unsafe; every wave reaches the same verdict
   const bool unsafe = __any(!(gmax <= kSafeExp2));
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       }
   }
   if (l2) {
-    const float qscale = 1.0f / sqrtf(static_cast<float>(kD));
+    const float qscale = 0.08838834764831845f;  // D^-1/2
     float ss[8];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -361,8 +370,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     wave_sum8(ss);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float rq = 1.0f / sqrtf(ss[2 * u] + 1e-6f);
-      const float rk = 1.0f / sqrtf(ss[2 * u + 1] + 1e-6f);
+      const float rq = rsqrtf(ss[2 * u] + 1e-6f);
+      const float rk = rsqrtf(ss[2 * u + 1] + 1e-6f);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         y[u][0][e] = (y[u][0][e] * rq) * qscale;
@@ -650,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunk_out_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss += yv[j] * yv[j];
     ss = row_sum16(ss);
-    const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+    const float rs = rsqrtf(ss * (1.0f / kD) + p.eps);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t w2 = gate_raw[j >> 1];

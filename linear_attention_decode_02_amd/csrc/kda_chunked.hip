@@ -412,19 +412,27 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     f2 G = {0.f, 0.f};
     float gmax = 0.0f;
     {
+      // in groups of the 4 tokens a wave owns: the wave keeps its own
+      // group's prefixes under a wave-uniform branch (no per-token select)
 #pragma unroll
-      for (int t = 0; t < kC; ++t) {
-        const f2 gv = gl[t];
-        if (t < nv) G += gv;
-        gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+      for (int grp = 0; grp < 4; ++grp) {
+        f2 Gt[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (t == 4 * pw + u) Gu[u] = G;
+        for (int u = 0; u < 4; ++u) {
+          const int t = 4 * grp + u;
+          if (t < nv) G += gl[t];
+          gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+          Gt[u] = G;
+        }
+        if (grp == pw) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) Gu[u] = Gt[u];
+        }
       }
     }
     // NaN counts as unsafe; the same verdict in every prep wave
     const bool unsafe = __any(!(gmax <= kSafeExp2));
-    const float qscale = 1.0f / sqrtf(static_cast<float>(kD));
+    const float qscale = 0.08838834764831845f;  // D^-1/2
     // conv + SiLU of the 4 tokens (weights read once), then the 8 norm
     // reductions side by side, then the tables
     f2 cwv[3][kW];
@@ -470,8 +478,8 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       wave_sum8(ss);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float rq = 1.0f / sqrtf(ss[2 * u] + 1e-6f);
-        const float rk = 1.0f / sqrtf(ss[2 * u + 1] + 1e-6f);
+        const float rq = rsqrtf(ss[2 * u] + 1e-6f);
+        const float rk = rsqrtf(ss[2 * u + 1] + 1e-6f);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           y[u][0][e] = (y[u][0][e] * rq) * qscale;
@@ -661,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss += yv[j] * yv[j];
       ss = row_sum16(ss);  // the 16 lanes of token ot
-      const float rs = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+      const float rs = rsqrtf(ss * (1.0f / kD) + p.eps);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t w2 = gate_raw[j >> 1];
