@@ -24,26 +24,39 @@
 // summed with its own exponential, which is exact for any decay.
 //
 // Mapping: one 512-thread workgroup (8 waves) per (sequence, head), in two
-// roles that share each SIMD (waves w and w + 4 run on SIMD w):
+// roles that share each SIMD (waves w and w + 4 run on SIMD w), each role
+// in a loop of its own; three barriers per chunk hand the double-buffered
+// LDS tables over.
 //   * state waves 0-3 own value columns 32w .. 32w+31 of the [128 key,
 //     128 value] fp32 state, held for the whole sequence in registers in
-//     the accumulator layout of v_mfma_f32_16x16x4_f32 (lane l: column
-//     l%16, key rows 4(l/16) .. +3 of each 16-row block).  That layout is
-//     also the B operand of the next product once the summation index is
-//     permuted (key 16kb + 4(l/16) + j in step j), so the state never
-//     leaves the registers.  Per chunk and wave: 64 MFMAs for K~ S, 64 for
-//     Q~ S, 16 for the triangular solve and B Delta, 64 for the state
-//     update; every lane also solves for the row of the 16 x 16 inverse
-//     T = (I + diag(beta) A)^{-1} its operand needs, by backward
-//     substitution, in the shadow of its matrix products.
+//     the accumulator layout of the 16x16 MFMAs (lane l: column l%16, key
+//     rows 4(l/16) .. +3 of each 16-row block).  The products with the
+//     state run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with
+//     every fp32 operand split into three bf16 pieces hi + mid + lo (about
+//     24 significant bits) and the six products of pieces down to 2^-18 of
+//     the leading one accumulated in fp32: the result matches fp32
+//     products.  The state's accumulator layout is the B operand once the
+//     summation index is permuted (lane l holds keys 32P + 4(l/16) .. +3
+//     and 32P + 16 + 4(l/16) .. +3 of block P; the prep waves store the
+//     A-operand tables in that key order), so the state never leaves the
+//     registers.  Per chunk and wave: 48 MFMAs for K~ S and 48 for Q~ S,
+//     16 fp32 MFMAs for the triangular solve and B Delta, 48 for the
+//     state update (its k runs over 2 pieces x 4 tokens per lane group);
+//     every lane also solves for the row of T = (I + diag(beta) A)^{-1}
+//     its operand needs, by backward substitution.
 //   * prep waves 4-7 build the next chunk's operands meanwhile (4 tokens
 //     each): causal conv + SiLU from the raw bf16 inputs, q/k L2
 //     normalisation (wave-local: a wave holds all channels of its tokens),
-//     the cumulative decay, the decayed tables K~, Q~, K^, K e^{-G}, and
-//     then the A / B products on the matrix cores.
-// The tables are double-buffered in LDS; three barriers per chunk hand
-// them over.  The state waves also write the gated-RMSNorm outputs, one
-// 16-byte store per lane.
+//     the cumulative decay, the decayed tables K~, Q~, K^, K e^{-G} (split
+//     in three), and then the A / B products on the matrix cores.  Their
+//     inputs are loaded straight into registers a chunk ahead.
+// Why bf16 pieces and not fp32 MFMAs (v_mfma_f32_16x16x4_f32): while one
+// wave of a SIMD streams fp32 MFMAs, LDS reads and global loads of the
+// other wave on that SIMD return about 20 times later (measured on gfx950:
+// LDS 77 -> 2125 cycles, global 224 -> 4318); bf16 MFMA streams leave them
+// untouched, and 3-piece products take fewer matrix cycles besides (6 x 17
+// cycles per 32 keys against 8 x 32).  The state waves also write the
+// gated-RMSNorm outputs, one 16-byte store per lane.
 
 #include <hip/hip_runtime.h>
 
@@ -68,39 +81,44 @@ constexpr float kSafeExp2 = 80.0f * kLog2e;
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+// Split rows: a [16 token][128 key] table as three bf16 pieces hi + mid +
+// lo of every fp32 value (each the rounded remainder of the ones before:
+// together about 24 significant bits), in the operand order of
+// v_mfma_f32_16x16x32_bf16: per 32-key block P and lane group g, 12 dwords
+// -- hi of keys 32P+4g .. +3 and 32P+16+4g .. +3, then mid, then lo of
+// the same keys -- so each piece of one lane's operand is one aligned
+// 16-byte read.
+constexpr int kRowU = 4 * 4 * 12 + 4;  // dwords per split row (+ pad)
+// Split K^ rows: per key and group g of 4 tokens, 8 dwords: the pieces
+// [hi | mid] and [hi | lo] of the 4 tokens (two A operands of the state
+// update, k = 8 slots = 2 pieces x 4 tokens)
+constexpr int kKhU = 4 * 8 + 4;        // dwords per split K^ row (+ pad)
 
 // Operands of one chunk for the state waves (double-buffered).
 struct ChunkTables {
-  float qt[kC][kLd];    // q_t e^{G_t}
-  float kt[kC][kLd];    // k_t e^{G_t}
-  float v[kC][kLd];     // v_t
-  float khT[kD][kTd];   // k_t e^{G_last - G_t}, as [key][token]
-  float gam[kD];        // e^{G_last}
+  uint32_t qt[kC][kRowU];  // q_t e^{G_t}, split
+  uint32_t kt[kC][kRowU];  // k_t e^{G_t}, split
+  float v[kC][kLd];        // v_t
+  uint32_t kh[kD][kKhU];   // k_t e^{G_last - G_t} per key, split
+  float gam[kD];           // e^{G_last}
   float beta[kC];
 };
 
 struct alignas(16) Smem {
   ChunkTables tab[2];
-  float ki[kC][kLd];    // k_t e^{-G_t}; raw k on the exact path
+  uint32_t kis[kC][kRowU];  // k_t e^{-G_t}, split (matrix-core path)
+  float ki[kC][kLd];    // exact path: raw k
   float qraw[kC][kLd];  // exact path: q_t
   float graw[kC][kLd];  // exact path: cumulative log2 decay
   float part[4][kC][kC];  // A (keys 0-63, 64-127), B (same)
   float LT[kC][kTd];    // LT[s][t] = beta_t A_ts for s < t, else 0
   float B[kC][kTd];     // B_ts for s <= t, else 0
   float o[kC][kLd];     // this chunk's outputs before the norm
-  float cw[3][kW][kD];  // this head's conv weights
-  float cb[3][kD];      // raw gates: conv bias (zeros without one)
-  float dtb[kD];        // raw gates: this head's dt_bias
   float nw[kD];         // norm weight
-  uint32_t win[3][kW - 1][kD / 2];  // stored conv window, channel pairs
-  // raw inputs of the next chunk, copied in by the prep waves' LDS-direct
-  // loads: per prep wave its 7 input rows (3 parts, channel pairs), the
-  // chunk's 16 rows of g and its 16 betas
-  // (g and beta are read by every prep wave: two buffers by chunk parity;
-  // raw gates fill the first half of each g row with bf16 pairs)
-  uint32_t stage[4][7][3][kD / 2];
-  float gst[2][kC][kD];
-  float bst[2][64];
   int unsafe;           // exact path for the chunk being prepared
 };
 
@@ -114,6 +132,26 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {  // RNE
   return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, (__bf16)lo)) |
          (static_cast<uint32_t>(__builtin_bit_cast(unsigned short, (__bf16)hi))
           << 16);
+}
+// (a, b) in three bf16 pieces, each a pair (a in the low half): hi =
+// RNE(a, b), mid = RNE of the remainders, lo = RNE of what is left; the
+// sum of the pieces is within 2^-26 of each value (relative)
+struct Split3 {
+  uint32_t h, m, l;
+};
+__device__ __forceinline__ uint32_t bf2_(f2 v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2v));
+}
+__device__ __forceinline__ f2 bf2_val(uint32_t w) {
+  return f2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+}
+__device__ __forceinline__ Split3 split3(float a, float b) {
+  const f2 v = {a, b};
+  const uint32_t h = bf2_(v);
+  const f2 r1 = v - bf2_val(h);
+  const uint32_t m = bf2_(r1);
+  const f2 r2 = r1 - bf2_val(m);
+  return Split3{h, m, bf2_(r2)};
 }
 // 2^x on the transcendental unit (v_exp_f32)
 __device__ __forceinline__ float exp2_(float x) {
@@ -137,39 +175,6 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_<0x140>(v);
   return v;
 }
-// Global-memory pointers (address space 1).
-template <typename T>
-using gptr = __attribute__((address_space(1))) T*;
-// A wave-uniform global pointer made opaque to the compiler (readfirstlane
-// of both halves): loads become a scalar base plus a 32-bit lane offset
-// instead of a 64-bit address per lane.
-template <typename T>
-__device__ __forceinline__ gptr<const T> uniform_gptr(const T* ptr) {
-  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi =
-      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<gptr<const T>>((static_cast<uint64_t>(hi) << 32) |
-                                         lo);
-}
-// *(U*)(base + byte_off)
-template <typename U, typename T>
-__device__ __forceinline__ U load_at(gptr<const T> base, uint32_t byte_off) {
-  return *reinterpret_cast<gptr<const U>>(
-      reinterpret_cast<__attribute__((address_space(1))) const char*>(base) +
-      byte_off);
-}
-
-// One dword per lane from global memory straight into LDS: lane l's value
-// lands at dst[l] (dst wave-uniform).  Counted by vmcnt.
-__device__ __forceinline__ void load_lds(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
-}
-// s_waitcnt fields (gfx9 encoding): vmcnt 0 with the others at maximum,
-// and lgkmcnt 0 with the others at maximum
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
 // Eight wave sums side by side (independent DPP chains), each result in
 // every lane.
 __device__ __forceinline__ void wave_sum8(float (&v)[8]) {
@@ -193,6 +198,30 @@ __device__ __forceinline__ void wave_sum8(float (&v)[8]) {
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// D += A B with 8 bf16 per lane of each operand (16x16x32)
+__device__ __forceinline__ f4 mfma_bf(u4 a, u4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ u4 ld_u4(const uint32_t* p) {
+  return *reinterpret_cast<const u4*>(p);
+}
+// D += A B over 32 keys from split operands (hi, mid, lo at dwords 0, 4, 8
+// of each): the six products of pieces down to 2^-18 of the leading term
+__device__ __forceinline__ f4 mfma6_(u4 ah, u4 am, u4 al, u4 bh, u4 bm, u4 bl,
+                                    f4 acc) {
+  acc = mfma_bf(al, bh, acc);
+  acc = mfma_bf(ah, bl, acc);
+  acc = mfma_bf(am, bm, acc);
+  acc = mfma_bf(am, bh, acc);
+  acc = mfma_bf(ah, bm, acc);
+  return mfma_bf(ah, bh, acc);
+}
+__device__ __forceinline__ f4 mfma6(const uint32_t* a, const uint32_t* b,
+                                   f4 acc) {
+  return mfma6_(ld_u4(a), ld_u4(a + 4), ld_u4(a + 8), ld_u4(b), ld_u4(b + 4),
+                ld_u4(b + 8), acc);
 }
 __device__ __forceinline__ f4 ld4(const float* p) {
   return *reinterpret_cast<const f4*>(p);
@@ -251,161 +280,131 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   // state waves: the wave's 32 columns of the state, 2 blocks of 16
   float* st = p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD) +
               32 * pw + c;
-  f4 S[2][8];
   // output lanes: token tid/16 (of the 16), columns 8 (tid%16) .. +7
   const int ot = (tid & 255) >> 4;
   const int oc = 8 * (tid & 15);
-  if (state_wave) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[cb][kb][r] = st[(16 * kb + 4 * gq + r) * kD + 16 * cb];
-  } else {
-    // conv weights and the norm weight of this head into LDS
-    const int i = tid - 256;  // 0..255
-    for (int e = i; e < 3 * kW * kD; e += 256) {
-      const int pp = e / (kW * kD), t = (e / kD) % kW, k = e % kD;
-      sm.cw[pp][t][k] =
-          p.conv_w[(static_cast<int64_t>(pp) * kW + t) * C + col0 + k];
-    }
-    if (i < kD) sm.nw[i] = kNorm ? p.norm_w[i] : 0.0f;
-    if (kRaw) {
-      for (int e = i; e < 3 * kD; e += 256)
-        sm.cb[e / kD][e % kD] =
-            p.rg.conv_bias
-                ? p.rg.conv_bias[(e / kD) * static_cast<int64_t>(C) + col0 +
-                                 e % kD]
-                : 0.0f;
-      if (i < kD) sm.dtb[i] = p.rg.dt_bias[col0 + i];
-    }
-    // the stored window of channels 2 lane, 2 lane + 1 of each part
-    if (i < kD / 2) {
-#pragma unroll
-      for (int pp = 0; pp < 3; ++pp)
-#pragma unroll
-        for (int e = 0; e < kW - 1; ++e) {
-          const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * i;
-          uint32_t wv;
-          if (tap_major) {
-            wv = *reinterpret_cast<const uint32_t*>(
-                p.conv_state +
-                (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch);
-          } else {
-            const uint16_t* cs = p.conv_state +
-                                 (static_cast<int64_t>(slot) * C3 + ch) *
-                                     (kW - 1) + e;
-            wv = static_cast<uint32_t>(cs[0]) |
-                 (static_cast<uint32_t>(cs[kW - 1]) << 16);
-          }
-          sm.win[pp][e][i] = wv;
-        }
-    }
-  }
+  if (!state_wave && tid - 256 < kD)  // norm weight, read by the state waves
+    sm.nw[tid - 256] = kNorm ? p.norm_w[tid - 256] : 0.0f;
 
   // ---- prep stage 1 of chunk ci: conv, norms, decay, tables (wave-local)
-  // Requests chunk ci's raw inputs into the staging buffers (prep waves):
-  // wave pw the input rows of tokens 4pw-3 .. 4pw+3 (chunk-relative; rows
-  // before the sequence or past its end are clamped to valid rows and
-  // replaced or masked where used), rows 4pw .. 4pw+3 of g, and (wave 0)
-  // the betas.  The loads land while the wave works on the current chunk.
-  uint32_t rbeta = 0;  // raw gates: bf16 beta of token 4pw + lane (lane < 4)
-  auto stage_chunk = [&](int ci) {
-    const int c0 = ci * kC;
+  // Prep wave pw reads what it needs straight into registers, one chunk
+  // ahead (the loads are in flight while the wave works on the current
+  // chunk; the first use waits for them): for channels 2 lane, 2 lane + 1
+  // the input rows of tokens 4pw-3 .. 4pw+3 (chunk-relative; rows before
+  // the sequence or past its end are clamped to valid rows and replaced or
+  // masked where used), the gates of all 16 tokens and (lanes 0-3) the
+  // beta of token 4pw + lane.  No LDS on this path: while the state waves
+  // run their matrix products, LDS reads of the other wave on the SIMD
+  // wait far longer than register loads that were issued early.
+  uint32_t in_raw[3][7];
+  uint32_t in_g[kC][2];  // fp32 pair, or (raw gates) a bf16 pair in [0]
+  uint32_t in_b = 0;     // fp32 or (raw gates) bf16 bits
+  auto load_chunk = [&](int cj) {
+    const int c0 = cj * kC;
     const int nv = len - c0 < kC ? len - c0 : kC;
     const int64_t tok0 = tb + c0;
 #pragma unroll
     for (int u = 0; u < 7; ++u) {
       const int rel = 4 * pw - 3 + u;
       const int rr =
-          rel < 0 ? (ci > 0 ? rel : 0) : (rel < nv - 1 ? rel : nv - 1);
+          rel < 0 ? (cj > 0 ? rel : 0) : (rel < nv - 1 ? rel : nv - 1);
       const uint16_t* row = p.qkv + (tok0 + rr) * C3 + col0 + 2 * lane;
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp)
-        load_lds(row + pp * C, &sm.stage[pw][u][pp][0]);
+        in_raw[pp][u] = *reinterpret_cast<const uint32_t*>(row + pp * C);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = 4 * pw + u;
+    for (int t = 0; t < kC; ++t) {
       const int rr = t < nv - 1 ? t : nv - 1;
+      const int64_t e = ((tok0 + rr) * H + h) * kD + 2 * lane;
       if (kRaw) {
-        load_lds(p.rg.raw_g + ((tok0 + rr) * H + h) * kD + 2 * lane,
-                 &sm.gst[ci & 1][t][0]);
+        in_g[t][0] = *reinterpret_cast<const uint32_t*>(p.rg.raw_g + e);
       } else {
-        const float* row = p.g + ((tok0 + rr) * H + h) * kD + lane;
-        load_lds(row, &sm.gst[ci & 1][t][0]);
-        load_lds(row + 64, &sm.gst[ci & 1][t][64]);
+        const u2 v = *reinterpret_cast<const u2*>(p.g + e);
+        in_g[t][0] = v.x;
+        in_g[t][1] = v.y;
       }
     }
-    if (kRaw) {
-      if (lane < 4) {
-        const int t = 4 * pw + lane;
-        const int rr = t < nv - 1 ? t : nv - 1;
-        rbeta = p.rg.raw_beta[(tok0 + rr) * H + h];
-      }
-    } else if (pw == 0) {
-      const int rr = lane < nv - 1 ? lane : nv - 1;
-      load_lds(p.beta + (tok0 + rr) * H + h, &sm.bst[ci & 1][0]);
+    if (lane < 4) {
+      const int t = 4 * pw + lane;
+      const int rr = t < nv - 1 ? t : nv - 1;
+      const int64_t e = (tok0 + rr) * H + h;
+      in_b = kRaw ? static_cast<uint32_t>(p.rg.raw_beta[e])
+                  : __float_as_uint(p.beta[e]);
     }
   };
-
-  // Raw gates: once its own requests for chunk cj have landed, prep wave pw
-  // turns its 4 staged g rows (bf16 pairs of raw_g, keys 2 lane, 2 lane + 1
-  // in dword lane) into log2-unit decays in place, and its 4 betas into
-  // bst.  Each wave activates a quarter of the chunk; the barrier that
-  // follows publishes the rows to the other prep waves.
-  auto activate = [&](int cj) {
-    if (!kRaw || cj >= nchunks) return;
-    const f2 db = *reinterpret_cast<const f2*>(&sm.dtb[2 * lane]);
-    const float a_rate = __expf(p.rg.A_log[h]);
-    const float lb2 = p.rg.lower_bound * kLog2e;
-    float(*rows)[kD] = sm.gst[cj & 1];
-    uint32_t w[4];
+  // per-sequence constants of the prep waves, for channels 2 lane,
+  // 2 lane + 1: conv weights, conv bias and dt_bias (raw gates), and the
+  // stored conv window
+  f2 cwv[3][kW];
+  f2 cbv[3] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  f2 dtb = {0.f, 0.f};
+  uint32_t wv[3][kW - 1];
+  auto load_constants = [&]() {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w[u] = reinterpret_cast<const uint32_t*>(&rows[4 * pw + u][0])[lane];
-    // every lane's read is done before any lane's write lands over it
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    constexpr bool kB = kGate == kGateBounded;
+    for (int pp = 0; pp < 3; ++pp) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<f2*>(&rows[4 * pw + u][2 * lane]) =
-          f2{kda_gate2_from_raw<kB>(bf16_lo(w[u]) + db.x, a_rate, lb2),
-             kda_gate2_from_raw<kB>(bf16_hi(w[u]) + db.y, a_rate, lb2)};
-    if (lane < 4) sm.bst[cj & 1][4 * pw + lane] = sigmoid_(bf16_lo(rbeta));
+      for (int tap = 0; tap < kW; ++tap)
+        cwv[pp][tap] = *reinterpret_cast<const f2*>(
+            p.conv_w + (static_cast<int64_t>(pp) * kW + tap) * C + col0 +
+            2 * lane);
+      if (kRaw && p.rg.conv_bias)
+        cbv[pp] = *reinterpret_cast<const f2*>(
+            p.rg.conv_bias + static_cast<int64_t>(pp) * C + col0 + 2 * lane);
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e) {
+        const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
+        if (tap_major) {
+          wv[pp][e] = *reinterpret_cast<const uint32_t*>(
+              p.conv_state +
+              (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch);
+        } else {
+          const uint16_t* cs =
+              p.conv_state + (static_cast<int64_t>(slot) * C3 + ch) * (kW - 1) +
+              e;
+          wv[pp][e] = static_cast<uint32_t>(cs[0]) |
+                      (static_cast<uint32_t>(cs[kW - 1]) << 16);
+        }
+      }
+    }
+    if (kRaw)
+      dtb = *reinterpret_cast<const f2*>(p.rg.dt_bias + col0 + 2 * lane);
   };
 
   auto prep_tables = [&](int ci) {
     ChunkTables& T = sm.tab[ci & 1];
     const int c0 = ci * kC;
     const int nv = len - c0 < kC ? len - c0 : kC;
-    // raw[pp][u]: input of token 4pw - 3 + u (chunk-relative) for channels
-    // 2 lane, 2 lane + 1 of part pp (staged during the previous chunk)
+    // this chunk's inputs (loaded a chunk ago), then the next chunk's loads
     uint32_t raw[3][7];
 #pragma unroll
     for (int u = 0; u < 7; ++u)
 #pragma unroll
-      for (int pp = 0; pp < 3; ++pp) raw[pp][u] = sm.stage[pw][u][pp][lane];
-    // per-token decays of keys 2 lane, 2 lane + 1 in log2 units (raw
-    // gates: activated in place by activate())
+      for (int pp = 0; pp < 3; ++pp) raw[pp][u] = in_raw[pp][u];
+    // per-token decays of keys 2 lane, 2 lane + 1 in log2 units
     f2 gl[kC];
+    if (kRaw) {
+      const float a_rate = __expf(p.rg.A_log[h]);
+      const float lb2 = p.rg.lower_bound * kLog2e;
+      constexpr bool kB = kGate == kGateBounded;
 #pragma unroll
-    for (int t = 0; t < kC; ++t) {
-      gl[t] = *reinterpret_cast<const f2*>(&sm.gst[ci & 1][t][2 * lane]);
-      if (!kRaw) gl[t] *= kLog2e;
-      gl[t] = kda_decay_floor2(gl[t]);
+      for (int t = 0; t < kC; ++t)
+        gl[t] = f2{kda_gate2_from_raw<kB>(bf16_lo(in_g[t][0]) + dtb.x, a_rate,
+                                          lb2),
+                   kda_gate2_from_raw<kB>(bf16_hi(in_g[t][0]) + dtb.y, a_rate,
+                                          lb2)};
+    } else {
+#pragma unroll
+      for (int t = 0; t < kC; ++t)
+        gl[t] = f2{__uint_as_float(in_g[t][0]), __uint_as_float(in_g[t][1])} *
+                kLog2e;
     }
-    const float bt = lane < 4 ? sm.bst[ci & 1][4 * pw + lane] : 0.0f;
-    // the staging buffers are free again: request the next chunk
-    wait_lds();
-    if (ci + 1 < nchunks) stage_chunk(ci + 1);
-    uint32_t wv[3][kW - 1];
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp)
-#pragma unroll
-      for (int e = 0; e < kW - 1; ++e) wv[pp][e] = sm.win[pp][e][lane];
+    for (int t = 0; t < kC; ++t) gl[t] = kda_decay_floor2(gl[t]);
+    const float bt =
+        lane < 4 ? (kRaw ? sigmoid_(bf16_lo(in_b)) : __uint_as_float(in_b))
+                 : 0.0f;
+    if (ci + 1 < nchunks) load_chunk(ci + 1);
     // cumulative decay of keys 2 lane, 2 lane + 1 (log2 units) over the
     // whole chunk; the values at this wave's 4 tokens and at the end
     f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
@@ -435,15 +434,6 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     const float qscale = 0.08838834764831845f;  // D^-1/2
     // conv + SiLU of the 4 tokens (weights read once), then the 8 norm
     // reductions side by side, then the tables
-    f2 cwv[3][kW];
-    f2 cbv[3] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-#pragma unroll
-    for (int pp = 0; pp < 3; ++pp) {
-#pragma unroll
-      for (int tap = 0; tap < kW; ++tap)
-        cwv[pp][tap] = *reinterpret_cast<const f2*>(&sm.cw[pp][tap][2 * lane]);
-      if (kRaw) cbv[pp] = *reinterpret_cast<const f2*>(&sm.cb[pp][2 * lane]);
-    }
     float y[4][3][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -457,11 +447,14 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
           for (int tap = 0; tap < kW; ++tap) {
             // with the update a token sees the inputs before it (the stored
             // window before the sequence); without it, the stored window
-            const int rin = 4 * pw + u - (kW - 1) + tap;
+            // (only wave 0 reaches before the chunk: index rin0 = rin there,
+            // a constant, so the window stays in registers)
+            const int rin0 = u - (kW - 1) + tap;
+            const bool before = rin0 < 0 && pw == 0 && ci == 0;
             const uint32_t w2 =
                 tap == kW - 1 ? raw[pp][u + tap]
-                : conv_update ? (rin < 0 && ci == 0 ? wv[pp][(kW - 1) + rin]
-                                                    : raw[pp][u + tap])
+                : conv_update ? (before ? wv[pp][(kW - 1) + (rin0 < 0 ? rin0 : 0)]
+                                        : raw[pp][u + tap])
                               : wv[pp][tap];
             a += cwv[pp][tap][e] * (e ? bf16_hi(w2) : bf16_lo(w2));
           }
@@ -487,20 +480,30 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
         }
       }
     }
+    // dword of keys 2 lane, 2 lane + 1 in a split row (hi; mid at + 4, lo
+    // at + 8)
+    const int m = lane & 15;
+    const int pos = (4 * (lane >> 4) + ((m & 7) >> 1)) * 12 +
+                    (m >= 8 ? 2 : 0) + (m & 1);
+    auto put3 = [&](uint32_t* row, float a, float b) {
+      const Split3 x = split3(a, b);
+      row[pos] = x.h;
+      row[pos + 4] = x.m;
+      row[pos + 8] = x.l;
+    };
+    f2 khv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = 4 * pw + u;
       const f2 ee = {exp2_(Gu[u].x), exp2_(Gu[u].y)};
-      *reinterpret_cast<f2*>(&T.qt[t][2 * lane]) =
-          f2{y[u][0][0] * ee.x, y[u][0][1] * ee.y};
-      *reinterpret_cast<f2*>(&T.kt[t][2 * lane]) =
-          f2{y[u][1][0] * ee.x, y[u][1][1] * ee.y};
+      put3(T.qt[t], y[u][0][0] * ee.x, y[u][0][1] * ee.y);
+      put3(T.kt[t], y[u][1][0] * ee.x, y[u][1][1] * ee.y);
       *reinterpret_cast<f2*>(&T.v[t][2 * lane]) = f2{y[u][2][0], y[u][2][1]};
-      T.khT[2 * lane][t] = y[u][1][0] * exp2_(G.x - Gu[u].x);
-      T.khT[2 * lane + 1][t] = y[u][1][1] * exp2_(G.y - Gu[u].y);
+      khv[u] = f2{y[u][1][0] * exp2_(G.x - Gu[u].x),
+                  y[u][1][1] * exp2_(G.y - Gu[u].y)};
       if (!unsafe) {
-        *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) =
-            f2{y[u][1][0] * exp2_(-Gu[u].x), y[u][1][1] * exp2_(-Gu[u].y)};
+        put3(sm.kis[t], y[u][1][0] * exp2_(-Gu[u].x),
+             y[u][1][1] * exp2_(-Gu[u].y));
       } else {
         *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) =
             f2{y[u][1][0], y[u][1][1]};
@@ -508,6 +511,16 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
             f2{y[u][0][0], y[u][0][1]};
         *reinterpret_cast<f2*>(&sm.graw[t][2 * lane]) = Gu[u];
       }
+    }
+    // K^ of keys 2 lane, 2 lane + 1 for this wave's 4 tokens: two 16-byte
+    // stores per key
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const Split3 a = split3(khv[0][e], khv[1][e]);
+      const Split3 b = split3(khv[2][e], khv[3][e]);
+      u4* dst = reinterpret_cast<u4*>(&T.kh[2 * lane + e][8 * pw]);
+      dst[0] = u4{a.h, b.h, a.m, b.m};
+      dst[1] = u4{a.h, b.h, a.l, b.l};
     }
     if (pw == 0) {
       *reinterpret_cast<f2*>(&T.gam[2 * lane]) = f2{exp2_(G.x), exp2_(G.y)};
@@ -524,15 +537,12 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     const ChunkTables& T = sm.tab[ci & 1];
     if (!sm.unsafe) {
       // wave 4: A over keys 0-63, 5: A over 64-127, 6 / 7: B likewise
-      const float(*src)[kLd] = pw < 2 ? T.kt : T.qt;
+      const uint32_t(*src)[kRowU] = pw < 2 ? T.kt : T.qt;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int key = 64 * (pw & 1) + 16 * kb + 4 * gq;
-        const f4 a = ld4(&src[c][key]);
-        const f4 b = ld4(&sm.ki[c][key]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma(a[j], b[j], acc);
+      for (int q = 0; q < 2; ++q) {
+        const int off = (4 * (2 * (pw & 1) + q) + gq) * 12;
+        acc = mfma6(&src[c][off], &sm.kis[c][off], acc);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.part[pw][4 * gq + r][c] = acc[r];
@@ -566,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   };
 
   // ---- state stage: one chunk through the recurrence ---------------------
-  auto state_chunk = [&](int ci) {
+  auto state_chunk = [&](int ci, f4 (&S)[2][8]) {
     const ChunkTables& T = sm.tab[ci & 1];
     f4 ks[2], o[2];
 #pragma unroll
@@ -574,27 +584,29 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       ks[cb] = f4{0.f, 0.f, 0.f, 0.f};
       o[cb] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    // operands one key block ahead; the scheduling fence keeps the
-    // compiler from hoisting all of them (register pressure)
-    f4 ak = ld4(&T.kt[c][4 * gq]);
-    f4 aq = ld4(&T.qt[c][4 * gq]);
+    // per 32-key block P: the split K~ and Q~ rows (A operands) and the
+    // state split in place (B operand: lane l holds S rows 32P + 4(l/16)
+    // .. +3 and 32P + 16 + 4(l/16) .. +3 of its column, the order the split
+    // rows use)
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      f4 akn = ak, aqn = aq;
-      if (kb < 7) {
-        akn = ld4(&T.kt[c][16 * kb + 16 + 4 * gq]);
-        aqn = ld4(&T.qt[c][16 * kb + 16 + 4 * gq]);
+    for (int P = 0; P < 4; ++P) {
+      const int off = (4 * P + gq) * 12;
+      const u4 kh_ = ld_u4(&T.kt[c][off]), km_ = ld_u4(&T.kt[c][off + 4]),
+               kl_ = ld_u4(&T.kt[c][off + 8]);
+      const u4 qh_ = ld_u4(&T.qt[c][off]), qm_ = ld_u4(&T.qt[c][off + 4]),
+               ql_ = ld_u4(&T.qt[c][off + 8]);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const Split3 s0 = split3(S[cb][2 * P][0], S[cb][2 * P][1]);
+        const Split3 s1 = split3(S[cb][2 * P][2], S[cb][2 * P][3]);
+        const Split3 s2 = split3(S[cb][2 * P + 1][0], S[cb][2 * P + 1][1]);
+        const Split3 s3 = split3(S[cb][2 * P + 1][2], S[cb][2 * P + 1][3]);
+        const u4 sh = {s0.h, s1.h, s2.h, s3.h};
+        const u4 sm_ = {s0.m, s1.m, s2.m, s3.m};
+        const u4 sl = {s0.l, s1.l, s2.l, s3.l};
+        ks[cb] = mfma6_(kh_, km_, kl_, sh, sm_, sl, ks[cb]);
+        o[cb] = mfma6_(qh_, qm_, ql_, sh, sm_, sl, o[cb]);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          ks[cb] = mfma(ak[j], S[cb][kb][j], ks[cb]);
-          o[cb] = mfma(aq[j], S[cb][kb][j], o[cb]);
-        }
-      ak = akn;
-      aq = aqn;
-      __builtin_amdgcn_sched_barrier(0);
     }
     // row c of T: (I + L)^T y = e_c, backward
     float y[kC];
@@ -635,25 +647,31 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.o[4 * gq + r][col] = o[cb][r];
     }
-    f4 gm = ld4(&T.gam[4 * gq]);
-    f4 ah = ld4(&T.khT[c][4 * gq]);
+    // state update over the 16 tokens (k = 2 pieces x 4 tokens per lane
+    // group): [K^hi | K^mid] against [Dhi; Dhi] and [Dmid; Dmid], and
+    // [K^hi | K^lo] against [Dlo; Dhi] -- the six products of pieces down
+    // to 2^-18 of the leading term
+    u4 dh[2], dm[2], dx[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const Split3 d01 = split3(dl[cb][0], dl[cb][1]);
+      const Split3 d23 = split3(dl[cb][2], dl[cb][3]);
+      dh[cb] = u4{d01.h, d23.h, d01.h, d23.h};
+      dm[cb] = u4{d01.m, d23.m, d01.m, d23.m};
+      dx[cb] = u4{d01.l, d23.l, d01.h, d23.h};
+    }
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      f4 gmn = gm, ahn = ah;
-      if (kb < 7) {
-        gmn = ld4(&T.gam[16 * kb + 16 + 4 * gq]);
-        ahn = ld4(&T.khT[16 * kb + 16 + c][4 * gq]);
-      }
+      const f4 gm = ld4(&T.gam[16 * kb + 4 * gq]);
+      const u4 ahm = ld_u4(&T.kh[16 * kb + c][8 * gq]);
+      const u4 ahl = ld_u4(&T.kh[16 * kb + c][8 * gq + 4]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         S[cb][kb] *= gm;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          S[cb][kb] = mfma(ah[j], dl[cb][j], S[cb][kb]);
+        S[cb][kb] = mfma_bf(ahl, dx[cb], S[cb][kb]);
+        S[cb][kb] = mfma_bf(ahm, dm[cb], S[cb][kb]);
+        S[cb][kb] = mfma_bf(ahm, dh[cb], S[cb][kb]);
       }
-      gm = gmn;
-      ah = ahn;
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -686,55 +704,36 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   };
 
   // ---- the pipeline --------------------------------------------------------
-  if (!state_wave) {
-    stage_chunk(0);
-    wait_vmem();
-  }
-  __syncthreads();  // conv and norm weights, the first chunk's inputs
-  if (kRaw) {       // (activate reads the dt_bias row written above)
-    if (!state_wave) activate(0);
-    __syncthreads();
-  }
-  if (!state_wave) prep_tables(0);
-  __syncthreads();
-  if (!state_wave) prep_gram(0);
-  __syncthreads();
-  if (!state_wave) {
-    prep_reduce(0);
-    wait_vmem();
-    activate(1);
-  }
-  __syncthreads();
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const bool more = ci + 1 < nchunks;
-    u4 gate_raw = {0u, 0u, 0u, 0u};
-    if (state_wave) {
+  // Each role runs a loop of its own (the state lives only in the state
+  // waves' loop, so the prep code does not carry its registers); both meet
+  // at the same barriers: 3 before the first chunk, then 3 per chunk.
+  if (state_wave) {
+    f4 S[2][8];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[cb][kb][r] = st[(16 * kb + 4 * gq + r) * kD + 16 * cb];
+    __syncthreads();  // first chunk's tables (and the norm weight)
+    __syncthreads();  // its partial products
+    __syncthreads();  // its A and B
+    for (int ci = 0; ci < nchunks; ++ci) {
+      u4 gate_raw = {0u, 0u, 0u, 0u};
       if (kNorm) {
         const int nv = len - ci * kC < kC ? len - ci * kC : kC;
         const int rr = ot < nv - 1 ? ot : nv - 1;
         gate_raw = *reinterpret_cast<const u4*>(
             p.gate + (tb + ci * kC + rr) * C + col0 + oc);
       }
-      state_chunk(ci);
-    } else if (more) {
-      prep_tables(ci + 1);
-    }
-    __syncthreads();
-    if (state_wave)
+      state_chunk(ci, S);
+      __syncthreads();  // outputs in sm.o; next chunk's tables ready
       emit(ci, gate_raw);
-    else if (more)
-      prep_gram(ci + 1);
-    __syncthreads();
-    if (!state_wave && more) prep_reduce(ci + 1);
-    if (!state_wave) {
-      wait_vmem();  // the staged inputs of the chunk after the next
-      activate(ci + 2);
+      __syncthreads();  // next chunk's partial products
+      __syncthreads();  // next chunk's A and B
     }
-    __syncthreads();
-  }
-
-  // ---- write back the state and the conv window ---------------------------
-  if (state_wave) {
+    // ---- write back the state ----
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -742,7 +741,27 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           st[(16 * kb + 4 * gq + r) * kD + 16 * cb] = S[cb][kb][r];
+  } else {
+    load_chunk(0);
+    load_constants();
+    prep_tables(0);
+    __syncthreads();
+    prep_gram(0);
+    __syncthreads();
+    prep_reduce(0);
+    __syncthreads();
+    for (int ci = 0; ci < nchunks; ++ci) {
+      const bool more = ci + 1 < nchunks;
+      if (more) prep_tables(ci + 1);
+      __syncthreads();
+      if (more) prep_gram(ci + 1);
+      __syncthreads();
+      if (more) prep_reduce(ci + 1);
+      __syncthreads();
+    }
   }
+
+  // ---- write back the conv window -----------------------------------------
   if (conv_update && tid < 3 * kD) {
     // new window = the last W-1 inputs of (stored window ++ tokens)
     const int64_t ch =
