@@ -175,6 +175,29 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_<0x140>(v);
   return v;
 }
+// Global-memory pointers (address space 1).
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+// A wave-uniform address made opaque to the compiler (readfirstlane of both
+// halves): loads from it become a scalar base plus a 32-bit lane offset
+// instead of a 64-bit address per lane.
+__device__ __forceinline__ gptr<const char> uniform_gptr(const void* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<gptr<const char>>((static_cast<uint64_t>(hi) << 32) |
+                                            lo);
+}
+// *(U*)(base + byte_off); the offset is made opaque where the load is, so
+// the 32-bit lane offset is not widened ahead of the loop and the load
+// keeps the scalar-base form
+template <typename U>
+__device__ __forceinline__ U load_at(gptr<const char> base, uint32_t byte_off) {
+  asm volatile("" : "+v"(byte_off));
+  return *reinterpret_cast<gptr<const U>>(base + byte_off);
+}
+
 // Eight wave sums side by side (independent DPP chains), each result in
 // every lane.
 __device__ __forceinline__ void wave_sum8(float (&v)[8]) {
@@ -299,28 +322,39 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   uint32_t in_raw[3][7];
   uint32_t in_g[kC][2];  // fp32 pair, or (raw gates) a bf16 pair in [0]
   uint32_t in_b = 0;     // fp32 or (raw gates) bf16 bits
+  // this lane's byte offsets in an input row (parts q, k, v) and a gate row
+  const uint32_t off_raw = 4 * lane;
+  const uint32_t off_part = 2 * static_cast<uint32_t>(C);
+  const uint32_t off_g = (kRaw ? 4 : 8) * lane;
   auto load_chunk = [&](int cj) {
     const int c0 = cj * kC;
     const int nv = len - c0 < kC ? len - c0 : kC;
     const int64_t tok0 = tb + c0;
+    // row addresses are wave-uniform (scalar); lanes add 32-bit offsets
+    const char* q0 = reinterpret_cast<const char*>(p.qkv + tok0 * C3 + col0);
+    const int qrow = 2 * C3;  // bytes per token row (rows differ by < 16)
 #pragma unroll
     for (int u = 0; u < 7; ++u) {
       const int rel = 4 * pw - 3 + u;
       const int rr =
           rel < 0 ? (cj > 0 ? rel : 0) : (rel < nv - 1 ? rel : nv - 1);
-      const uint16_t* row = p.qkv + (tok0 + rr) * C3 + col0 + 2 * lane;
+      const gptr<const char> row = uniform_gptr(q0 + rr * qrow);  // 32-bit
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp)
-        in_raw[pp][u] = *reinterpret_cast<const uint32_t*>(row + pp * C);
+        in_raw[pp][u] = load_at<uint32_t>(row, off_raw + pp * off_part);
     }
+    const int64_t g0 = (tok0 * H + h) * kD;
+    const char* gb = kRaw ? reinterpret_cast<const char*>(p.rg.raw_g + g0)
+                          : reinterpret_cast<const char*>(p.g + g0);
+    const int grow = H * kD * (kRaw ? 2 : 4);
 #pragma unroll
     for (int t = 0; t < kC; ++t) {
       const int rr = t < nv - 1 ? t : nv - 1;
-      const int64_t e = ((tok0 + rr) * H + h) * kD + 2 * lane;
+      const gptr<const char> row = uniform_gptr(gb + rr * grow);
       if (kRaw) {
-        in_g[t][0] = *reinterpret_cast<const uint32_t*>(p.rg.raw_g + e);
+        in_g[t][0] = load_at<uint32_t>(row, off_g);
       } else {
-        const u2 v = *reinterpret_cast<const u2*>(p.g + e);
+        const u2 v = load_at<u2>(row, off_g);
         in_g[t][0] = v.x;
         in_g[t][1] = v.y;
       }
@@ -375,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     ChunkTables& T = sm.tab[ci & 1];
     const int c0 = ci * kC;
     const int nv = len - c0 < kC ? len - c0 : kC;
-    // this chunk's inputs (loaded a chunk ago), then the next chunk's loads
+    // this chunk's inputs (loaded a chunk ago)
     uint32_t raw[3][7];
 #pragma unroll
     for (int u = 0; u < 7; ++u)
@@ -404,7 +438,6 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     const float bt =
         lane < 4 ? (kRaw ? sigmoid_(bf16_lo(in_b)) : __uint_as_float(in_b))
                  : 0.0f;
-    if (ci + 1 < nchunks) load_chunk(ci + 1);
     // cumulative decay of keys 2 lane, 2 lane + 1 (log2 units) over the
     // whole chunk; the values at this wave's 4 tokens and at the end
     f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
@@ -461,6 +494,10 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
           y[u][pp][e] = valid ? a * sigmoid_(a) : 0.0f;
         }
     }
+    // the inputs are consumed: the next chunk's loads reuse their registers
+    // (unconditional -- the last chunk loads itself again -- so no copy
+    // has to wait for them)
+    load_chunk(ci + 1 < nchunks ? ci + 1 : ci);
     if (l2) {
       float ss[8];
 #pragma unroll
@@ -750,15 +787,18 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     __syncthreads();
     prep_reduce(0);
     __syncthreads();
-    for (int ci = 0; ci < nchunks; ++ci) {
-      const bool more = ci + 1 < nchunks;
-      if (more) prep_tables(ci + 1);
+    for (int ci = 0; ci + 1 < nchunks; ++ci) {
+      prep_tables(ci + 1);
       __syncthreads();
-      if (more) prep_gram(ci + 1);
+      prep_gram(ci + 1);
       __syncthreads();
-      if (more) prep_reduce(ci + 1);
+      prep_reduce(ci + 1);
       __syncthreads();
     }
+    // the last chunk: nothing left to prepare
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
   }
 
   // ---- write back the conv window -----------------------------------------
