@@ -35,10 +35,19 @@ HBM_PEAK_GBS = 8000.0
 FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 # kda_decode_tokens runs the chunked matrix-core form from this many tokens
 CHUNKED_MIN_TOKENS = 29
-# fp32 MFMA flop per (16-token chunk, head) of the chunked form: K~S, Q~S
+# fp32 matrix flop per (16-token chunk, head) of the chunked form: K~S, Q~S
 # and the state update (3 x 2*16*128*128), A, B, the solve and B Delta
-# (4 x 2*16*16*128)
+# (4 x 2*16*16*128).  The kernel reaches fp32 precision on the bf16 matrix
+# cores (three bf16 pieces per operand, six piece products), so this
+# fp32-equivalent work is priced against the fp32 matrix peak; the bf16
+# instructions it executes per (chunk, head) are counted beside it.
 CHUNK_MFMA_FLOP = 3 * 2 * 16 * 128 * 128 + 4 * 2 * 16 * 16 * 128
+BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+# executed per (chunk, head): 4 state waves x (48 + 48 + 48) and 4 prep
+# waves x 12 v_mfma_f32_16x16x32_bf16 (16384 flop each), 4 x 16
+# v_mfma_f32_16x16x4_f32 (2048 flop each)
+CHUNK_BF16_MFMA = 4 * 144 + 4 * 12
+CHUNK_FP32_MFMA = 4 * 16
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_decode_02_amd", "csrc",
                           "kda_decode.hip")
 KERNEL_END_MARK = "// Several tokens per row in one launch"
@@ -585,7 +594,13 @@ def bench_prefill(args, np, torch, kda, synth):
                      "traffic": None},
         "cpu_baseline": cpu,
         "extra": {"kernel_us": round(kern * 1e6, 2),
-                  "path": "kda_prefill_chunked (fp32 MFMA, 16-token chunks)",
+                  "path": "kda_prefill_chunked (16-token chunks; fp32 "
+                          "products as 3-piece bf16 on the matrix cores)",
+                  "bf16_mfma_tflops_executed": round(
+                      chunks * H * CHUNK_BF16_MFMA * 16384 / kern / 1e12, 1),
+                  "bf16_mfma_frac_executed": round(
+                      chunks * H * CHUNK_BF16_MFMA * 16384 / kern / 1e12
+                      / BF16_MFMA_TFLOPS, 4),
                   "chunk_heads": chunks * H,
                   "mfma_flop_per_chunk_head": flop_chunk,
                   "longest_sequence_chunks": int((lens.max() + 15) // 16),
