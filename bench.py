@@ -34,7 +34,7 @@ METRIC = "KDA decode (seq*head) updates/sec + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 # kda_decode_tokens runs the chunked matrix-core form from this many tokens
-CHUNKED_MIN_TOKENS = 29
+CHUNKED_MIN_TOKENS = 11
 # fp32 matrix flop per (16-token chunk, head) of the chunked form: K~S, Q~S
 # and the state update (3 x 2*16*128*128), A, B, the solve and B Delta
 # (4 x 2*16*16*128).  The kernel reaches fp32 precision on the bf16 matrix

@@ -26,7 +26,14 @@
 // Mapping: one 512-thread workgroup (8 waves) per (sequence, head), in two
 // roles that share each SIMD (waves w and w + 4 run on SIMD w), each role
 // in a loop of its own; three barriers per chunk hand the double-buffered
-// LDS tables over.
+// LDS tables over.  Rows mode (tokens_per_row, no cu_seqlens: the
+// multi-token decode, rows of up to 32 tokens): a workgroup takes a run of
+// up to 64 (row, head) segments in head-major order, about one workgroup
+// per CU, and pipelines their chunks as one stream -- the prep waves prepare the next segment's
+// first chunk while the state waves finish the current one, whose state
+// goes back to memory right after its update while the next segment's
+// state loads into the same registers (16-byte rows, a quad transpose
+// away from the accumulator layout).
 //   * state waves 0-3 own value columns 32w .. 32w+31 of the [128 key,
 //     128 value] fp32 state, held for the whole sequence in registers in
 //     the accumulator layout of the 16x16 MFMAs (lane l: column l%16, key
@@ -49,7 +56,9 @@
 //     normalisation (wave-local: a wave holds all channels of its tokens),
 //     the cumulative decay, the decayed tables K~, Q~, K^, K e^{-G} (split
 //     in three), and then the A / B products on the matrix cores.  Their
-//     inputs are loaded straight into registers a chunk ahead.
+//     inputs are loaded straight into registers a chunk ahead.  At a
+//     segment's last chunk the prep wave holding its last three input rows
+//     writes them as the new stored conv window.
 // Why bf16 pieces and not fp32 MFMAs (v_mfma_f32_16x16x4_f32): while one
 // wave of a SIMD streams fp32 MFMAs, LDS reads and global loads of the
 // other wave on that SIMD return about 20 times later (measured on gfx950:
@@ -72,6 +81,8 @@ constexpr int kD = 128;      // head dim (key = value)
 constexpr int kW = 4;        // conv width
 constexpr int kC = 16;       // tokens per chunk (one MFMA row block)
 constexpr int kThreads = 512;
+// stream mode: at most this many (row, head) segments per workgroup
+constexpr int kMaxSegs = KDA_CHUNKED_MAX_SEGS;
 constexpr int kLd = kD + 4;  // padded row of [kC][kD] tables (floats)
 constexpr int kTd = kC + 4;  // padded row of [kD][kC] and [kC][kC] tables
 constexpr float kLog2e = 1.44269504088896341f;
@@ -120,6 +131,8 @@ struct alignas(16) Smem {
   float o[kC][kLd];     // this chunk's outputs before the norm
   float nw[kD];         // norm weight
   int unsafe;           // exact path for the chunk being prepared
+  int seg_count;        // stream mode: this workgroup's live segments
+  int seg_list[kMaxSegs];
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) {
@@ -167,6 +180,19 @@ __device__ __forceinline__ float dpp_(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
                                          0xF, 0xF, false));
+}
+// 4x4 transpose across the 4 lanes of each quad: lane b's element r goes
+// to lane r's element b (two butterfly stages: lane bit 0 with element
+// bit 0, then bit 1 with bit 1).  odd1 / odd2: bit 0 / bit 1 of the lane.
+__device__ __forceinline__ f4 quad_transpose(f4 x, bool odd1, bool odd2) {
+  const float p0 = dpp_<0xB1>(x[0]), p1 = dpp_<0xB1>(x[1]);
+  const float p2 = dpp_<0xB1>(x[2]), p3 = dpp_<0xB1>(x[3]);
+  const f4 y = {odd1 ? p1 : x[0], odd1 ? x[1] : p0, odd1 ? p3 : x[2],
+                odd1 ? x[3] : p2};
+  const float q0 = dpp_<0x4E>(y[0]), q1 = dpp_<0x4E>(y[1]);
+  const float q2 = dpp_<0x4E>(y[2]), q3 = dpp_<0x4E>(y[3]);
+  return f4{odd2 ? q2 : y[0], odd2 ? q3 : y[1], odd2 ? y[2] : q0,
+            odd2 ? y[3] : q1};
 }
 __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_<0xB1>(v);
@@ -254,7 +280,17 @@ __device__ __forceinline__ f4 ld4(const float* p) {
 // the default (softplus) or the bounded gate.
 enum GateForm { kGateInput = 0, kGateSoftplus = 1, kGateBounded = 2 };
 
-template <bool kNorm, int kGate>
+// One segment of a workgroup's chunk stream: the tokens of one (sequence or
+// row, head).
+struct Seg {
+  int64_t tb;  // first token
+  int len;     // tokens
+  int slot;
+  int h;
+  int nch;     // 16-token chunks
+};
+
+template <bool kNorm, int kGate, bool kStream>
 __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     KdaChunkedArgs p) {
   constexpr bool kRaw = kGate != kGateInput;
@@ -269,43 +305,102 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   const int H = p.heads;
   const int C = H * kD;
   const int C3 = 3 * C;
-  const int n = static_cast<int>(blockIdx.x) / H;
-  const int h = static_cast<int>(blockIdx.x) % H;
-  // token offsets in 64 bits: tb * 3C passes 2^31 from 58,255 tokens at
-  // 96 heads
-  const int64_t tb = p.cu_seqlens ? p.cu_seqlens[n] : n * p.tokens_per_row;
-  const int64_t te =
-      p.cu_seqlens ? p.cu_seqlens[n + 1] : (n + 1) * p.tokens_per_row;
-  const int len = te > tb ? static_cast<int>(te - tb) : 0;
-  if (len == 0) return;
-  const int32_t slot = p.state_idx[n];
-  const int64_t col0 = static_cast<int64_t>(h) * kD;
-  if (slot <= 0 || slot >= p.num_slots) {
-    // null slot: +0.0 outputs, no state traffic
-    uint32_t* o32 = reinterpret_cast<uint32_t*>(p.out);
-    for (int64_t idx = tid; idx < static_cast<int64_t>(len) * (kD / 2);
-         idx += kThreads) {
-      const int64_t t = idx / (kD / 2);
-      o32[((tb + t) * C + col0) / 2 + idx % (kD / 2)] = 0u;
-    }
-    return;
-  }
   const uint32_t flags = p.flags;
   const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
   const bool conv_update = (flags & KDA_NO_CONV_UPDATE) == 0;
   const bool l2 = (flags & KDA_QK_L2NORM) != 0;
   const bool gate_silu = (flags & KDA_GATE_SILU) != 0;
-  const int nchunks = (len + kC - 1) / kC;
   const bool state_wave = wave < 4;
   const int pw = wave & 3;  // index within the role
-
-  // ---- per-sequence set-up ----------------------------------------------
-  // state waves: the wave's 32 columns of the state, 2 blocks of 16
-  float* st = p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD) +
-              32 * pw + c;
   // output lanes: token tid/16 (of the 16), columns 8 (tid%16) .. +7
   const int ot = (tid & 255) >> 4;
   const int oc = 8 * (tid & 15);
+
+  // Segments.  Prefill: one (sequence, head) per workgroup, s = n H + h.
+  // Stream mode (rows of tokens_per_row tokens): a contiguous run of
+  // segments per workgroup in head-major order, s = h N + n, so a
+  // workgroup's conv weights change at most a few times; its chunks form
+  // one stream through the same pipeline.
+  auto seg_at = [&](int sg) -> Seg {
+    Seg g;
+    int n;
+    if (kStream) {
+      g.h = sg / p.num_seqs;
+      n = sg - g.h * p.num_seqs;
+    } else {
+      n = sg / H;
+      g.h = sg - n * H;
+    }
+    // token offsets in 64 bits: tb * 3C passes 2^31 from 58,255 tokens at
+    // 96 heads
+    const int64_t tb =
+        p.cu_seqlens ? p.cu_seqlens[n] : static_cast<int64_t>(n) * p.tokens_per_row;
+    const int64_t te = p.cu_seqlens ? p.cu_seqlens[n + 1]
+                                    : tb + p.tokens_per_row;
+    g.tb = tb;
+    g.len = te > tb ? static_cast<int>(te - tb) : 0;
+    g.slot = p.state_idx[n];
+    g.nch = (g.len + kC - 1) / kC;
+    return g;
+  };
+  auto live = [&](const Seg& g) {
+    return g.len > 0 && g.slot > 0 && g.slot < p.num_slots;
+  };
+  // +0.0 outputs of a segment with tokens and a null slot (no state
+  // traffic), by `nthr` threads from thread index `t0`
+  auto zero_outputs = [&](const Seg& g, int t0, int nthr) {
+    uint32_t* o32 = reinterpret_cast<uint32_t*>(p.out);
+    const int64_t col0 = static_cast<int64_t>(g.h) * kD;
+    for (int64_t idx = t0; idx < static_cast<int64_t>(g.len) * (kD / 2);
+         idx += nthr) {
+      const int64_t t = idx / (kD / 2);
+      o32[((g.tb + t) * C + col0) / 2 + idx % (kD / 2)] = 0u;
+    }
+  };
+  int nseg_live;
+  int seg0 = static_cast<int>(blockIdx.x);
+  if (!kStream) {
+    const Seg g = seg_at(seg0);
+    if (g.len == 0) return;
+    if (!live(g)) {
+      zero_outputs(g, tid, kThreads);
+      return;
+    }
+    nseg_live = 1;
+  } else {
+    const int nseg = p.num_seqs * H;
+    const int s_begin = static_cast<int>(blockIdx.x) * p.segs_per_group;
+    const int s_end = s_begin + p.segs_per_group < nseg
+                          ? s_begin + p.segs_per_group
+                          : nseg;
+    if (wave == 0) {
+      // lane i looks at segment s_begin + i; the live ones are listed in
+      // order
+      const int sg = s_begin + lane;
+      bool lv = false;
+      if (sg < s_end) lv = live(seg_at(sg));
+      const uint64_t m = __ballot(lv);
+      const int rank = __builtin_amdgcn_mbcnt_hi(
+          static_cast<uint32_t>(m >> 32),
+          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+      if (lv) sm.seg_list[rank] = sg;
+      if (lane == 0) sm.seg_count = __popcll(m);
+    }
+    if (state_wave) {
+      // segments with tokens and a null slot: +0.0 outputs
+      for (int sg = s_begin + pw; sg < s_end; sg += 4) {
+        const Seg g = seg_at(sg);
+        if (g.len > 0 && !live(g)) zero_outputs(g, lane, 64);
+      }
+    }
+    __syncthreads();  // the segment list
+    nseg_live = __builtin_amdgcn_readfirstlane(sm.seg_count);
+    if (nseg_live == 0) return;
+  }
+  auto seg_of = [&](int i) -> Seg {
+    return kStream ? seg_at(__builtin_amdgcn_readfirstlane(sm.seg_list[i]))
+                   : seg_at(seg0);
+  };
   if (!state_wave && tid - 256 < kD)  // norm weight, read by the state waves
     sm.nw[tid - 256] = kNorm ? p.norm_w[tid - 256] : 0.0f;
 
@@ -322,14 +417,43 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   uint32_t in_raw[3][7];
   uint32_t in_g[kC][2];  // fp32 pair, or (raw gates) a bf16 pair in [0]
   uint32_t in_b = 0;     // fp32 or (raw gates) bf16 bits
+  // stream mode: the segment's stored window, as loaded (tap-major: the
+  // channel pair in [0]; channel-major: one channel in each of [0], [1],
+  // combined where used, so no load waits at its issue)
+  uint32_t in_wv[2][3][kW - 1];
   // this lane's byte offsets in an input row (parts q, k, v) and a gate row
   const uint32_t off_raw = 4 * lane;
   const uint32_t off_part = 2 * static_cast<uint32_t>(C);
   const uint32_t off_g = (kRaw ? 4 : 8) * lane;
-  auto load_chunk = [&](int cj) {
+  // the stored conv window of channels 2 lane, 2 lane + 1 of each part,
+  // as loaded (see in_wv)
+  auto load_window = [&](int slot, int64_t col0,
+                         uint32_t (&wv)[2][3][kW - 1]) {
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e) {
+        const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
+        if (tap_major) {
+          wv[0][pp][e] = *reinterpret_cast<const uint32_t*>(
+              p.conv_state +
+              (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch);
+          wv[1][pp][e] = 0u;
+        } else {
+          const uint16_t* cs =
+              p.conv_state + (static_cast<int64_t>(slot) * C3 + ch) * (kW - 1) +
+              e;
+          wv[0][pp][e] = cs[0];
+          wv[1][pp][e] = cs[kW - 1];
+        }
+      }
+  };
+  auto load_chunk = [&](const Seg& sg, int cj) {
     const int c0 = cj * kC;
-    const int nv = len - c0 < kC ? len - c0 : kC;
-    const int64_t tok0 = tb + c0;
+    const int nv = sg.len - c0 < kC ? sg.len - c0 : kC;
+    const int64_t tok0 = sg.tb + c0;
+    const int h = sg.h;
+    const int64_t col0 = static_cast<int64_t>(h) * kD;
     // row addresses are wave-uniform (scalar); lanes add 32-bit offsets
     const char* q0 = reinterpret_cast<const char*>(p.qkv + tok0 * C3 + col0);
     const int qrow = 2 * C3;  // bytes per token row (rows differ by < 16)
@@ -366,15 +490,19 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       in_b = kRaw ? static_cast<uint32_t>(p.rg.raw_beta[e])
                   : __float_as_uint(p.beta[e]);
     }
+    if (kStream) load_window(sg.slot, col0, in_wv);
   };
-  // per-sequence constants of the prep waves, for channels 2 lane,
-  // 2 lane + 1: conv weights, conv bias and dt_bias (raw gates), and the
-  // stored conv window
+  // per-head constants of the prep waves, for channels 2 lane, 2 lane + 1:
+  // conv weights, conv bias and dt_bias (raw gates); prefill mode also
+  // keeps the sequence's stored conv window
   f2 cwv[3][kW];
   f2 cbv[3] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
   f2 dtb = {0.f, 0.f};
-  uint32_t wv[3][kW - 1];
-  auto load_constants = [&]() {
+  uint32_t wv[2][3][kW - 1];
+  int cw_h = -1;  // head the constants are loaded for
+  auto load_constants = [&](const Seg& sg) {
+    const int64_t col0 = static_cast<int64_t>(sg.h) * kD;
+    cw_h = sg.h;
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) {
 #pragma unroll
@@ -385,36 +513,34 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       if (kRaw && p.rg.conv_bias)
         cbv[pp] = *reinterpret_cast<const f2*>(
             p.rg.conv_bias + static_cast<int64_t>(pp) * C + col0 + 2 * lane);
-#pragma unroll
-      for (int e = 0; e < kW - 1; ++e) {
-        const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
-        if (tap_major) {
-          wv[pp][e] = *reinterpret_cast<const uint32_t*>(
-              p.conv_state +
-              (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch);
-        } else {
-          const uint16_t* cs =
-              p.conv_state + (static_cast<int64_t>(slot) * C3 + ch) * (kW - 1) +
-              e;
-          wv[pp][e] = static_cast<uint32_t>(cs[0]) |
-                      (static_cast<uint32_t>(cs[kW - 1]) << 16);
-        }
-      }
     }
     if (kRaw)
       dtb = *reinterpret_cast<const f2*>(p.rg.dt_bias + col0 + 2 * lane);
+    if (!kStream) load_window(sg.slot, col0, wv);
   };
 
-  auto prep_tables = [&](int ci) {
-    ChunkTables& T = sm.tab[ci & 1];
+  // Stage 1 of chunk ci of segment g, stream position j (its table
+  // buffer); (gs, cs) is the chunk after it, whose inputs it requests.
+  auto prep_tables = [&](const Seg& g, int ci, int j, const Seg& gs, int cs) {
+    ChunkTables& T = sm.tab[j & 1];
     const int c0 = ci * kC;
-    const int nv = len - c0 < kC ? len - c0 : kC;
+    const int nv = g.len - c0 < kC ? g.len - c0 : kC;
+    const int h = g.h;
+    // stream mode: another head's weights (a few times per workgroup)
+    if (kStream && h != cw_h) load_constants(g);
     // this chunk's inputs (loaded a chunk ago)
     uint32_t raw[3][7];
 #pragma unroll
     for (int u = 0; u < 7; ++u)
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp) raw[pp][u] = in_raw[pp][u];
+    uint32_t wc[3][kW - 1];
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e)
+        wc[pp][e] = kStream ? in_wv[0][pp][e] | (in_wv[1][pp][e] << 16)
+                            : wv[0][pp][e] | (wv[1][pp][e] << 16);
     // per-token decays of keys 2 lane, 2 lane + 1 in log2 units
     f2 gl[kC];
     if (kRaw) {
@@ -486,18 +612,55 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
             const bool before = rin0 < 0 && pw == 0 && ci == 0;
             const uint32_t w2 =
                 tap == kW - 1 ? raw[pp][u + tap]
-                : conv_update ? (before ? wv[pp][(kW - 1) + (rin0 < 0 ? rin0 : 0)]
+                : conv_update ? (before ? wc[pp][(kW - 1) + (rin0 < 0 ? rin0 : 0)]
                                         : raw[pp][u + tap])
-                              : wv[pp][tap];
+                              : wc[pp][tap];
             a += cwv[pp][tap][e] * (e ? bf16_hi(w2) : bf16_lo(w2));
           }
           y[u][pp][e] = valid ? a * sigmoid_(a) : 0.0f;
         }
     }
+    // At the segment's last chunk the prep wave whose 7 input rows hold
+    // the segment's last W-1 inputs writes them as the new stored window
+    // (for a segment shorter than that, the old window's newest entries
+    // come first); every read of the old window is behind it
+    if (conv_update && ci + 1 == g.nch && pw == (g.len - 1 - c0) / 4) {
+      const int64_t col0 = static_cast<int64_t>(h) * kD;
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e) {
+        const int idx = g.len - (kW - 1) + e;  // token in the segment
+        const int u = idx - c0 - (4 * pw - 3);  // its input row, 0..6
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+          uint32_t w = raw[pp][0];
+#pragma unroll
+          for (int q = 1; q < 7; ++q)
+            if (u == q) w = raw[pp][q];
+          if (idx < 0) {  // from the old window: entry idx + W-1
+            w = wc[pp][0];
+#pragma unroll
+            for (int q = 1; q < kW - 1; ++q)
+              if (idx + (kW - 1) == q) w = wc[pp][q];
+          }
+          const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
+          if (tap_major) {
+            *reinterpret_cast<uint32_t*>(
+                p.conv_state +
+                (static_cast<int64_t>(g.slot) * (kW - 1) + e) * C3 + ch) = w;
+          } else {
+            uint16_t* cs = p.conv_state +
+                           (static_cast<int64_t>(g.slot) * C3 + ch) * (kW - 1) +
+                           e;
+            cs[0] = static_cast<uint16_t>(w);
+            cs[kW - 1] = static_cast<uint16_t>(w >> 16);
+          }
+        }
+      }
+    }
     // the inputs are consumed: the next chunk's loads reuse their registers
-    // (unconditional -- the last chunk loads itself again -- so no copy
-    // has to wait for them)
-    load_chunk(ci + 1 < nchunks ? ci + 1 : ci);
+    // (unconditional -- after the last chunk its own inputs again -- so no
+    // copy has to wait for them)
+    load_chunk(gs, cs);
     if (l2) {
       float ss[8];
 #pragma unroll
@@ -570,8 +733,8 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   };
 
   // ---- prep stage 2: A / B products (or the exact per-entry sums) -------
-  auto prep_gram = [&](int ci) {
-    const ChunkTables& T = sm.tab[ci & 1];
+  auto prep_gram = [&](int j) {
+    const ChunkTables& T = sm.tab[j & 1];
     if (!sm.unsafe) {
       // wave 4: A over keys 0-63, 5: A over 64-127, 6 / 7: B likewise
       const uint32_t(*src)[kRowU] = pw < 2 ? T.kt : T.qt;
@@ -601,9 +764,9 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   };
 
   // ---- prep stage 3: sum the partial products, mask, scale by beta ------
-  auto prep_reduce = [&](int ci) {
+  auto prep_reduce = [&](int j) {
     if (sm.unsafe) return;
-    const ChunkTables& T = sm.tab[ci & 1];
+    const ChunkTables& T = sm.tab[j & 1];
     const int t = (tid & 255) >> 4;
     const int s = tid & 15;
     const float a = sm.part[0][t][s] + sm.part[1][t][s];
@@ -612,9 +775,47 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     sm.B[t][s] = s <= t ? b : 0.0f;
   };
 
+  // The wave's 32 columns of a segment's state, 2 blocks of 16, in the
+  // accumulator layout: element (cb, kb, r) of lane l is row 16 kb +
+  // 4 (l/16) + r, column 32 pw + 16 cb + l%16.  It moves as 16-byte rows:
+  // a quad transpose gives lane l row 16 kb + 4 (l/16) + l%4, columns
+  // 32 pw + 16 cb + 4 ((l%16)/4) .. +3.  Addressed as a wave-uniform base
+  // per 16-row block, one 32-bit lane offset and immediate offsets (no
+  // per-element 64-bit addresses to keep live).
+  const uint32_t st_lane = ((4 * gq + (c & 3)) * kD + 4 * (c >> 2)) * 4;
+  const bool q_odd1 = (c & 1) != 0;
+  const bool q_odd2 = (c & 2) != 0;
+  auto state_block = [&](const Seg& sg, int kb) {
+    return uniform_gptr(p.rec_state +
+                        (static_cast<int64_t>(sg.slot) * H + sg.h) *
+                            (kD * kD) +
+                        32 * pw + 16 * kb * kD);
+  };
+  auto load_block = [&](const Seg& sg, int kb, f4 (&S)[2][8]) {
+    const gptr<const char> b = state_block(sg, kb);
+    uint32_t lo = st_lane;
+    asm volatile("" : "+v"(lo));
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      S[cb][kb] = *reinterpret_cast<gptr<const f4>>(b + lo + 64 * cb);
+  };
+  auto unpack_block = [&](int kb, f4 (&S)[2][8]) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      S[cb][kb] = quad_transpose(S[cb][kb], q_odd1, q_odd2);
+  };
+  auto store_block = [&](const Seg& sg, int kb, const f4 (&S)[2][8]) {
+    gptr<char> b = const_cast<gptr<char>>(state_block(sg, kb));
+    uint32_t lo = st_lane;
+    asm volatile("" : "+v"(lo));
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      *reinterpret_cast<gptr<f4>>(b + lo + 64 * cb) =
+          quad_transpose(S[cb][kb], q_odd1, q_odd2);
+  };
   // ---- state stage: one chunk through the recurrence ---------------------
-  auto state_chunk = [&](int ci, f4 (&S)[2][8]) {
-    const ChunkTables& T = sm.tab[ci & 1];
+  auto state_chunk = [&](int j, f4 (&S)[2][8]) {
+    const ChunkTables& T = sm.tab[j & 1];
     f4 ks[2], o[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -713,9 +914,11 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   };
 
   // ---- state stage: gated RMSNorm and bf16 outputs of a chunk ------------
-  auto emit = [&](int ci, u4 gate_raw) {
+  auto emit = [&](const Seg& g, int ci, u4 gate_raw) {
     const int c0 = ci * kC;
-    const int nv = len - c0 < kC ? len - c0 : kC;
+    const int nv = g.len - c0 < kC ? g.len - c0 : kC;
+    const int64_t tb = g.tb;
+    const int64_t col0 = static_cast<int64_t>(g.h) * kD;
     const f4 v0 = ld4(&sm.o[ot][oc]);
     const f4 v1 = ld4(&sm.o[ot][oc + 4]);
     float yv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -742,57 +945,111 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 
   // ---- the pipeline --------------------------------------------------------
   // Each role runs a loop of its own (the state lives only in the state
-  // waves' loop, so the prep code does not carry its registers); both meet
-  // at the same barriers: 3 before the first chunk, then 3 per chunk.
+  // waves' loop, so the prep code does not carry its registers); both walk
+  // the same chunk stream -- the chunks of this workgroup's live segments
+  // in order -- and meet at the same barriers: 3 before the first chunk,
+  // then 3 per chunk.
   if (state_wave) {
+    int j = 0;  // stream position
+    auto gate_row = [&](const Seg& sg, int ci) -> u4 {
+      u4 gate_raw = {0u, 0u, 0u, 0u};
+      if (kNorm) {
+        const int nv = sg.len - ci * kC < kC ? sg.len - ci * kC : kC;
+        const int rr = ot < nv - 1 ? ot : nv - 1;
+        gate_raw = *reinterpret_cast<const u4*>(
+            p.gate + (sg.tb + ci * kC + rr) * C +
+            static_cast<int64_t>(sg.h) * kD + oc);
+      }
+      return gate_raw;
+    };
+    Seg g = seg_of(0);
     f4 S[2][8];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[cb][kb][r] = st[(16 * kb + 4 * gq + r) * kD + 16 * cb];
+    for (int kb = 0; kb < 8; ++kb) load_block(g, kb, S);
     __syncthreads();  // first chunk's tables (and the norm weight)
     __syncthreads();  // its partial products
     __syncthreads();  // its A and B
-    for (int ci = 0; ci < nchunks; ++ci) {
-      u4 gate_raw = {0u, 0u, 0u, 0u};
-      if (kNorm) {
-        const int nv = len - ci * kC < kC ? len - ci * kC : kC;
-        const int rr = ot < nv - 1 ? ot : nv - 1;
-        gate_raw = *reinterpret_cast<const u4*>(
-            p.gate + (tb + ci * kC + rr) * C + col0 + oc);
+    if constexpr (!kStream) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) unpack_block(kb, S);
+      for (int ci = 0; ci < g.nch; ++ci, ++j) {
+        const u4 gate_raw = gate_row(g, ci);
+        state_chunk(j, S);
+        __syncthreads();  // outputs in sm.o; next chunk's tables ready
+        emit(g, ci, gate_raw);
+        __syncthreads();  // next chunk's partial products
+        __syncthreads();  // next chunk's A and B
       }
-      state_chunk(ci, S);
-      __syncthreads();  // outputs in sm.o; next chunk's tables ready
-      emit(ci, gate_raw);
-      __syncthreads();  // next chunk's partial products
-      __syncthreads();  // next chunk's A and B
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) store_block(g, kb, S);
+    } else {
+      for (int i = 0; i < nseg_live; ++i) {
+        // the next segment (the last one names itself: its state comes
+        // back once more, unused)
+        const Seg gn = seg_of(i + 1 < nseg_live ? i + 1 : i);
+        for (int ci = 0; ci < g.nch; ++ci, ++j) {
+          const u4 gate_raw = gate_row(g, ci);
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) unpack_block(kb, S);
+          state_chunk(j, S);
+          // the state goes back to memory after every chunk and the state
+          // of the chunk that runs next -- this segment's again, or after
+          // its last chunk the next segment's -- loads into the same
+          // registers while the outputs are emitted (one unconditional
+          // reload: no register copies)
+          const Seg& gl = ci + 1 == g.nch ? gn : g;
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) store_block(g, kb, S);
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) load_block(gl, kb, S);
+          __syncthreads();  // outputs in sm.o; next chunk's tables ready
+          emit(g, ci, gate_raw);
+          __syncthreads();  // next chunk's partial products
+          __syncthreads();  // next chunk's A and B
+        }
+        g = gn;
+      }
     }
-    // ---- write back the state ----
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          st[(16 * kb + 4 * gq + r) * kD + 16 * cb] = S[cb][kb][r];
   } else {
-    load_chunk(0);
-    load_constants();
-    prep_tables(0);
+    // the chunk being prepared (segment i, chunk ci, stream position j)
+    int i = 0, ci = 0, j = 0;
+    Seg g = seg_of(0);
+    // the chunk after (i, ci); false at the end of the stream
+    auto advance = [&](int& i_, int& ci_, Seg& g_) -> bool {
+      if (ci_ + 1 < g_.nch) {
+        ++ci_;
+        return true;
+      }
+      if (i_ + 1 >= nseg_live) return false;
+      ++i_;
+      ci_ = 0;
+      g_ = seg_of(i_);
+      return true;
+    };
+    int i2 = i, ci2 = ci;
+    Seg g2 = g;
+    bool more = advance(i2, ci2, g2);
+    load_constants(g);
+    load_chunk(g, 0);
+    prep_tables(g, 0, 0, g2, ci2);
     __syncthreads();
     prep_gram(0);
     __syncthreads();
     prep_reduce(0);
     __syncthreads();
-    for (int ci = 0; ci + 1 < nchunks; ++ci) {
-      prep_tables(ci + 1);
+    while (more) {
+      i = i2;
+      ci = ci2;
+      g = g2;
+      ++j;
+      more = advance(i2, ci2, g2);
+      prep_tables(g, ci, j, g2, ci2);
       __syncthreads();
-      prep_gram(ci + 1);
+      prep_gram(j);
       __syncthreads();
-      prep_reduce(ci + 1);
+      prep_reduce(j);
       __syncthreads();
     }
     // the last chunk: nothing left to prepare
@@ -800,48 +1057,54 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     __syncthreads();
     __syncthreads();
   }
-
-  // ---- write back the conv window -----------------------------------------
-  if (conv_update && tid < 3 * kD) {
-    // new window = the last W-1 inputs of (stored window ++ tokens)
-    const int64_t ch =
-        (tid >> 7) * static_cast<int64_t>(C) + col0 + (tid & 127);
-    auto at = [&](int e) -> int64_t {
-      return tap_major ? (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch
-                       : (static_cast<int64_t>(slot) * C3 + ch) * (kW - 1) + e;
-    };
-    uint16_t nwin[kW - 1];
-#pragma unroll
-    for (int e = 0; e < kW - 1; ++e) {
-      const int idx = len - (kW - 1) + e;  // token index in the sequence
-      nwin[e] = idx >= 0 ? p.qkv[(tb + idx) * C3 + ch]
-                         : p.conv_state[at(e + len)];
-    }
-#pragma unroll
-    for (int e = 0; e < kW - 1; ++e) p.conv_state[at(e)] = nwin[e];
-  }
 }
 
-template <int kGate>
+template <int kGate, bool kStream>
 void launch_gate(const KdaChunkedArgs& args, dim3 grid, hipStream_t stream) {
   if (args.flags & KDA_OUTPUT_NORM)
-    hipLaunchKernelGGL((kda_chunked_prefill_kernel<true, kGate>), grid,
-                       dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((kda_chunked_prefill_kernel<true, kGate, kStream>),
+                       grid, dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((kda_chunked_prefill_kernel<false, kGate>), grid,
-                       dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((kda_chunked_prefill_kernel<false, kGate, kStream>),
+                       grid, dim3(kThreads), 0, stream, args);
+}
+
+template <bool kStream>
+void launch_mode(const KdaChunkedArgs& args, dim3 grid, hipStream_t stream) {
+  if (!args.rg.raw_g)
+    launch_gate<kGateInput, kStream>(args, grid, stream);
+  else if (args.flags & KDA_BOUNDED_GATE)
+    launch_gate<kGateBounded, kStream>(args, grid, stream);
+  else
+    launch_gate<kGateSoftplus, kStream>(args, grid, stream);
 }
 
 }  // namespace
 
 hipError_t kda_chunked_prefill_launch(const KdaChunkedArgs& args,
                                       int32_t num_seqs, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(num_seqs * args.heads));
-  if (!args.rg.raw_g)
-    launch_gate<kGateInput>(args, grid, stream);
-  else if (args.flags & KDA_BOUNDED_GATE)
-    launch_gate<kGateBounded>(args, grid, stream);
-  else
-    launch_gate<kGateSoftplus>(args, grid, stream);
+  KdaChunkedArgs a = args;
+  a.num_seqs = num_seqs;
+  const int64_t nseg = static_cast<int64_t>(num_seqs) * args.heads;
+  if (args.cu_seqlens || args.tokens_per_row > KDA_CHUNKED_STREAM_MAX_TOKENS) {
+    // one (sequence, head) per workgroup
+    a.segs_per_group = 1;
+    launch_mode<false>(a, dim3(static_cast<unsigned>(nseg)), stream);
+  } else {
+    // rows of a few tokens: runs of segments per workgroup, one workgroup
+    // per compute unit where the rows allow (at most kMaxSegs each)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    int64_t per = (nseg + cus - 1) / cus;
+    if (per < 1) per = 1;
+    if (per > kMaxSegs) per = kMaxSegs;
+    a.segs_per_group = static_cast<int32_t>(per);
+    launch_mode<true>(a, dim3(static_cast<unsigned>((nseg + per - 1) / per)),
+                      stream);
+  }
   return hipGetLastError();
 }

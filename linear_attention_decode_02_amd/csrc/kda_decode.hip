@@ -894,12 +894,11 @@ Params base_params(const kda_dims* d, const void* qkv, const float* conv_w,
 }
 
 // From this many tokens per row on, kda_decode_tokens runs the chunked
-// (matrix-core) kernel: measured on MI355X with 256 rows x 48 heads and
-// L2-normalised q/k, the token-by-token kernel takes 888 / 1021 / 1084 /
-// 1165 / 1228 / 1299 us at T = 20 / 24 / 26 / 28 / 30 / 32 against about
-// 1175 us chunked at each of them (a chunk is 16 tokens, so 17..32 tokens
-// cost two).
-constexpr int32_t kChunkedMinTokens = 29;
+// (matrix-core) kernel, which pipelines the rows of a workgroup as one
+// chunk stream: measured on MI355X with 224 live rows x 48 heads, token by
+// token / chunked, 507 / 537 us at T = 9, 548 / 544 at 10, 567 / 536 at
+// 11, 602 / 527 at 12 (a chunk is 16 tokens: up to 16 cost one).
+constexpr int32_t kChunkedMinTokens = 11;
 
 KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
                             int32_t tokens_per_row, const void* qkv,

@@ -186,18 +186,23 @@ def test_tokens_b256_h48_full_size():
 
 
 CHUNKED_CASES = [
-    ("plain", 0, True, 29), ("nonorm", 0, False, 30),
-    ("tap_major", O.CONV_TAP_MAJOR, True, 33),
-    ("l2_silu", O.QK_L2NORM | O.GATE_SILU, True, 29),
-    ("no_conv_update", O.NO_CONV_UPDATE, True, 40),
+    ("plain", 0, True, 11), ("nonorm", 0, False, 12),
+    ("tap_major", O.CONV_TAP_MAJOR, True, 16),
+    ("l2_silu", O.QK_L2NORM | O.GATE_SILU, True, 13),
+    ("no_conv_update", O.NO_CONV_UPDATE, True, 15),
+    ("plain_two_chunks", 0, True, 29), ("nonorm_two_chunks", 0, False, 30),
+    ("tap_major_three_chunks", O.CONV_TAP_MAJOR, True, 33),
+    ("no_conv_update_three_chunks", O.NO_CONV_UPDATE, True, 40),
 ]
 
 
 @pytest.mark.parametrize("name,flags,norm,T", CHUNKED_CASES,
                          ids=[c[0] for c in CHUNKED_CASES])
-def test_tokens_from_29_take_the_chunked_form(name, flags, norm, T):
-    """From 29 tokens per row the call runs the chunked matrix-core form;
-    it must still equal T successive single-token steps (the oracle)."""
+def test_tokens_from_11_take_the_chunked_form(name, flags, norm, T):
+    """From 11 tokens per row the call runs the chunked matrix-core form
+    (the rows of a workgroup one chunk stream; from 17 tokens two chunks
+    per row); it must still equal T successive single-token steps (the
+    oracle)."""
     H = 24
     w = synth.small(f"tc_{name}", batch=9, heads=H, num_slots=14,
                     seed=150 + T, null_every=4, norm=norm,
@@ -217,10 +222,10 @@ def test_tokens_from_29_take_the_chunked_form(name, flags, norm, T):
     print(f"[tokens chunked] {name}: {st}", flush=True)
 
 
-def test_tokens_28_and_29_agree_with_single_calls():
+def test_tokens_10_and_11_agree_with_single_calls():
     """Either side of the switch to the chunked form, against T single-token
-    kernel calls on the same inputs."""
-    for T in (28, 29):
+    kernel calls on the same inputs (and two chunks per row at 29)."""
+    for T in (10, 11, 29):
         w = synth.small(f"tsw{T}", batch=12, heads=48, num_slots=20,
                         seed=170 + T, null_every=5, conv_w_sigma=0.05)
         inp = synth.make_tokens(w, T)
@@ -237,12 +242,12 @@ def test_tokens_28_and_29_agree_with_single_calls():
                            inp["state_idx"], w.num_slots, w.heads)
 
 
-@pytest.mark.parametrize("T", [16, 29])
+@pytest.mark.parametrize("T", [10, 16, 29])
 def test_tokens_b256_h48_full_size(T):
-    """The batch-256, 48-head workload (32 null rows) with 16 tokens per
-    row (token by token) and 29 (the chunked form, a ragged second chunk)
-    at full size, every
-    element against the oracle.
+    """The batch-256, 48-head workload (32 null rows) with 10 tokens per
+    row (token by token), 16 (the chunked form, one chunk per row) and 29
+    (two chunks, the second ragged) at full size, every element against
+    the oracle.
     q/k are L2-normalised (unit keys, beta < 1: each update contracts the
     state along k).  Without it these inputs give beta |k|^2 near 40, and
     16 or more chained updates amplify fp32 rounding order by that factor
@@ -338,10 +343,10 @@ def test_tokens_graph_replay_matches_eager(T):
         print(f"[tokens graph T={T}] replay {r} matches eager", flush=True)
 
 
-@pytest.mark.parametrize("T", [28, 29])
+@pytest.mark.parametrize("T", [10, 11, 29])
 def test_tokens_decay_contract_independent_of_T(T):
     """The contract on g is the same on both sides of the switch to the
-    chunked form at 29 tokens: per element -inf (5 %, the key row is
+    chunked form at 11 tokens: per element -inf (5 %, the key row is
     forgotten), -1e30 (5 %), -100 (5 %, exp underflows), -1e-4 (5 %) or an
     ordinary decay, against the oracle (exp(-inf) = 0 there)."""
     w = synth.small(f"tginf{T}", batch=6, heads=24, num_slots=10,
