@@ -224,8 +224,16 @@ __device__ __forceinline__ U load_at(gptr<const char> base, uint32_t byte_off) {
   return *reinterpret_cast<gptr<const U>>(base + byte_off);
 }
 
+// DPP with a row mask: rows outside it keep 0
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_rows_(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                         kRowMask, 0xF, false));
+}
 // Eight wave sums side by side (independent DPP chains), each result in
-// every lane.
+// every lane: the row sums (xor butterfly), then row_bcast:15 into rows 1
+// and 3 and row_bcast:31 into rows 2 and 3, so lane 63 holds the total.
 __device__ __forceinline__ void wave_sum8(float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] += dpp_<0xB1>(v[i]);
@@ -236,13 +244,13 @@ __device__ __forceinline__ void wave_sum8(float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] += dpp_<0x140>(v[i]);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = __builtin_bit_cast(int, v[i]);
-    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16)) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-  }
+  for (int i = 0; i < 8; ++i) v[i] += dpp_rows_<0x142, 0xA>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += dpp_rows_<0x143, 0xC>(v[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[i]), 63));
 }
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
@@ -692,6 +700,10 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       row[pos + 8] = x.l;
     };
     f2 khv[4];
+    // e^{G_last}; on the matrix-core path e^{G_last - G_t} is taken as
+    // e^{G_last} e^{-G_t} (every |G| <= 80 there, so both factors are
+    // normal numbers), which saves an exponential per channel and token
+    const f2 eG = {exp2_(G.x), exp2_(G.y)};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = 4 * pw + u;
@@ -699,12 +711,13 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       put3(T.qt[t], y[u][0][0] * ee.x, y[u][0][1] * ee.y);
       put3(T.kt[t], y[u][1][0] * ee.x, y[u][1][1] * ee.y);
       *reinterpret_cast<f2*>(&T.v[t][2 * lane]) = f2{y[u][2][0], y[u][2][1]};
-      khv[u] = f2{y[u][1][0] * exp2_(G.x - Gu[u].x),
-                  y[u][1][1] * exp2_(G.y - Gu[u].y)};
       if (!unsafe) {
-        put3(sm.kis[t], y[u][1][0] * exp2_(-Gu[u].x),
-             y[u][1][1] * exp2_(-Gu[u].y));
+        const f2 ei = {exp2_(-Gu[u].x), exp2_(-Gu[u].y)};
+        khv[u] = f2{(y[u][1][0] * eG.x) * ei.x, (y[u][1][1] * eG.y) * ei.y};
+        put3(sm.kis[t], y[u][1][0] * ei.x, y[u][1][1] * ei.y);
       } else {
+        khv[u] = f2{y[u][1][0] * exp2_(G.x - Gu[u].x),
+                    y[u][1][1] * exp2_(G.y - Gu[u].y)};
         *reinterpret_cast<f2*>(&sm.ki[t][2 * lane]) =
             f2{y[u][1][0], y[u][1][1]};
         *reinterpret_cast<f2*>(&sm.qraw[t][2 * lane]) =
@@ -723,7 +736,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       dst[1] = u4{a.h, b.h, a.l, b.l};
     }
     if (pw == 0) {
-      *reinterpret_cast<f2*>(&T.gam[2 * lane]) = f2{exp2_(G.x), exp2_(G.y)};
+      *reinterpret_cast<f2*>(&T.gam[2 * lane]) = eG;
       if (lane == 0) sm.unsafe = unsafe ? 1 : 0;
     }
     if (lane < 4) {
