@@ -262,6 +262,25 @@ def test_tokens_b256_h48_full_size(T):
     print(f"[tokens b256 T={T}] {st}", flush=True)
 
 
+def test_tokens_rows_mode_at_the_segment_cap():
+    """Rows of 12 tokens at 200 rows x 96 heads: 19,200 (row, head)
+    segments, more than 64 per compute unit, so the chunked kernel's rows
+    mode runs workgroups of 64 segments in more than one round, with null
+    rows inside the runs; every element against the oracle (q/k
+    L2-normalised, the contractive regime: absolute state bar)."""
+    T, H = 12, 96
+    w = synth.small("rows_cap", batch=200, heads=H, num_slots=210, seed=410,
+                    null_every=7, conv_w_sigma=0.5)
+    inp = synth.make_tokens(w, T)
+    ref = O.decode_tokens(inp, heads=H, tokens=T, norm=True, eps=w.eps,
+                          flags=O.QK_L2NORM)
+    got = run_tokens(w, inp, T, variants=O.QK_L2NORM)
+    st = check_tokens(w, inp, got, ref, T)
+    null = ~((inp["state_idx"] > 0) & (inp["state_idx"] < w.num_slots))
+    assert null.any() and np.all(got["out"][null] == 0)
+    print(f"[tokens rows cap] {st}", flush=True)
+
+
 def test_tokens_argument_checks():
     w = synth.small("tc", batch=2, heads=12, num_slots=4, seed=60)
     inp = synth.make_tokens(w, 2)
