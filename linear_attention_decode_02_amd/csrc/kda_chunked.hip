@@ -71,6 +71,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kda_chunked.h"
 #include "kda_decode.h"
@@ -527,9 +528,42 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     if (!kStream) load_window(sg.slot, col0, wv);
   };
 
+  // a segment's new conv window, held from its last chunk's stage 1 to the
+  // barrier after it
+  bool win_pending = false;
+  int win_slot = 0, win_h = 0;
+  uint32_t win_new[3][kW - 1];
+  auto flush_window = [&]() {
+    if (!win_pending) return;
+    const int64_t col0 = static_cast<int64_t>(win_h) * kD;
+#pragma unroll
+    for (int e = 0; e < kW - 1; ++e)
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) {
+        const uint32_t w = win_new[pp][e];
+        const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
+        if (tap_major) {
+          *reinterpret_cast<uint32_t*>(
+              p.conv_state +
+              (static_cast<int64_t>(win_slot) * (kW - 1) + e) * C3 + ch) = w;
+        } else {
+          uint16_t* cs = p.conv_state +
+                         (static_cast<int64_t>(win_slot) * C3 + ch) * (kW - 1) +
+                         e;
+          cs[0] = static_cast<uint16_t>(w);
+          cs[kW - 1] = static_cast<uint16_t>(w >> 16);
+        }
+      }
+    win_pending = false;
+  };
   // Stage 1 of chunk ci of segment g, stream position j (its table
   // buffer); (gs, cs) is the chunk after it, whose inputs it requests.
-  auto prep_tables = [&](const Seg& g, int ci, int j, const Seg& gs, int cs) {
+  // `plain` (a compile-time tag) is the common case -- a full chunk that is
+  // not the segment's first, with the conv update -- where no token is
+  // masked and no input comes from the stored window.
+  auto prep_tables = [&](auto plain, const Seg& g, int ci, int j,
+                         const Seg& gs, int cs) {
+    constexpr bool kPlain = decltype(plain)::value;
     ChunkTables& T = sm.tab[j & 1];
     const int c0 = ci * kC;
     const int nv = g.len - c0 < kC ? g.len - c0 : kC;
@@ -586,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int t = 4 * grp + u;
-          if (t < nv) G += gl[t];
+          if (kPlain || t < nv) G += gl[t];
           gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
           Gt[u] = G;
         }
@@ -604,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     float y[4][3][2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bool valid = 4 * pw + u < nv;
+      const bool valid = kPlain || 4 * pw + u < nv;
 #pragma unroll
       for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
@@ -617,23 +651,27 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
             // (only wave 0 reaches before the chunk: index rin0 = rin there,
             // a constant, so the window stays in registers)
             const int rin0 = u - (kW - 1) + tap;
-            const bool before = rin0 < 0 && pw == 0 && ci == 0;
+            const bool before = !kPlain && rin0 < 0 && pw == 0 && ci == 0;
             const uint32_t w2 =
                 tap == kW - 1 ? raw[pp][u + tap]
-                : conv_update ? (before ? wc[pp][(kW - 1) + (rin0 < 0 ? rin0 : 0)]
-                                        : raw[pp][u + tap])
-                              : wc[pp][tap];
+                : (kPlain || conv_update)
+                    ? (before ? wc[pp][(kW - 1) + (rin0 < 0 ? rin0 : 0)]
+                              : raw[pp][u + tap])
+                    : wc[pp][tap];
             a += cwv[pp][tap][e] * (e ? bf16_hi(w2) : bf16_lo(w2));
           }
           y[u][pp][e] = valid ? a * sigmoid_(a) : 0.0f;
         }
     }
     // At the segment's last chunk the prep wave whose 7 input rows hold
-    // the segment's last W-1 inputs writes them as the new stored window
+    // the segment's last W-1 inputs keeps them as the new stored window
     // (for a segment shorter than that, the old window's newest entries
-    // come first); every read of the old window is behind it
-    if (conv_update && ci + 1 == g.nch && pw == (g.len - 1 - c0) / 4) {
-      const int64_t col0 = static_cast<int64_t>(h) * kD;
+    // come first); it writes them after the next barrier, once every prep
+    // wave's reads of the old window are done (see flush_window)
+    win_pending = conv_update && ci + 1 == g.nch && pw == (g.len - 1 - c0) / 4;
+    if (win_pending) {
+      win_slot = g.slot;
+      win_h = h;
 #pragma unroll
       for (int e = 0; e < kW - 1; ++e) {
         const int idx = g.len - (kW - 1) + e;  // token in the segment
@@ -650,18 +688,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
             for (int q = 1; q < kW - 1; ++q)
               if (idx + (kW - 1) == q) w = wc[pp][q];
           }
-          const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
-          if (tap_major) {
-            *reinterpret_cast<uint32_t*>(
-                p.conv_state +
-                (static_cast<int64_t>(g.slot) * (kW - 1) + e) * C3 + ch) = w;
-          } else {
-            uint16_t* cs = p.conv_state +
-                           (static_cast<int64_t>(g.slot) * C3 + ch) * (kW - 1) +
-                           e;
-            cs[0] = static_cast<uint16_t>(w);
-            cs[kW - 1] = static_cast<uint16_t>(w >> 16);
-          }
+          win_new[pp][e] = w;
         }
       }
     }
@@ -747,6 +774,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 
   // ---- prep stage 2: A / B products (or the exact per-entry sums) -------
   auto prep_gram = [&](int j) {
+    flush_window();  // behind the barrier: every old-window read is done
     const ChunkTables& T = sm.tab[j & 1];
     if (!sm.unsafe) {
       // wave 4: A over keys 0-63, 5: A over 64-127, 6 / 7: B likewise
@@ -1046,7 +1074,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     bool more = advance(i2, ci2, g2);
     load_constants(g);
     load_chunk(g, 0);
-    prep_tables(g, 0, 0, g2, ci2);
+    prep_tables(std::false_type{}, g, 0, 0, g2, ci2);
     __syncthreads();
     prep_gram(0);
     __syncthreads();
@@ -1058,7 +1086,12 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       g = g2;
       ++j;
       more = advance(i2, ci2, g2);
-      prep_tables(g, ci, j, g2, ci2);
+      // (prefill mode only: rows mode rows are short, and the second copy
+      // costs its registers)
+      if (!kStream && ci > 0 && g.len - ci * kC >= kC && conv_update)
+        prep_tables(std::true_type{}, g, ci, j, g2, ci2);
+      else
+        prep_tables(std::false_type{}, g, ci, j, g2, ci2);
       __syncthreads();
       prep_gram(j);
       __syncthreads();
