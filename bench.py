@@ -33,7 +33,9 @@ if ROOT not in sys.path:
 METRIC = "KDA decode (seq*head) updates/sec + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
-# kda_decode_tokens runs the chunked matrix-core form from this many tokens
+# kda_decode_tokens runs the short-row chunk kernel for rows of these many
+# tokens and the chunked matrix-core form from CHUNKED_MIN_TOKENS on
+SHORT_ROW_TOKENS = (5, 8)
 CHUNKED_MIN_TOKENS = 11
 # fp32 matrix flop per (16-token chunk, head) of the chunked form: K~S, Q~S
 # and the state update (3 x 2*16*128*128), A, B, the solve and B Delta
@@ -245,6 +247,8 @@ def main():
         "launches_per_step": L,
         "wall_GBs": round(alg_bytes * L * K / wall / 1e9, 1),
     }
+    if T > 1:
+        extra["tokens_path"] = tokens_path(T)
 
     if not args.no_graph:
         R = max(1, (max(10, K // 4) + L - 1) // L)      # steps per replay
@@ -323,6 +327,19 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def tokens_path(T):
+    """The kernel kda_decode_tokens runs for rows of T tokens."""
+    if SHORT_ROW_TOKENS[0] <= T <= SHORT_ROW_TOKENS[1]:
+        return "short rows: the row's tokens as one chunk, one workgroup " \
+               "per (row, head)"
+    if T < CHUNKED_MIN_TOKENS:
+        return "token by token"
+    if T <= 32:
+        return "chunked rows mode: runs of (row, head) segments per " \
+               "workgroup as one chunk stream"
+    return "chunked: one workgroup per (row, head)"
 
 
 def bench_serving(args, np, torch, kda, synth, copies=8, calls=64):

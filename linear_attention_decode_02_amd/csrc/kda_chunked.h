@@ -45,3 +45,10 @@ struct KdaChunkedArgs {
 // of (row, head) segments per workgroup, about one workgroup per CU.
 hipError_t kda_chunked_prefill_launch(const KdaChunkedArgs& args,
                                       int32_t num_seqs, hipStream_t stream);
+
+// Rows of 2 .. KDA_SHORT_ROWS_MAX_TOKENS tokens (cu_seqlens null): one
+// workgroup per (row, head), the row's tokens as one chunk, several
+// workgroups per compute unit.
+#define KDA_SHORT_ROWS_MAX_TOKENS 8
+hipError_t kda_short_rows_launch(const KdaChunkedArgs& args, int32_t num_rows,
+                                 hipStream_t stream);

@@ -899,6 +899,11 @@ Params base_params(const kda_dims* d, const void* qkv, const float* conv_w,
 // token / chunked, 507 / 537 us at T = 9, 548 / 544 at 10, 567 / 536 at
 // 11, 602 / 527 at 12 (a chunk is 16 tokens: up to 16 cost one).
 constexpr int32_t kChunkedMinTokens = 11;
+// Rows of kShortMinTokens .. KDA_SHORT_ROWS_MAX_TOKENS tokens run the
+// short-row kernel (the row's tokens as one chunk, one workgroup per (row,
+// head)): measured on MI355X with 224 live rows x 48 heads, token by token
+// / short rows, 296 / 320 us at T = 4, 341 / 314 at 5, 432 / 320 at 8.
+constexpr int32_t kShortMinTokens = 5;
 
 KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
                             int32_t tokens_per_row, const void* qkv,
@@ -1044,6 +1049,14 @@ kda_status kda_decode_tokens(const kda_dims* d, int32_t tokens,
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return KDA_ERR_DEVICE;
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (tokens >= kShortMinTokens && tokens <= KDA_SHORT_ROWS_MAX_TOKENS) {
+    const KdaChunkedArgs a =
+        chunked_args(d, nullptr, tokens, qkv, conv_w, conv_state, rec_state,
+                     g, beta, gate, norm_w, state_idx, out);
+    return kda_short_rows_launch(a, d->batch, stream) == hipSuccess
+               ? KDA_OK
+               : KDA_ERR_LAUNCH;
+  }
   if (tokens >= kChunkedMinTokens) {
     // [B, T, ...] token-major buffers are the prefill layout with row n
     // owning tokens n*T .. n*T + T-1

@@ -91,7 +91,7 @@ def test_one_token_equals_single_step_kernel():
     assert d_rs <= 1e-6
 
 
-@pytest.mark.parametrize("T", [2, 4, 7])
+@pytest.mark.parametrize("T", [2, 4, 5, 7, 8])
 def test_tokens_match_successive_single_calls(T):
     """State kept on chip across T tokens == T calls through HBM."""
     w = synth.small(f"tt{T}", batch=24, heads=24, num_slots=30, seed=40 + T,
@@ -185,6 +185,43 @@ def test_tokens_b256_h48_full_size():
     print(f"[tokens b256] {st}", flush=True)
 
 
+SHORT_CASES = [
+    ("plain", 0, True, 8), ("nonorm", 0, False, 6),
+    ("tap_major", O.CONV_TAP_MAJOR, True, 8),
+    ("l2_silu", O.QK_L2NORM | O.GATE_SILU, True, 7),
+    ("no_conv_update", O.NO_CONV_UPDATE, True, 5),
+    ("tap_major_no_conv_update", O.CONV_TAP_MAJOR | O.NO_CONV_UPDATE, True,
+     6),
+]
+
+
+@pytest.mark.parametrize("name,flags,norm,T", SHORT_CASES,
+                         ids=[c[0] for c in SHORT_CASES])
+def test_tokens_5_to_8_take_the_short_row_form(name, flags, norm, T):
+    """Rows of 5 .. 8 tokens run the short-row kernel (the row's tokens as
+    one chunk, one workgroup per (row, head)); every variant must still
+    equal T successive single-token steps (the oracle).  Null and
+    out-of-range slots inside the batch."""
+    H = 24
+    w = synth.small(f"ts_{name}", batch=9, heads=H, num_slots=14,
+                    seed=130 + T, null_every=4, norm=norm,
+                    conv_w_sigma=0.05)
+    inp = synth.make_tokens(w, T)
+    inp["state_idx"][2] = -3
+    inp["state_idx"][5] = w.num_slots
+    if flags & O.CONV_TAP_MAJOR:
+        inp["conv_state"] = np.ascontiguousarray(
+            inp["conv_state"].transpose(0, 2, 1))
+    print(f"[tokens short] {name} H={H} T={T}", flush=True)
+    ref = O.decode_tokens(inp, heads=H, tokens=T, norm=norm, eps=w.eps,
+                          flags=flags)
+    got = run_tokens(w, inp, T, variants=flags)
+    st = check_tokens(w, inp, got, ref, T, flags)
+    if flags & O.NO_CONV_UPDATE:
+        assert np.array_equal(got["conv_state"], inp["conv_state"])
+    print(f"[tokens short] {name}: {st}", flush=True)
+
+
 CHUNKED_CASES = [
     ("plain", 0, True, 11), ("nonorm", 0, False, 12),
     ("tap_major", O.CONV_TAP_MAJOR, True, 16),
@@ -222,10 +259,12 @@ def test_tokens_from_11_take_the_chunked_form(name, flags, norm, T):
     print(f"[tokens chunked] {name}: {st}", flush=True)
 
 
-def test_tokens_10_and_11_agree_with_single_calls():
-    """Either side of the switch to the chunked form, against T single-token
-    kernel calls on the same inputs (and two chunks per row at 29)."""
-    for T in (10, 11, 29):
+def test_tokens_agree_with_single_calls_across_the_switches():
+    """Either side of each switch of form (token by token up to 4, short
+    rows 5 .. 8, token by token 9 and 10, chunked from 11), against T
+    single-token kernel calls on the same inputs (and two chunks per row at
+    29)."""
+    for T in (4, 5, 8, 10, 11, 29):
         w = synth.small(f"tsw{T}", batch=12, heads=48, num_slots=20,
                         seed=170 + T, null_every=5, conv_w_sigma=0.05)
         inp = synth.make_tokens(w, T)
@@ -242,12 +281,12 @@ def test_tokens_10_and_11_agree_with_single_calls():
                            inp["state_idx"], w.num_slots, w.heads)
 
 
-@pytest.mark.parametrize("T", [10, 16, 29])
+@pytest.mark.parametrize("T", [8, 10, 16, 29])
 def test_tokens_b256_h48_full_size(T):
-    """The batch-256, 48-head workload (32 null rows) with 10 tokens per
-    row (token by token), 16 (the chunked form, one chunk per row) and 29
-    (two chunks, the second ragged) at full size, every element against
-    the oracle.
+    """The batch-256, 48-head workload (32 null rows) with 8 tokens per row
+    (short rows: one chunk per (row, head)), 10 (token by token), 16 (the
+    chunked form, one chunk per row) and 29 (two chunks, the second ragged)
+    at full size, every element against the oracle.
     q/k are L2-normalised (unit keys, beta < 1: each update contracts the
     state along k).  Without it these inputs give beta |k|^2 near 40, and
     16 or more chained updates amplify fp32 rounding order by that factor
@@ -315,10 +354,11 @@ def test_tokens_maximum_T():
     print(f"[tokens T=1024] {st}", flush=True)
 
 
-@pytest.mark.parametrize("T", [4, 30])
+@pytest.mark.parametrize("T", [4, 8, 30])
 def test_tokens_graph_replay_matches_eager(T):
     """kda_decode_tokens captured in a HIP graph (T = 4 token by token,
-    T = 30 the chunked form) and replayed three times with eager work and
+    T = 8 short rows, T = 30 the chunked form) and replayed three times
+    with eager work and
     synchronisation in between: each replay equals the same eager call bit
     for bit (pools updated in place, so every replay advances the state)."""
     w = synth.small(f"tgraph{T}", batch=10, heads=24, num_slots=16,
@@ -362,12 +402,12 @@ def test_tokens_graph_replay_matches_eager(T):
         print(f"[tokens graph T={T}] replay {r} matches eager", flush=True)
 
 
-@pytest.mark.parametrize("T", [10, 11, 29])
+@pytest.mark.parametrize("T", [4, 5, 8, 10, 11, 29])
 def test_tokens_decay_contract_independent_of_T(T):
-    """The contract on g is the same on both sides of the switch to the
-    chunked form at 11 tokens: per element -inf (5 %, the key row is
-    forgotten), -1e30 (5 %), -100 (5 %, exp underflows), -1e-4 (5 %) or an
-    ordinary decay, against the oracle (exp(-inf) = 0 there)."""
+    """The contract on g is the same in every form (token by token, short
+    rows from 5 tokens, chunked from 11): per element -inf (5 %, the key
+    row is forgotten), -1e30 (5 %), -100 (5 %, exp underflows), -1e-4
+    (5 %) or an ordinary decay, against the oracle (exp(-inf) = 0 there)."""
     w = synth.small(f"tginf{T}", batch=6, heads=24, num_slots=10,
                     seed=310 + T, null_every=4, conv_w_sigma=0.05)
     inp = synth.make_tokens(w, T)
