@@ -33,10 +33,13 @@ if ROOT not in sys.path:
 METRIC = "KDA decode (seq*head) updates/sec + achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
-# kda_decode_tokens runs the short-row chunk kernel for rows of these many
-# tokens and the chunked matrix-core form from CHUNKED_MIN_TOKENS on
-SHORT_ROW_TOKENS = (5, 8)
-CHUNKED_MIN_TOKENS = 11
+# kda_decode_tokens runs the token-by-token kernel for rows of up to 4
+# tokens, the short-row kernel from 5 to 16 tokens (and up to 64 with at
+# least 4 (row, head) units per compute unit), else the chunked kernel
+SHORT_ROW_MIN_TOKENS = 5
+SHORT_ROW_ANY_UNITS_MAX_TOKENS = 16
+SHORT_ROW_MAX_TOKENS = 64
+SHORT_ROW_MIN_UNITS_PER_CU = 4
 # fp32 matrix flop per (16-token chunk, head) of the chunked form: K~S, Q~S
 # and the state update (3 x 2*16*128*128), A, B, the solve and B Delta
 # (4 x 2*16*16*128).  The kernel reaches fp32 precision on the bf16 matrix
@@ -247,8 +250,11 @@ def main():
         "launches_per_step": L,
         "wall_GBs": round(alg_bytes * L * K / wall / 1e9, 1),
     }
+    path = None
     if T > 1:
-        extra["tokens_path"] = tokens_path(T)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        path = tokens_path(T, w.batch * w.heads, cus)
+        extra["tokens_path"] = path
 
     if not args.no_graph:
         R = max(1, (max(10, K // 4) + L - 1) // L)      # steps per replay
@@ -292,7 +298,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic}
-    if T >= CHUNKED_MIN_TOKENS:
+    if path is not None and path.startswith("chunked"):
         # the chunked matrix-core form: priced in its fp32 MFMA work per
         # (16-token chunk, live row, head)
         chunks = -(-T // 16) * live_rows * w.heads      # per launch
@@ -329,17 +335,16 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def tokens_path(T):
-    """The kernel kda_decode_tokens runs for rows of T tokens."""
-    if SHORT_ROW_TOKENS[0] <= T <= SHORT_ROW_TOKENS[1]:
-        return "short rows: the row's tokens as one chunk, one workgroup " \
-               "per (row, head)"
-    if T < CHUNKED_MIN_TOKENS:
+def tokens_path(T, units, cus):
+    """The kernel kda_decode_tokens runs for rows of T tokens and `units`
+    (row, head) pairs on a device of `cus` compute units."""
+    if T < SHORT_ROW_MIN_TOKENS:
         return "token by token"
-    if T <= 32:
-        return "chunked rows mode: runs of (row, head) segments per " \
-               "workgroup as one chunk stream"
-    return "chunked: one workgroup per (row, head)"
+    if T <= SHORT_ROW_ANY_UNITS_MAX_TOKENS or (
+            T <= SHORT_ROW_MAX_TOKENS and
+            units >= SHORT_ROW_MIN_UNITS_PER_CU * cus):
+        return "short rows: chunks of 8 tokens, one workgroup per (row, head)"
+    return "chunked: chunks of 16 tokens, one workgroup per (row, head)"
 
 
 def bench_serving(args, np, torch, kda, synth, copies=8, calls=64):

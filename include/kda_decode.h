@@ -170,12 +170,12 @@ kda_status kda_decode_raw_gates(const kda_dims* dims, const void* qkv,
  * Other buffers, flags (KDA_BOUNDED_GATE excluded), rules and status codes
  * as kda_decode; T outside 1..1024 is KDA_ERR_INVALID_ARG.  With
  * KDA_NO_CONV_UPDATE every token sees the stored conv window, as T
- * successive calls with that flag would.  For T = 5 .. 8 the call runs
- * the chunk form of kda_prefill_chunked with the row's tokens as one chunk
- * (one workgroup per row and head), and from T = 11 on the chunked
- * matrix-core form itself (each row one sequence of T tokens, the rows of
- * a workgroup one pipelined chunk stream): equal up to rounding, and
- * faster there.  The contract on g does not change with T: any g <= 0
+ * successive calls with that flag would.  From T = 5 on, the call runs
+ * the chunk form of kda_prefill_chunked (the rows' tokens in chunks of 8,
+ * one workgroup per row and head, up to 16 tokens per row or up to 64 with
+ * at least 4 rows x heads per compute unit; else the chunked prefill
+ * kernel itself, each row one sequence of T tokens): equal up to rounding,
+ * and faster there.  The contract on g does not change with T: any g <= 0
  * down to -inf is accepted by every form (-inf forgets the key row, as
  * exp(-inf) = 0).
  */

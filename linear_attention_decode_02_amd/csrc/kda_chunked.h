@@ -27,28 +27,16 @@ struct KdaChunkedArgs {
   int32_t heads;
   int32_t num_slots;
   float eps;
-  int32_t num_seqs;        // set by the launcher
-  int32_t segs_per_group;  // set by the launcher (rows mode)
 };
 
-// Rows mode (cu_seqlens null, rows of at most KDA_CHUNKED_STREAM_MAX_TOKENS
-// tokens): a workgroup runs the chunks of at most KDA_CHUNKED_MAX_SEGS
-// (row, head) segments as one pipelined stream.  Its state goes back to
-// memory after every chunk, which longer rows would pay for once per
-// chunk: measured at 224 rows x 48 heads, 64 tokens per row take 1651 us
-// that way against 1335 us with one workgroup per (row, head).
-#define KDA_CHUNKED_MAX_SEGS 64
-#define KDA_CHUNKED_STREAM_MAX_TOKENS 32
-
-// Queues the chunked prefill of `num_seqs` sequences on `stream`: with
-// cu_seqlens one workgroup per (sequence, head); with tokens_per_row runs
-// of (row, head) segments per workgroup, about one workgroup per CU.
+// Queues the chunked prefill of `num_seqs` sequences (cu_seqlens) or rows
+// (tokens_per_row) on `stream`: one workgroup per (sequence, head).
 hipError_t kda_chunked_prefill_launch(const KdaChunkedArgs& args,
                                       int32_t num_seqs, hipStream_t stream);
 
-// Rows of 2 .. KDA_SHORT_ROWS_MAX_TOKENS tokens (cu_seqlens null): one
-// workgroup per (row, head), the row's tokens as one chunk, several
+// Rows of tokens_per_row tokens (cu_seqlens null, rg.raw_g null) through
+// the short-row kernel: one workgroup per (row, head), the row's tokens in
+// chunks of 8 with the state held in registers between them, several
 // workgroups per compute unit.
-#define KDA_SHORT_ROWS_MAX_TOKENS 8
 hipError_t kda_short_rows_launch(const KdaChunkedArgs& args, int32_t num_rows,
                                  hipStream_t stream);

@@ -26,14 +26,8 @@
 // Mapping: one 512-thread workgroup (8 waves) per (sequence, head), in two
 // roles that share each SIMD (waves w and w + 4 run on SIMD w), each role
 // in a loop of its own; three barriers per chunk hand the double-buffered
-// LDS tables over.  Rows mode (tokens_per_row, no cu_seqlens: the
-// multi-token decode, rows of up to 32 tokens): a workgroup takes a run of
-// up to 64 (row, head) segments in head-major order, about one workgroup
-// per CU, and pipelines their chunks as one stream -- the prep waves prepare the next segment's
-// first chunk while the state waves finish the current one, whose state
-// goes back to memory right after its update while the next segment's
-// state loads into the same registers (16-byte rows, a quad transpose
-// away from the accumulator layout).
+// LDS tables over.  Rows of tokens_per_row tokens (no cu_seqlens: the
+// multi-token decode of long rows) are sequences of equal length.
 //   * state waves 0-3 own value columns 32w .. 32w+31 of the [128 key,
 //     128 value] fp32 state, held for the whole sequence in registers in
 //     the accumulator layout of the 16x16 MFMAs (lane l: column l%16, key
@@ -82,8 +76,6 @@ constexpr int kD = 128;      // head dim (key = value)
 constexpr int kW = 4;        // conv width
 constexpr int kC = 16;       // tokens per chunk (one MFMA row block)
 constexpr int kThreads = 512;
-// stream mode: at most this many (row, head) segments per workgroup
-constexpr int kMaxSegs = KDA_CHUNKED_MAX_SEGS;
 constexpr int kLd = kD + 4;  // padded row of [kC][kD] tables (floats)
 constexpr int kTd = kC + 4;  // padded row of [kD][kC] and [kC][kC] tables
 constexpr float kLog2e = 1.44269504088896341f;
@@ -132,8 +124,6 @@ struct alignas(16) Smem {
   float o[kC][kLd];     // this chunk's outputs before the norm
   float nw[kD];         // norm weight
   int unsafe;           // exact path for the chunk being prepared
-  int seg_count;        // stream mode: this workgroup's live segments
-  int seg_list[kMaxSegs];
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) {
@@ -290,8 +280,7 @@ __device__ __forceinline__ f4 ld4(const float* p) {
 // the default (softplus) or the bounded gate.
 enum GateForm { kGateInput = 0, kGateSoftplus = 1, kGateBounded = 2 };
 
-// One segment of a workgroup's chunk stream: the tokens of one (sequence or
-// row, head).
+// The tokens of one (sequence or row, head): the workgroup's work.
 struct Seg {
   int64_t tb;  // first token
   int len;     // tokens
@@ -300,7 +289,7 @@ struct Seg {
   int nch;     // 16-token chunks
 };
 
-template <bool kNorm, int kGate, bool kStream>
+template <bool kNorm, int kGate>
 __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     KdaChunkedArgs p) {
   constexpr bool kRaw = kGate != kGateInput;
@@ -326,21 +315,11 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   const int ot = (tid & 255) >> 4;
   const int oc = 8 * (tid & 15);
 
-  // Segments.  Prefill: one (sequence, head) per workgroup, s = n H + h.
-  // Stream mode (rows of tokens_per_row tokens): a contiguous run of
-  // segments per workgroup in head-major order, s = h N + n, so a
-  // workgroup's conv weights change at most a few times; its chunks form
-  // one stream through the same pipeline.
+  // One (sequence, head) per workgroup, s = n H + h.
   auto seg_at = [&](int sg) -> Seg {
     Seg g;
-    int n;
-    if (kStream) {
-      g.h = sg / p.num_seqs;
-      n = sg - g.h * p.num_seqs;
-    } else {
-      n = sg / H;
-      g.h = sg - n * H;
-    }
+    const int n = sg / H;
+    g.h = sg - n * H;
     // token offsets in 64 bits: tb * 3C passes 2^31 from 58,255 tokens at
     // 96 heads
     const int64_t tb =
@@ -367,50 +346,12 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       o32[((g.tb + t) * C + col0) / 2 + idx % (kD / 2)] = 0u;
     }
   };
-  int nseg_live;
-  int seg0 = static_cast<int>(blockIdx.x);
-  if (!kStream) {
-    const Seg g = seg_at(seg0);
-    if (g.len == 0) return;
-    if (!live(g)) {
-      zero_outputs(g, tid, kThreads);
-      return;
-    }
-    nseg_live = 1;
-  } else {
-    const int nseg = p.num_seqs * H;
-    const int s_begin = static_cast<int>(blockIdx.x) * p.segs_per_group;
-    const int s_end = s_begin + p.segs_per_group < nseg
-                          ? s_begin + p.segs_per_group
-                          : nseg;
-    if (wave == 0) {
-      // lane i looks at segment s_begin + i; the live ones are listed in
-      // order
-      const int sg = s_begin + lane;
-      bool lv = false;
-      if (sg < s_end) lv = live(seg_at(sg));
-      const uint64_t m = __ballot(lv);
-      const int rank = __builtin_amdgcn_mbcnt_hi(
-          static_cast<uint32_t>(m >> 32),
-          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-      if (lv) sm.seg_list[rank] = sg;
-      if (lane == 0) sm.seg_count = __popcll(m);
-    }
-    if (state_wave) {
-      // segments with tokens and a null slot: +0.0 outputs
-      for (int sg = s_begin + pw; sg < s_end; sg += 4) {
-        const Seg g = seg_at(sg);
-        if (g.len > 0 && !live(g)) zero_outputs(g, lane, 64);
-      }
-    }
-    __syncthreads();  // the segment list
-    nseg_live = __builtin_amdgcn_readfirstlane(sm.seg_count);
-    if (nseg_live == 0) return;
+  const Seg seg = seg_at(static_cast<int>(blockIdx.x));
+  if (seg.len == 0) return;
+  if (!live(seg)) {
+    zero_outputs(seg, tid, kThreads);
+    return;
   }
-  auto seg_of = [&](int i) -> Seg {
-    return kStream ? seg_at(__builtin_amdgcn_readfirstlane(sm.seg_list[i]))
-                   : seg_at(seg0);
-  };
   if (!state_wave && tid - 256 < kD)  // norm weight, read by the state waves
     sm.nw[tid - 256] = kNorm ? p.norm_w[tid - 256] : 0.0f;
 
@@ -427,16 +368,14 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   uint32_t in_raw[3][7];
   uint32_t in_g[kC][2];  // fp32 pair, or (raw gates) a bf16 pair in [0]
   uint32_t in_b = 0;     // fp32 or (raw gates) bf16 bits
-  // stream mode: the segment's stored window, as loaded (tap-major: the
-  // channel pair in [0]; channel-major: one channel in each of [0], [1],
-  // combined where used, so no load waits at its issue)
-  uint32_t in_wv[2][3][kW - 1];
   // this lane's byte offsets in an input row (parts q, k, v) and a gate row
   const uint32_t off_raw = 4 * lane;
   const uint32_t off_part = 2 * static_cast<uint32_t>(C);
   const uint32_t off_g = (kRaw ? 4 : 8) * lane;
   // the stored conv window of channels 2 lane, 2 lane + 1 of each part,
-  // as loaded (see in_wv)
+  // as loaded (tap-major: the channel pair in [0]; channel-major: one
+  // channel in each of [0], [1], combined where used, so no load waits at
+  // its issue)
   auto load_window = [&](int slot, int64_t col0,
                          uint32_t (&wv)[2][3][kW - 1]) {
 #pragma unroll
@@ -500,19 +439,16 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       in_b = kRaw ? static_cast<uint32_t>(p.rg.raw_beta[e])
                   : __float_as_uint(p.beta[e]);
     }
-    if (kStream) load_window(sg.slot, col0, in_wv);
   };
   // per-head constants of the prep waves, for channels 2 lane, 2 lane + 1:
-  // conv weights, conv bias and dt_bias (raw gates); prefill mode also
-  // keeps the sequence's stored conv window
+  // conv weights, conv bias and dt_bias (raw gates), and the sequence's
+  // stored conv window
   f2 cwv[3][kW];
   f2 cbv[3] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
   f2 dtb = {0.f, 0.f};
   uint32_t wv[2][3][kW - 1];
-  int cw_h = -1;  // head the constants are loaded for
   auto load_constants = [&](const Seg& sg) {
     const int64_t col0 = static_cast<int64_t>(sg.h) * kD;
-    cw_h = sg.h;
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) {
 #pragma unroll
@@ -526,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     }
     if (kRaw)
       dtb = *reinterpret_cast<const f2*>(p.rg.dt_bias + col0 + 2 * lane);
-    if (!kStream) load_window(sg.slot, col0, wv);
+    load_window(sg.slot, col0, wv);
   };
 
   // a segment's new conv window, held from its last chunk's stage 1 to the
@@ -569,8 +505,6 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     const int c0 = ci * kC;
     const int nv = g.len - c0 < kC ? g.len - c0 : kC;
     const int h = g.h;
-    // stream mode: another head's weights (a few times per workgroup)
-    if (kStream && h != cw_h) load_constants(g);
     // this chunk's inputs (loaded a chunk ago)
     uint32_t raw[3][7];
 #pragma unroll
@@ -582,8 +516,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
       for (int e = 0; e < kW - 1; ++e)
-        wc[pp][e] = kStream ? in_wv[0][pp][e] | (in_wv[1][pp][e] << 16)
-                            : wv[0][pp][e] | (wv[1][pp][e] << 16);
+        wc[pp][e] = wv[0][pp][e] | (wv[1][pp][e] << 16);
     // per-token decays of keys 2 lane, 2 lane + 1 in log2 units
     f2 gl[kC];
     if (kRaw) {
@@ -988,11 +921,9 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   // ---- the pipeline --------------------------------------------------------
   // Each role runs a loop of its own (the state lives only in the state
   // waves' loop, so the prep code does not carry its registers); both walk
-  // the same chunk stream -- the chunks of this workgroup's live segments
-  // in order -- and meet at the same barriers: 3 before the first chunk,
-  // then 3 per chunk.
+  // the sequence's chunks in order and meet at the same barriers: 3 before
+  // the first chunk, then 3 per chunk.
   if (state_wave) {
-    int j = 0;  // stream position
     auto gate_row = [&](const Seg& sg, int ci) -> u4 {
       u4 gate_raw = {0u, 0u, 0u, 0u};
       if (kNorm) {
@@ -1004,99 +935,45 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       }
       return gate_raw;
     };
-    Seg g = seg_of(0);
     f4 S[2][8];
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) load_block(g, kb, S);
+    for (int kb = 0; kb < 8; ++kb) load_block(seg, kb, S);
     __syncthreads();  // first chunk's tables (and the norm weight)
     __syncthreads();  // its partial products
     __syncthreads();  // its A and B
-    if constexpr (!kStream) {
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) unpack_block(kb, S);
-      for (int ci = 0; ci < g.nch; ++ci, ++j) {
-        const u4 gate_raw = gate_row(g, ci);
-        state_chunk(j, S);
-        __syncthreads();  // outputs in sm.o; next chunk's tables ready
-        emit(g, ci, gate_raw);
-        __syncthreads();  // next chunk's partial products
-        __syncthreads();  // next chunk's A and B
-      }
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) store_block(g, kb, S);
-    } else {
-      for (int i = 0; i < nseg_live; ++i) {
-        // the next segment (the last one names itself: its state comes
-        // back once more, unused)
-        const Seg gn = seg_of(i + 1 < nseg_live ? i + 1 : i);
-        for (int ci = 0; ci < g.nch; ++ci, ++j) {
-          const u4 gate_raw = gate_row(g, ci);
-#pragma unroll
-          for (int kb = 0; kb < 8; ++kb) unpack_block(kb, S);
-          state_chunk(j, S);
-          // the state goes back to memory after every chunk and the state
-          // of the chunk that runs next -- this segment's again, or after
-          // its last chunk the next segment's -- loads into the same
-          // registers while the outputs are emitted (one unconditional
-          // reload: no register copies)
-          const Seg& gl = ci + 1 == g.nch ? gn : g;
-#pragma unroll
-          for (int kb = 0; kb < 8; ++kb) store_block(g, kb, S);
-          __builtin_amdgcn_sched_barrier(0);
-          asm volatile("" ::: "memory");
-#pragma unroll
-          for (int kb = 0; kb < 8; ++kb) load_block(gl, kb, S);
-          __syncthreads();  // outputs in sm.o; next chunk's tables ready
-          emit(g, ci, gate_raw);
-          __syncthreads();  // next chunk's partial products
-          __syncthreads();  // next chunk's A and B
-        }
-        g = gn;
-      }
+    for (int kb = 0; kb < 8; ++kb) unpack_block(kb, S);
+    for (int ci = 0; ci < seg.nch; ++ci) {
+      const u4 gate_raw = gate_row(seg, ci);
+      state_chunk(ci, S);
+      __syncthreads();  // outputs in sm.o; next chunk's tables ready
+      emit(seg, ci, gate_raw);
+      __syncthreads();  // next chunk's partial products
+      __syncthreads();  // next chunk's A and B
     }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) store_block(seg, kb, S);
   } else {
-    // the chunk being prepared (segment i, chunk ci, stream position j)
-    int i = 0, ci = 0, j = 0;
-    Seg g = seg_of(0);
-    // the chunk after (i, ci); false at the end of the stream
-    auto advance = [&](int& i_, int& ci_, Seg& g_) -> bool {
-      if (ci_ + 1 < g_.nch) {
-        ++ci_;
-        return true;
-      }
-      if (i_ + 1 >= nseg_live) return false;
-      ++i_;
-      ci_ = 0;
-      g_ = seg_of(i_);
-      return true;
-    };
-    int i2 = i, ci2 = ci;
-    Seg g2 = g;
-    bool more = advance(i2, ci2, g2);
-    load_constants(g);
-    load_chunk(g, 0);
-    prep_tables(std::false_type{}, g, 0, 0, g2, ci2);
+    // chunk ci is prepared while chunk ci - 1 runs; the inputs of the chunk
+    // after it (or its own again, after the last) are requested meanwhile
+    load_constants(seg);
+    load_chunk(seg, 0);
+    prep_tables(std::false_type{}, seg, 0, 0, seg, seg.nch > 1 ? 1 : 0);
     __syncthreads();
     prep_gram(0);
     __syncthreads();
     prep_reduce(0);
     __syncthreads();
-    while (more) {
-      i = i2;
-      ci = ci2;
-      g = g2;
-      ++j;
-      more = advance(i2, ci2, g2);
-      // (prefill mode only: rows mode rows are short, and the second copy
-      // costs its registers)
-      if (!kStream && ci > 0 && g.len - ci * kC >= kC && conv_update)
-        prep_tables(std::true_type{}, g, ci, j, g2, ci2);
+    for (int ci = 1; ci < seg.nch; ++ci) {
+      const int cn = ci + 1 < seg.nch ? ci + 1 : ci;
+      if (seg.len - ci * kC >= kC && conv_update)
+        prep_tables(std::true_type{}, seg, ci, ci, seg, cn);
       else
-        prep_tables(std::false_type{}, g, ci, j, g2, ci2);
+        prep_tables(std::false_type{}, seg, ci, ci, seg, cn);
       __syncthreads();
-      prep_gram(j);
+      prep_gram(ci);
       __syncthreads();
-      prep_reduce(j);
+      prep_reduce(ci);
       __syncthreads();
     }
     // the last chunk: nothing left to prepare
@@ -1107,13 +984,15 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 }
 
 // ===========================================================================
-// Short rows: the multi-token decode of rows of a few tokens (at most
-// kS = 8), one chunk per (row, head) and one 256-thread workgroup per
-// (row, head), four workgroups per compute unit, so that the state of some
-// units moves while others compute (the hardware dispatcher interleaves
-// them; there is no pipeline inside a workgroup).  The algebra is the chunk
-// form above with at most 8 tokens, which lets K~ (rows 0-7) and Q~ (rows
-// 8-15) share one 16-row A operand: K~ S and Q~ S are one product.
+// Short rows: the multi-token decode of rows of tokens_per_row tokens in
+// chunks of kS = 8, one 256-thread workgroup per (row, head) and several
+// workgroups per compute unit (four for rows of one chunk, three for longer
+// rows, whose state stays in registers from chunk to chunk), so that the
+// state of some units moves while others compute (the hardware dispatcher
+// interleaves them; there is no pipeline inside a workgroup).  The algebra
+// is the chunk form above with at most 8 tokens per chunk, which lets K~
+// (rows 0-7) and Q~ (rows 8-15) share one 16-row A operand: K~ S and Q~ S
+// are one product.
 //   * wave w owns value columns 32w .. 32w+31 of the state, held in the
 //     accumulator layout with the columns taken in pairs: lane l holds
 //     columns 32w + 2(l%16) and 32w + 2(l%16) + 1 (the two 16-column
@@ -1136,7 +1015,7 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 //     0 .. 7; the state update packs four piece products per MFMA (groups
 //     0-1: K^hi Dhi + K^mid Dhi, then K^mid Dmid + K^lo Dhi; groups 2-3:
 //     K^hi Dmid + K^hi Dlo, then K^mid Dlo + K^lo Dmid).
-constexpr int kS = 8;            // tokens of a short row at most
+constexpr int kS = 8;            // tokens per chunk
 constexpr int kSThreads = 256;   // 4 waves
 constexpr int kKhS = 16 + 4;     // dwords per split K^ key row (+ pad)
 
@@ -1165,28 +1044,26 @@ struct alignas(16) ShortSmem {
 // four workgroups per compute unit: 160 KiB of LDS, 128 VGPRs per lane
 static_assert(4 * sizeof(ShortSmem) <= 160 * 1024, "short-row LDS");
 
-template <bool kNorm>
-__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4)))
+template <bool kNorm, bool kMulti>
+__global__ __launch_bounds__(kSThreads)
+__attribute__((amdgpu_waves_per_eu(kMulti ? 3 : 4)))
 void kda_short_rows_kernel(KdaChunkedArgs p) {
   __shared__ ShortSmem sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int c = lane & 15;
-  const int gq = lane >> 4;
   const int H = p.heads;
   const int C = H * kD;
   const int C3 = 3 * C;
-  const int nv = p.tokens_per_row;  // 1 .. kS
+  const int T = p.tokens_per_row;  // tokens of the row
   const int unit = static_cast<int>(blockIdx.x);
   const int n = unit / H;
   const int h = unit - n * H;
-  const int64_t tb = static_cast<int64_t>(n) * nv;  // first token of the row
+  const int64_t tb = static_cast<int64_t>(n) * T;  // first token of the row
   const int64_t col0 = static_cast<int64_t>(h) * kD;
   const int slot = p.state_idx[n];
   if (slot <= 0 || slot >= p.num_slots) {
     // null row: +0.0 outputs, no state traffic
-    for (int i = tid; i < nv * (kD / 8); i += kSThreads)
+    for (int i = tid; i < T * (kD / 8); i += kSThreads)
       *reinterpret_cast<u4*>(p.out + (tb + i / (kD / 8)) * C + col0 +
                              8 * (i % (kD / 8))) = u4{0u, 0u, 0u, 0u};
     return;
@@ -1197,519 +1074,523 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
   const bool l2 = (flags & KDA_QK_L2NORM) != 0;
   const bool gate_silu = (flags & KDA_GATE_SILU) != 0;
 
-  // ---- inputs of tokens 2w, 2w+1, channels 2 lane, 2 lane + 1 ------------
-  // input rows 2w-3 .. 2w+1 (row indices clamped into the row; rows before
-  // it come from the stored window)
-  uint32_t raw[3][5];
-  {
-    const char* q0 = reinterpret_cast<const char*>(p.qkv + tb * C3 + col0);
-#pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      const int rel = 2 * wave - 3 + u;
-      const int rr = rel < 0 ? 0 : (rel < nv - 1 ? rel : nv - 1);
-      const gptr<const char> row = uniform_gptr(q0 + rr * (2 * C3));
-#pragma unroll
-      for (int pp = 0; pp < 3; ++pp)
-        raw[pp][u] = load_at<uint32_t>(row, 4 * lane + pp * (2 * C));
-    }
-  }
-  // the stored conv window (tap-major: the channel pair in [0];
-  // channel-major: one channel in each of [0], [1])
-  uint32_t wv[2][3][kW - 1];
-#pragma unroll
-  for (int pp = 0; pp < 3; ++pp)
-#pragma unroll
-    for (int e = 0; e < kW - 1; ++e) {
-      const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
-      if (tap_major) {
-        wv[0][pp][e] = *reinterpret_cast<const uint32_t*>(
-            p.conv_state + (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 +
-            ch);
-        wv[1][pp][e] = 0u;
-      } else {
-        const uint16_t* cs =
-            p.conv_state + (static_cast<int64_t>(slot) * C3 + ch) * (kW - 1) + e;
-        wv[0][pp][e] = cs[0];
-        wv[1][pp][e] = cs[kW - 1];
-      }
-    }
-  // decays of keys 2 lane, 2 lane + 1 for every token of the row
-  u2 in_g[kS];
-  {
-    const char* gb = reinterpret_cast<const char*>(p.g + (tb * H + h) * kD);
-#pragma unroll
-    for (int t = 0; t < kS; ++t) {
-      const int rr = t < nv - 1 ? t : nv - 1;
-      in_g[t] = load_at<u2>(uniform_gptr(gb + rr * (H * kD * 4)), 8 * lane);
-    }
-  }
-  float bt = 0.0f;  // beta of token 2w + lane (lanes 0, 1)
-  if (lane < 2) {
-    const int t = 2 * wave + lane;
-    bt = p.beta[(tb + (t < nv ? t : nv - 1)) * H + h];
-  }
-  f2 cwv[3][kW];
-#pragma unroll
-  for (int pp = 0; pp < 3; ++pp)
-#pragma unroll
-    for (int tap = 0; tap < kW; ++tap)
-      cwv[pp][tap] = *reinterpret_cast<const f2*>(
-          p.conv_w + (static_cast<int64_t>(pp) * kW + tap) * C + col0 +
-          2 * lane);
-  if (tid >= 128 && tid < 128 + kD)
-    sm.nw[tid - 128] = kNorm ? p.norm_w[tid - 128] : 0.0f;
-
-  // ---- prep ---------------------------------------------------------------
-  // cumulative decay (log2 units) over the row, its value at this wave's
-  // tokens and at the last one
-  f2 G = {0.f, 0.f};
-  f2 Gu[2] = {{0.f, 0.f}, {0.f, 0.f}};
-  float gmax = 0.0f;
-#pragma unroll
-  for (int t = 0; t < kS; ++t) {
-    f2 gl = f2{__uint_as_float(in_g[t].x), __uint_as_float(in_g[t].y)} * kLog2e;
-    gl = kda_decay_floor2(gl);
-    if (t < nv) G += gl;
-    gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
-    if (t == 2 * wave) Gu[0] = G;
-    if (t == 2 * wave + 1) Gu[1] = G;
-  }
-  // NaN counts as unsafe; the same verdict in every wave
-  const bool unsafe = __any(!(gmax <= kSafeExp2));
-  // conv + SiLU
-  uint32_t wc[3][kW - 1];
-#pragma unroll
-  for (int pp = 0; pp < 3; ++pp)
-#pragma unroll
-    for (int e = 0; e < kW - 1; ++e)
-      wc[pp][e] = wv[0][pp][e] | (wv[1][pp][e] << 16);
-  float y[2][3][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const bool valid = 2 * wave + u < nv;
-#pragma unroll
-    for (int pp = 0; pp < 3; ++pp)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float a = 0.0f;
-#pragma unroll
-        for (int tap = 0; tap < kW; ++tap) {
-          // input row of this tap relative to the row start: 2w + u - 3 +
-          // tap; only waves 0 and 1 reach before it (compile-time indices)
-          const int r0 = u - (kW - 1) + tap;  // for wave 0
-          uint32_t w2 = raw[pp][u + tap];
-          if (tap < kW - 1) {
-            if (conv_update) {
-              if (r0 < 0 && wave == 0) w2 = wc[pp][r0 < 0 ? (kW - 1) + r0 : 0];
-              if (r0 + 2 < 0 && wave == 1)
-                w2 = wc[pp][r0 + 2 < 0 ? (kW - 1) + r0 + 2 : 0];
-            } else {
-              w2 = wc[pp][tap];
-            }
-          }
-          a += cwv[pp][tap][e] * (e ? bf16_hi(w2) : bf16_lo(w2));
-        }
-        y[u][pp][e] = valid ? a * sigmoid_(a) : 0.0f;
-      }
-  }
-  // the new conv window: the row's last W-1 inputs (older ones from the
-  // stored window for rows shorter than that), held by wave (nv-1)/2 and
-  // written after the first barrier, once every wave has read the old one
-  const bool win_wave = conv_update && wave == (nv - 1) / 2;
-  uint32_t win_new[3][kW - 1];
-  if (win_wave) {
-#pragma unroll
-    for (int e = 0; e < kW - 1; ++e) {
-      const int idx = nv - (kW - 1) + e;    // token in the row
-      const int u = idx - (2 * wave - 3);   // its input row, 0..4
-#pragma unroll
-      for (int pp = 0; pp < 3; ++pp) {
-        uint32_t w = raw[pp][0];
-#pragma unroll
-        for (int q = 1; q < 5; ++q)
-          if (u == q) w = raw[pp][q];
-        if (idx < 0) {
-          w = wc[pp][0];
-#pragma unroll
-          for (int q = 1; q < kW - 1; ++q)
-            if (idx + (kW - 1) == q) w = wc[pp][q];
-        }
-        win_new[pp][e] = w;
-      }
-    }
-  }
-  if (l2) {
-    float ss[4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      ss[2 * u] = y[u][0][0] * y[u][0][0] + y[u][0][1] * y[u][0][1];
-      ss[2 * u + 1] = y[u][1][0] * y[u][1][0] + y[u][1][1] * y[u][1][1];
-    }
-    wave_sum<4>(ss);
-    const float qscale = 0.08838834764831845f;  // D^-1/2
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float rq = rsqrtf(ss[2 * u] + 1e-6f);
-      const float rk = rsqrtf(ss[2 * u + 1] + 1e-6f);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        y[u][0][e] = (y[u][0][e] * rq) * qscale;
-        y[u][1][e] = y[u][1][e] * rk;
-      }
-    }
-  }
-  // split tables
-  {
-    const int m = lane & 15;
-    const int pos = (4 * (lane >> 4) + ((m & 7) >> 1)) * 12 +
-                    (m >= 8 ? 2 : 0) + (m & 1);
-    auto put3 = [&](uint32_t* row, float a, float b) {
-      const Split3 x = split3(a, b);
-      row[pos] = x.h;
-      row[pos + 4] = x.m;
-      row[pos + 8] = x.l;
-    };
-    const f2 eG = {exp2_(G.x), exp2_(G.y)};
-    f2 khv[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = 2 * wave + u;
-      const f2 ee = {exp2_(Gu[u].x), exp2_(Gu[u].y)};
-      put3(sm.kq[t], y[u][1][0] * ee.x, y[u][1][1] * ee.y);
-      put3(sm.kq[kS + t], y[u][0][0] * ee.x, y[u][0][1] * ee.y);
-      *reinterpret_cast<f2*>(&sm.v[t][2 * lane]) = f2{y[u][2][0], y[u][2][1]};
-      if (!unsafe) {
-        const f2 ei = {exp2_(-Gu[u].x), exp2_(-Gu[u].y)};
-        khv[u] = f2{(y[u][1][0] * eG.x) * ei.x, (y[u][1][1] * eG.y) * ei.y};
-        put3(sm.u.kis[t], y[u][1][0] * ei.x, y[u][1][1] * ei.y);
-      } else {
-        khv[u] = f2{y[u][1][0] * exp2_(G.x - Gu[u].x),
-                    y[u][1][1] * exp2_(G.y - Gu[u].y)};
-        *reinterpret_cast<f2*>(&sm.u.ex.ki[t][2 * lane]) =
-            f2{y[u][1][0], y[u][1][1]};
-        *reinterpret_cast<f2*>(&sm.u.ex.graw[t][2 * lane]) = Gu[u];
-      }
-    }
-    // K^ pieces of tokens 2w, 2w+1 (one bf16 pair per piece) into the
-    // operand slots of both update products
-    const int q4 = 4 * (wave >> 1) + (wave & 1);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const Split3 a = split3(khv[0][e], khv[1][e]);
-      uint32_t* row = sm.kh[2 * lane + e];
-      row[q4] = a.h;
-      row[q4 + 2] = a.m;
-      row[8 + q4] = a.m;
-      row[8 + q4 + 2] = a.l;
-    }
-    if (wave == 0) {
-      *reinterpret_cast<f2*>(&sm.gam[2 * lane]) = eG;
-      if (lane == 0) sm.unsafe = unsafe ? 1 : 0;
-    }
-    if (lane < 2) {
-      const int t = 2 * wave + lane;
-      sm.beta[t] = t < nv ? bt : 0.0f;
-    }
-  }
-
-  // ---- the state: element (cb, kb, r) of lane l is key row 16 kb +
-  // 4 (l/16) + r, column 32 w + 2 (l%16) + cb -------------------------------
-  __builtin_amdgcn_sched_barrier(0);
+  // the state: element (cb, kb, r) of lane l is key row 16 kb + 4 (l/16) +
+  // r, column 32 w + 2 (l%16) + cb
   f4 S[2][8];
   const float* st_base =
       p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD) + 32 * wave;
-  const uint32_t st_lane = (4 * gq * kD + 2 * c) * 4;
+  // the row's tokens in chunks of kS
+  const int nch = kMulti ? (T + kS - 1) / kS : 1;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int c0 = ch * kS;
+    const int nv = T - c0 < kS ? T - c0 : kS;  // tokens of this chunk
+    const bool last = ch + 1 == nch;
+    // lane-derived values from an opaque copy of the thread id, so that no
+    // per-lane address stays live across the chunks
+    int tid_l = tid;
+    asm volatile("" : "+v"(tid_l));
+    const int lane = tid_l & 63;
+    const int c = lane & 15;
+    const int gq = lane >> 4;
+    const uint32_t st_lane = (4 * gq * kD + 2 * c) * 4;
+    // ---- inputs of tokens 2w, 2w+1, channels 2 lane, 2 lane + 1 ------------
+    // input rows 2w-3 .. 2w+1 (row indices clamped into the row; rows before
+    // it come from the stored window)
+    uint32_t raw[3][5];
+    {
+      const char* q0 = reinterpret_cast<const char*>(p.qkv + tb * C3 + col0);
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const gptr<const char> b = uniform_gptr(st_base + 16 * kb * kD);
-    uint32_t lo = st_lane;
-    asm volatile("" : "+v"(lo));
+      for (int u = 0; u < 5; ++u) {
+        const int rel = 2 * wave - 3 + u;
+        const int ra = c0 + rel;  // row-relative
+        const int rr = ra < 0 ? 0 : (ra < T - 1 ? ra : T - 1);
+        const gptr<const char> row = uniform_gptr(q0 + rr * (2 * C3));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f2 v2 = __builtin_nontemporal_load(
-          reinterpret_cast<gptr<const f2>>(b + lo + r * kD * 4));
-      S[0][kb][r] = v2.x;
-      S[1][kb][r] = v2.y;
+        for (int pp = 0; pp < 3; ++pp)
+          raw[pp][u] = load_at<uint32_t>(row, 4 * lane + pp * (2 * C));
+      }
     }
-  }
-  __syncthreads();  // tables
-  // every wave's reads of the old window are done: the new one goes out
-  if (win_wave) {
+    // the stored conv window (tap-major: the channel pair in [0];
+    // channel-major: one channel in each of [0], [1])
+    uint32_t wv[2][3][kW - 1] = {};
+    if (ch == 0 || !conv_update) {
 #pragma unroll
-    for (int e = 0; e < kW - 1; ++e)
+    for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
-      for (int pp = 0; pp < 3; ++pp) {
-        const uint32_t w = win_new[pp][e];
-        const int64_t ch = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
+      for (int e = 0; e < kW - 1; ++e) {
+        const int64_t chn = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
         if (tap_major) {
-          *reinterpret_cast<uint32_t*>(
-              p.conv_state +
-              (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + ch) = w;
+          wv[0][pp][e] = *reinterpret_cast<const uint32_t*>(
+              p.conv_state + (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 +
+              chn);
+          wv[1][pp][e] = 0u;
         } else {
-          uint16_t* cs = p.conv_state +
-                         (static_cast<int64_t>(slot) * C3 + ch) * (kW - 1) + e;
-          cs[0] = static_cast<uint16_t>(w);
-          cs[kW - 1] = static_cast<uint16_t>(w >> 16);
+          const uint16_t* cs =
+              p.conv_state + (static_cast<int64_t>(slot) * C3 + chn) * (kW - 1) + e;
+          wv[0][pp][e] = cs[0];
+          wv[1][pp][e] = cs[kW - 1];
         }
       }
-  }
-
-  // ---- Gram block of keys 32w .. 32w+31 ---------------------------------
-  if (!sm.unsafe) {
-    const int off = (4 * wave + gq) * 12;
-    const u4 z = {0u, 0u, 0u, 0u};
-    const bool bc = c < kS;
-    const u4 bh = bc ? ld_u4(&sm.u.kis[c & 7][off]) : z;
-    const u4 bm = bc ? ld_u4(&sm.u.kis[c & 7][off + 4]) : z;
-    const u4 bl = bc ? ld_u4(&sm.u.kis[c & 7][off + 8]) : z;
-    const f4 acc =
-        mfma6_(ld_u4(&sm.kq[c][off]), ld_u4(&sm.kq[c][off + 4]),
-               ld_u4(&sm.kq[c][off + 8]), bh, bm, bl, f4{0.f, 0.f, 0.f, 0.f});
-    if (c < kS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.part[wave][4 * gq + r][c] = acc[r];
     }
-  } else {
-    // large decay: each wave sums the rows of its own tokens exactly (one
-    // exponential per (t, s, key), k_s and G_s from LDS)
+    // decays of keys 2 lane, 2 lane + 1 for every token of the row
+    u2 in_g[kS];
+    {
+      const char* gb = reinterpret_cast<const char*>(p.g + (tb * H + h) * kD);
+#pragma unroll
+      for (int t = 0; t < kS; ++t) {
+        const int rr = c0 + t < T - 1 ? c0 + t : T - 1;
+        in_g[t] = load_at<u2>(uniform_gptr(gb + rr * (H * kD * 4)), 8 * lane);
+      }
+    }
+    float bt = 0.0f;  // beta of token 2w + lane (lanes 0, 1)
+    if (lane < 2) {
+      const int t = 2 * wave + lane;
+      bt = p.beta[(tb + (c0 + t < T ? c0 + t : T - 1)) * H + h];
+    }
+    // (reloaded per chunk from the cache rather than held across chunks)
+    const float* cw = p.conv_w + col0 + 2 * lane;
+    asm volatile("" : "+v"(cw));
+    f2 cwv[3][kW];
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+      for (int tap = 0; tap < kW; ++tap)
+        cwv[pp][tap] = *reinterpret_cast<const f2*>(
+            cw + (static_cast<int64_t>(pp) * kW + tap) * C);
+    if (ch == 0 && tid_l >= 128 && tid_l < 128 + kD)
+      sm.nw[tid_l - 128] = kNorm ? p.norm_w[tid_l - 128] : 0.0f;
+
+    // ---- prep ---------------------------------------------------------------
+    // cumulative decay (log2 units) over the row, its value at this wave's
+    // tokens and at the last one
+    f2 G = {0.f, 0.f};
+    f2 Gu[2] = {{0.f, 0.f}, {0.f, 0.f}};
+    float gmax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kS; ++t) {
+      f2 gl = f2{__uint_as_float(in_g[t].x), __uint_as_float(in_g[t].y)} * kLog2e;
+      gl = kda_decay_floor2(gl);
+      if (t < nv) G += gl;
+      gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+      if (t == 2 * wave) Gu[0] = G;
+      if (t == 2 * wave + 1) Gu[1] = G;
+    }
+    // NaN counts as unsafe; the same verdict in every wave
+    const bool unsafe = __any(!(gmax <= kSafeExp2));
+    // conv + SiLU
+    uint32_t wc[3][kW - 1];
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e)
+        wc[pp][e] = wv[0][pp][e] | (wv[1][pp][e] << 16);
+    float y[2][3][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int t = 2 * wave + u;
-      float ab[2 * kS];  // [A, B][s]
+      const bool valid = 2 * wave + u < nv;
 #pragma unroll
-      for (int i = 0; i < 2 * kS; ++i) ab[i] = 0.0f;
-      const f2 kt2 = *reinterpret_cast<const f2*>(&sm.u.ex.ki[t][2 * lane]);
-      const f2 gt2 = *reinterpret_cast<const f2*>(&sm.u.ex.graw[t][2 * lane]);
-#pragma unroll
-      for (int s_ = 0; s_ < kS; ++s_) {
-        if (s_ > t) continue;
-        const f2 ks2 = *reinterpret_cast<const f2*>(&sm.u.ex.ki[s_][2 * lane]);
-        const f2 gs2 =
-            *reinterpret_cast<const f2*>(&sm.u.ex.graw[s_][2 * lane]);
+      for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const float ks = ks2[e] * exp2_(gt2[e] - gs2[e]);
-          ab[s_] += kt2[e] * ks;
-          ab[kS + s_] += y[u][0][e] * ks;
+          float a = 0.0f;
+#pragma unroll
+          for (int tap = 0; tap < kW; ++tap) {
+            // input row of this tap relative to the row start: 2w + u - 3 +
+            // tap; only waves 0 and 1 of the first chunk reach before it
+            // (compile-time indices)
+            const int r0 = u - (kW - 1) + tap;  // for wave 0
+            uint32_t w2 = raw[pp][u + tap];
+            if (tap < kW - 1) {
+              if (conv_update) {
+                if (ch == 0 && r0 < 0 && wave == 0)
+                  w2 = wc[pp][r0 < 0 ? (kW - 1) + r0 : 0];
+                if (ch == 0 && r0 + 2 < 0 && wave == 1)
+                  w2 = wc[pp][r0 + 2 < 0 ? (kW - 1) + r0 + 2 : 0];
+              } else {
+                w2 = wc[pp][tap];
+              }
+            }
+            a += cwv[pp][tap][e] * (e ? bf16_hi(w2) : bf16_lo(w2));
+          }
+          y[u][pp][e] = valid ? a * sigmoid_(a) : 0.0f;
+        }
+    }
+    // the new conv window: the row's last W-1 inputs (older ones from the
+    // stored window for rows shorter than that), held in the last chunk by
+    // wave (nv-1)/2 and written after its first barrier, once every wave has
+    // read the old one
+    const bool win_wave = conv_update && last && wave == (nv - 1) / 2;
+    uint32_t win_new[3][kW - 1];
+    if (win_wave) {
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e) {
+        const int idx = T - (kW - 1) + e;          // token in the row
+        const int u = idx - c0 - (2 * wave - 3);   // its input row, 0..4
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+          uint32_t w = raw[pp][0];
+#pragma unroll
+          for (int q = 1; q < 5; ++q)
+            if (u == q) w = raw[pp][q];
+          if (idx < 0) {
+            w = wc[pp][0];
+#pragma unroll
+            for (int q = 1; q < kW - 1; ++q)
+              if (idx + (kW - 1) == q) w = wc[pp][q];
+          }
+          win_new[pp][e] = w;
         }
       }
-      wave_sum<2 * kS>(ab);
-      // lane i < 16 writes entry i of row t of A (i < 8) or B (part 0 holds
-      // the sum, parts 1-3 zero)
-      float val = 0.0f;
+    }
+    if (l2) {
+      float ss[4];
 #pragma unroll
-      for (int i = 0; i < 2 * kS; ++i)
-        if (lane == i) val = ab[i];
-      if (lane < 2 * kS) {
-        const int row = (lane >= kS ? kS : 0) + t;
-        const int s_ = lane & 7;
-        sm.part[0][row][s_] = val;
-        sm.part[1][row][s_] = 0.0f;
-        sm.part[2][row][s_] = 0.0f;
-        sm.part[3][row][s_] = 0.0f;
+      for (int u = 0; u < 2; ++u) {
+        ss[2 * u] = y[u][0][0] * y[u][0][0] + y[u][0][1] * y[u][0][1];
+        ss[2 * u + 1] = y[u][1][0] * y[u][1][0] + y[u][1][1] * y[u][1][1];
+      }
+      wave_sum<4>(ss);
+      const float qscale = 0.08838834764831845f;  // D^-1/2
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float rq = rsqrtf(ss[2 * u] + 1e-6f);
+        const float rk = rsqrtf(ss[2 * u + 1] + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          y[u][0][e] = (y[u][0][e] * rq) * qscale;
+          y[u][1][e] = y[u][1][e] * rk;
+        }
       }
     }
-  }
-  __syncthreads();  // Gram partials
-  if (tid < kS * kS) {
-    const int t = tid >> 3;
-    const int s_ = tid & 7;
-    const float a = (sm.part[0][t][s_] + sm.part[1][t][s_]) +
-                    (sm.part[2][t][s_] + sm.part[3][t][s_]);
-    const float b = (sm.part[0][kS + t][s_] + sm.part[1][kS + t][s_]) +
-                    (sm.part[2][kS + t][s_] + sm.part[3][kS + t][s_]);
-    sm.LT[s_][t] = s_ < t ? sm.beta[t] * a : 0.0f;
-    sm.Bm[t][s_] = s_ <= t ? b : 0.0f;
-  }
-  __syncthreads();  // A and B
-  // output lanes (threads 0-127): token tid/16, columns 8 (tid%16) .. +7
-  const int ot = tid >> 4;
-  const int oc = 8 * (tid & 15);
-  u4 gate_raw = {0u, 0u, 0u, 0u};
-  if (kNorm && tid < 16 * kS) {
-    const int rr = ot < nv - 1 ? ot : nv - 1;
-    gate_raw = *reinterpret_cast<const u4*>(p.gate + (tb + rr) * C + col0 + oc);
-  }
-
-  // ---- the chunk through the recurrence ---------------------------------
-  // X = [K~; Q~] S: accumulator rows 0-7 are K~ S, rows 8-15 Q~ S
-  f4 X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // split tables
+    {
+      const int m = lane & 15;
+      const int pos = (4 * (lane >> 4) + ((m & 7) >> 1)) * 12 +
+                      (m >= 8 ? 2 : 0) + (m & 1);
+      auto put3 = [&](uint32_t* row, float a, float b) {
+        const Split3 x = split3(a, b);
+        row[pos] = x.h;
+        row[pos + 4] = x.m;
+        row[pos + 8] = x.l;
+      };
+      const f2 eG = {exp2_(G.x), exp2_(G.y)};
+      f2 khv[2];
 #pragma unroll
-  for (int P = 0; P < 4; ++P) {
-    const int off = (4 * P + gq) * 12;
-    const u4 ah = ld_u4(&sm.kq[c][off]), am = ld_u4(&sm.kq[c][off + 4]),
-             al = ld_u4(&sm.kq[c][off + 8]);
+      for (int u = 0; u < 2; ++u) {
+        const int t = 2 * wave + u;
+        const f2 ee = {exp2_(Gu[u].x), exp2_(Gu[u].y)};
+        put3(sm.kq[t], y[u][1][0] * ee.x, y[u][1][1] * ee.y);
+        put3(sm.kq[kS + t], y[u][0][0] * ee.x, y[u][0][1] * ee.y);
+        *reinterpret_cast<f2*>(&sm.v[t][2 * lane]) = f2{y[u][2][0], y[u][2][1]};
+        if (!unsafe) {
+          const f2 ei = {exp2_(-Gu[u].x), exp2_(-Gu[u].y)};
+          khv[u] = f2{(y[u][1][0] * eG.x) * ei.x, (y[u][1][1] * eG.y) * ei.y};
+          put3(sm.u.kis[t], y[u][1][0] * ei.x, y[u][1][1] * ei.y);
+        } else {
+          khv[u] = f2{y[u][1][0] * exp2_(G.x - Gu[u].x),
+                      y[u][1][1] * exp2_(G.y - Gu[u].y)};
+          *reinterpret_cast<f2*>(&sm.u.ex.ki[t][2 * lane]) =
+              f2{y[u][1][0], y[u][1][1]};
+          *reinterpret_cast<f2*>(&sm.u.ex.graw[t][2 * lane]) = Gu[u];
+        }
+      }
+      // K^ pieces of tokens 2w, 2w+1 (one bf16 pair per piece) into the
+      // operand slots of both update products
+      const int q4 = 4 * (wave >> 1) + (wave & 1);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const Split3 s0 = split3(S[cb][2 * P][0], S[cb][2 * P][1]);
-      const Split3 s1 = split3(S[cb][2 * P][2], S[cb][2 * P][3]);
-      const Split3 s2 = split3(S[cb][2 * P + 1][0], S[cb][2 * P + 1][1]);
-      const Split3 s3 = split3(S[cb][2 * P + 1][2], S[cb][2 * P + 1][3]);
-      X[cb] = mfma6_(ah, am, al, u4{s0.h, s1.h, s2.h, s3.h},
-                     u4{s0.m, s1.m, s2.m, s3.m}, u4{s0.l, s1.l, s2.l, s3.l},
-                     X[cb]);
-    }
-  }
-  // row (c mod 8) of T = (I + L)^{-1}: (I + L)^T y = e_row, backward
-  const int rc = c & 7;
-  float yv[kS];
-#pragma unroll
-  for (int t = kS - 1; t >= 0; --t) {
-    float v = t == rc ? 1.0f : 0.0f;
-#pragma unroll
-    for (int s4 = 0; s4 < kS; s4 += 4) {
-      if (s4 + 3 <= t) continue;
-      const f4 lt = ld4(&sm.LT[t][s4]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (s4 + q > t) v -= lt[q] * yv[s4 + q];
-    }
-    yv[t] = v;
-  }
-  // A operands of the two small fp32 products, per k = 4 gq + j: the
-  // inverse [T 0; T 0] and [0 0; B 0]
-  f4 at, ab;
-  {
-    const f4 bl = ld4(&sm.Bm[rc][4 * (gq & 1)]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      at[j] = gq == 0 ? yv[j] : gq == 1 ? yv[4 + j] : 0.0f;
-      ab[j] = (c >= kS && gq < 2) ? bl[j] : 0.0f;
-    }
-  }
-  f4 dl[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int col = 32 * wave + 2 * c + cb;
-    f4 br;  // beta (V - K~ S) of tokens 4 gq + r (groups 0-1; else 0)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * (gq & 1) + r;
-      br[r] = gq < 2 ? sm.beta[t] * (sm.v[t][col] - X[cb][r]) : 0.0f;
-    }
-    dl[cb] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dl[cb] = mfma(at[j], br[j], dl[cb]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) X[cb] = mfma(ab[j], dl[cb][j], X[cb]);
-    if (gq >= 2) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.u.o[4 * (gq - 2) + r][col] = X[cb][r];
-    }
-  }
-  // state update: e^{G_last} S + K^T Delta
-  u4 b1[2], b2[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const Split3 d01 = split3(dl[cb][0], dl[cb][1]);
-    const Split3 d23 = split3(dl[cb][2], dl[cb][3]);
-    b1[cb] = gq < 2 ? u4{d01.h, d23.h, d01.h, d23.h}
-                    : u4{d01.m, d23.m, d01.l, d23.l};
-    b2[cb] = gq < 2 ? u4{d01.m, d23.m, d01.h, d23.h}
-                    : u4{d01.l, d23.l, d01.m, d23.m};
-  }
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const f4 gm = ld4(&sm.gam[16 * kb + 4 * gq]);
-    u4 a1 = ld_u4(&sm.kh[16 * kb + c][4 * (gq & 1)]);
-    if (gq >= 2) a1 = u4{a1.x, a1.y, a1.x, a1.y};
-    const u4 a2 = ld_u4(&sm.kh[16 * kb + c][8 + 4 * (gq & 1)]);
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      S[cb][kb] *= gm;
-      S[cb][kb] = mfma_bf(a1, b1[cb], S[cb][kb]);
-      S[cb][kb] = mfma_bf(a2, b2[cb], S[cb][kb]);
-    }
-  }
-  // the state back, in the layout it came in
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    gptr<char> b =
-        const_cast<gptr<char>>(uniform_gptr(st_base + 16 * kb * kD));
-    uint32_t lo = st_lane;
-    asm volatile("" : "+v"(lo));
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      __builtin_nontemporal_store(
-          f2{S[0][kb][r], S[1][kb][r]},
-          reinterpret_cast<gptr<f2>>(b + lo + r * kD * 4));
-  }
-  __syncthreads();  // outputs in sm.u.o
-
-  // ---- gated RMSNorm and bf16 outputs: 16 lanes per token ---------------
-  if (tid < 16 * kS) {
-    const f4 v0 = ld4(&sm.u.o[ot][oc]);
-    const f4 v1 = ld4(&sm.u.o[ot][oc + 4]);
-    float yo[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    if (kNorm) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss += yo[j] * yo[j];
-      ss = row_sum16(ss);
-      const float rs = rsqrtf(ss * (1.0f / kD) + p.eps);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t w2 = gate_raw[j >> 1];
-        const float gv = (j & 1) ? bf16_hi(w2) : bf16_lo(w2);
-        const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
-        yo[j] = ((yo[j] * rs) * sm.nw[oc + j]) * ga;
+      for (int e = 0; e < 2; ++e) {
+        const Split3 a = split3(khv[0][e], khv[1][e]);
+        uint32_t* row = sm.kh[2 * lane + e];
+        row[q4] = a.h;
+        row[q4 + 2] = a.m;
+        row[8 + q4] = a.m;
+        row[8 + q4 + 2] = a.l;
+      }
+      if (wave == 0) {
+        *reinterpret_cast<f2*>(&sm.gam[2 * lane]) = eG;
+        if (lane == 0) sm.unsafe = unsafe ? 1 : 0;
+      }
+      if (lane < 2) {
+        const int t = 2 * wave + lane;
+        sm.beta[t] = t < nv ? bt : 0.0f;
       }
     }
-    if (ot < nv) {
-      const u4 pk = {pack_bf16(yo[0], yo[1]), pack_bf16(yo[2], yo[3]),
-                     pack_bf16(yo[4], yo[5]), pack_bf16(yo[6], yo[7])};
-      *reinterpret_cast<u4*>(p.out + (tb + ot) * C + col0 + oc) = pk;
+
+    // ---- the state (first chunk; it stays in registers across the chunks)
+    if (ch == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const gptr<const char> b = uniform_gptr(st_base + 16 * kb * kD);
+        uint32_t lo = st_lane;
+        asm volatile("" : "+v"(lo));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f2 v2 = __builtin_nontemporal_load(
+              reinterpret_cast<gptr<const f2>>(b + lo + r * kD * 4));
+          S[0][kb][r] = v2.x;
+          S[1][kb][r] = v2.y;
+        }
+      }
     }
+    __syncthreads();  // tables
+    // every wave's reads of the old window are done: the new one goes out
+    if (win_wave) {
+#pragma unroll
+      for (int e = 0; e < kW - 1; ++e)
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+          const uint32_t w = win_new[pp][e];
+          const int64_t chn = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
+          if (tap_major) {
+            *reinterpret_cast<uint32_t*>(
+                p.conv_state +
+                (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + chn) = w;
+          } else {
+            uint16_t* cs = p.conv_state +
+                           (static_cast<int64_t>(slot) * C3 + chn) * (kW - 1) + e;
+            cs[0] = static_cast<uint16_t>(w);
+            cs[kW - 1] = static_cast<uint16_t>(w >> 16);
+          }
+        }
+    }
+
+    // ---- Gram block of keys 32w .. 32w+31 ---------------------------------
+    if (!sm.unsafe) {
+      const int off = (4 * wave + gq) * 12;
+      const u4 z = {0u, 0u, 0u, 0u};
+      const bool bc = c < kS;
+      const u4 bh = bc ? ld_u4(&sm.u.kis[c & 7][off]) : z;
+      const u4 bm = bc ? ld_u4(&sm.u.kis[c & 7][off + 4]) : z;
+      const u4 bl = bc ? ld_u4(&sm.u.kis[c & 7][off + 8]) : z;
+      const f4 acc =
+          mfma6_(ld_u4(&sm.kq[c][off]), ld_u4(&sm.kq[c][off + 4]),
+                 ld_u4(&sm.kq[c][off + 8]), bh, bm, bl, f4{0.f, 0.f, 0.f, 0.f});
+      if (c < kS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.part[wave][4 * gq + r][c] = acc[r];
+      }
+    } else {
+      // large decay: each wave sums the rows of its own tokens exactly (one
+      // exponential per (t, s, key), k_s and G_s from LDS)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = 2 * wave + u;
+        float ab[2 * kS];  // [A, B][s]
+#pragma unroll
+        for (int i = 0; i < 2 * kS; ++i) ab[i] = 0.0f;
+        const f2 kt2 = *reinterpret_cast<const f2*>(&sm.u.ex.ki[t][2 * lane]);
+        const f2 gt2 = *reinterpret_cast<const f2*>(&sm.u.ex.graw[t][2 * lane]);
+#pragma unroll
+        for (int s_ = 0; s_ < kS; ++s_) {
+          if (s_ > t) continue;
+          const f2 ks2 = *reinterpret_cast<const f2*>(&sm.u.ex.ki[s_][2 * lane]);
+          const f2 gs2 =
+              *reinterpret_cast<const f2*>(&sm.u.ex.graw[s_][2 * lane]);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float ks = ks2[e] * exp2_(gt2[e] - gs2[e]);
+            ab[s_] += kt2[e] * ks;
+            ab[kS + s_] += y[u][0][e] * ks;
+          }
+        }
+        wave_sum<2 * kS>(ab);
+        // lane i < 16 writes entry i of row t of A (i < 8) or B (part 0 holds
+        // the sum, parts 1-3 zero)
+        float val = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2 * kS; ++i)
+          if (lane == i) val = ab[i];
+        if (lane < 2 * kS) {
+          const int row = (lane >= kS ? kS : 0) + t;
+          const int s_ = lane & 7;
+          sm.part[0][row][s_] = val;
+          sm.part[1][row][s_] = 0.0f;
+          sm.part[2][row][s_] = 0.0f;
+          sm.part[3][row][s_] = 0.0f;
+        }
+      }
+    }
+    __syncthreads();  // Gram partials
+    if (tid_l < kS * kS) {
+      const int t = tid_l >> 3;
+      const int s_ = tid_l & 7;
+      const float a = (sm.part[0][t][s_] + sm.part[1][t][s_]) +
+                      (sm.part[2][t][s_] + sm.part[3][t][s_]);
+      const float b = (sm.part[0][kS + t][s_] + sm.part[1][kS + t][s_]) +
+                      (sm.part[2][kS + t][s_] + sm.part[3][kS + t][s_]);
+      sm.LT[s_][t] = s_ < t ? sm.beta[t] * a : 0.0f;
+      sm.Bm[t][s_] = s_ <= t ? b : 0.0f;
+    }
+    __syncthreads();  // A and B
+    // output lanes (threads 0-127): token tid_l/16, columns 8 (tid_l%16) .. +7
+    const int ot = tid_l >> 4;
+    const int oc = 8 * (tid_l & 15);
+    u4 gate_raw = {0u, 0u, 0u, 0u};
+    if (kNorm && tid_l < 16 * kS) {
+      const int rr = c0 + ot < T - 1 ? c0 + ot : T - 1;
+      gate_raw = *reinterpret_cast<const u4*>(p.gate + (tb + rr) * C + col0 + oc);
+    }
+
+    // ---- the chunk through the recurrence ---------------------------------
+    // X = [K~; Q~] S: accumulator rows 0-7 are K~ S, rows 8-15 Q~ S
+    f4 X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int P = 0; P < 4; ++P) {
+      const int off = (4 * P + gq) * 12;
+      const u4 ah = ld_u4(&sm.kq[c][off]), am = ld_u4(&sm.kq[c][off + 4]),
+               al = ld_u4(&sm.kq[c][off + 8]);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const Split3 s0 = split3(S[cb][2 * P][0], S[cb][2 * P][1]);
+        const Split3 s1 = split3(S[cb][2 * P][2], S[cb][2 * P][3]);
+        const Split3 s2 = split3(S[cb][2 * P + 1][0], S[cb][2 * P + 1][1]);
+        const Split3 s3 = split3(S[cb][2 * P + 1][2], S[cb][2 * P + 1][3]);
+        X[cb] = mfma6_(ah, am, al, u4{s0.h, s1.h, s2.h, s3.h},
+                       u4{s0.m, s1.m, s2.m, s3.m}, u4{s0.l, s1.l, s2.l, s3.l},
+                       X[cb]);
+      }
+    }
+    // row (c mod 8) of T = (I + L)^{-1}: (I + L)^T y = e_row, backward
+    const int rc = c & 7;
+    float yv[kS];
+#pragma unroll
+    for (int t = kS - 1; t >= 0; --t) {
+      float v = t == rc ? 1.0f : 0.0f;
+#pragma unroll
+      for (int s4 = 0; s4 < kS; s4 += 4) {
+        if (s4 + 3 <= t) continue;
+        const f4 lt = ld4(&sm.LT[t][s4]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (s4 + q > t) v -= lt[q] * yv[s4 + q];
+      }
+      yv[t] = v;
+    }
+    // A operands of the two small fp32 products, per k = 4 gq + j: the
+    // inverse [T 0; T 0] and [0 0; B 0]
+    f4 at, ab;
+    {
+      const f4 bl = ld4(&sm.Bm[rc][4 * (gq & 1)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        at[j] = gq == 0 ? yv[j] : gq == 1 ? yv[4 + j] : 0.0f;
+        ab[j] = (c >= kS && gq < 2) ? bl[j] : 0.0f;
+      }
+    }
+    f4 dl[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int col = 32 * wave + 2 * c + cb;
+      f4 br;  // beta (V - K~ S) of tokens 4 gq + r (groups 0-1; else 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * (gq & 1) + r;
+        br[r] = gq < 2 ? sm.beta[t] * (sm.v[t][col] - X[cb][r]) : 0.0f;
+      }
+      dl[cb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dl[cb] = mfma(at[j], br[j], dl[cb]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) X[cb] = mfma(ab[j], dl[cb][j], X[cb]);
+      if (gq >= 2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.u.o[4 * (gq - 2) + r][col] = X[cb][r];
+      }
+    }
+    // state update: e^{G_last} S + K^T Delta
+    u4 b1[2], b2[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const Split3 d01 = split3(dl[cb][0], dl[cb][1]);
+      const Split3 d23 = split3(dl[cb][2], dl[cb][3]);
+      b1[cb] = gq < 2 ? u4{d01.h, d23.h, d01.h, d23.h}
+                      : u4{d01.m, d23.m, d01.l, d23.l};
+      b2[cb] = gq < 2 ? u4{d01.m, d23.m, d01.h, d23.h}
+                      : u4{d01.l, d23.l, d01.m, d23.m};
+    }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const f4 gm = ld4(&sm.gam[16 * kb + 4 * gq]);
+      u4 a1 = ld_u4(&sm.kh[16 * kb + c][4 * (gq & 1)]);
+      if (gq >= 2) a1 = u4{a1.x, a1.y, a1.x, a1.y};
+      const u4 a2 = ld_u4(&sm.kh[16 * kb + c][8 + 4 * (gq & 1)]);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        S[cb][kb] *= gm;
+        S[cb][kb] = mfma_bf(a1, b1[cb], S[cb][kb]);
+        S[cb][kb] = mfma_bf(a2, b2[cb], S[cb][kb]);
+      }
+    }
+    // the state back after the last chunk, in the layout it came in
+    if (last) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        gptr<char> b =
+            const_cast<gptr<char>>(uniform_gptr(st_base + 16 * kb * kD));
+        uint32_t lo = st_lane;
+        asm volatile("" : "+v"(lo));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_nontemporal_store(
+              f2{S[0][kb][r], S[1][kb][r]},
+              reinterpret_cast<gptr<f2>>(b + lo + r * kD * 4));
+      }
+    }
+    __syncthreads();  // outputs in sm.u.o
+
+    // ---- gated RMSNorm and bf16 outputs: 16 lanes per token ---------------
+    if (tid_l < 16 * kS) {
+      const f4 v0 = ld4(&sm.u.o[ot][oc]);
+      const f4 v1 = ld4(&sm.u.o[ot][oc + 4]);
+      float yo[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      if (kNorm) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += yo[j] * yo[j];
+        ss = row_sum16(ss);
+        const float rs = rsqrtf(ss * (1.0f / kD) + p.eps);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w2 = gate_raw[j >> 1];
+          const float gv = (j & 1) ? bf16_hi(w2) : bf16_lo(w2);
+          const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
+          yo[j] = ((yo[j] * rs) * sm.nw[oc + j]) * ga;
+        }
+      }
+      if (ot < nv) {
+        const u4 pk = {pack_bf16(yo[0], yo[1]), pack_bf16(yo[2], yo[3]),
+                       pack_bf16(yo[4], yo[5]), pack_bf16(yo[6], yo[7])};
+        *reinterpret_cast<u4*>(p.out + (tb + c0 + ot) * C + col0 + oc) = pk;
+      }
+    }
+      if (!last) __syncthreads();  // the tables are free for the next chunk
   }
 }
 
-template <int kGate, bool kStream>
+template <int kGate>
 void launch_gate(const KdaChunkedArgs& args, dim3 grid, hipStream_t stream) {
   if (args.flags & KDA_OUTPUT_NORM)
-    hipLaunchKernelGGL((kda_chunked_prefill_kernel<true, kGate, kStream>),
-                       grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((kda_chunked_prefill_kernel<true, kGate>), grid,
+                       dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((kda_chunked_prefill_kernel<false, kGate, kStream>),
-                       grid, dim3(kThreads), 0, stream, args);
-}
-
-template <bool kStream>
-void launch_mode(const KdaChunkedArgs& args, dim3 grid, hipStream_t stream) {
-  if (!args.rg.raw_g)
-    launch_gate<kGateInput, kStream>(args, grid, stream);
-  else if (args.flags & KDA_BOUNDED_GATE)
-    launch_gate<kGateBounded, kStream>(args, grid, stream);
-  else
-    launch_gate<kGateSoftplus, kStream>(args, grid, stream);
+    hipLaunchKernelGGL((kda_chunked_prefill_kernel<false, kGate>), grid,
+                       dim3(kThreads), 0, stream, args);
 }
 
 }  // namespace
 
 hipError_t kda_chunked_prefill_launch(const KdaChunkedArgs& args,
                                       int32_t num_seqs, hipStream_t stream) {
-  KdaChunkedArgs a = args;
-  a.num_seqs = num_seqs;
-  const int64_t nseg = static_cast<int64_t>(num_seqs) * args.heads;
-  if (args.cu_seqlens || args.tokens_per_row > KDA_CHUNKED_STREAM_MAX_TOKENS) {
-    // one (sequence, head) per workgroup
-    a.segs_per_group = 1;
-    launch_mode<false>(a, dim3(static_cast<unsigned>(nseg)), stream);
-  } else {
-    // rows of a few tokens: runs of segments per workgroup, one workgroup
-    // per compute unit where the rows allow (at most kMaxSegs each)
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                              dev) != hipSuccess ||
-        cus < 1)
-      cus = 256;
-    int64_t per = (nseg + cus - 1) / cus;
-    if (per < 1) per = 1;
-    if (per > kMaxSegs) per = kMaxSegs;
-    a.segs_per_group = static_cast<int32_t>(per);
-    launch_mode<true>(a, dim3(static_cast<unsigned>((nseg + per - 1) / per)),
-                      stream);
-  }
+  // one (sequence, head) per workgroup
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(num_seqs) *
+                                        args.heads));
+  if (!args.rg.raw_g)
+    launch_gate<kGateInput>(args, grid, stream);
+  else if (args.flags & KDA_BOUNDED_GATE)
+    launch_gate<kGateBounded>(args, grid, stream);
+  else
+    launch_gate<kGateSoftplus>(args, grid, stream);
   return hipGetLastError();
 }
 
@@ -1717,11 +1598,20 @@ hipError_t kda_short_rows_launch(const KdaChunkedArgs& args, int32_t num_rows,
                                  hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(num_rows) *
                                         args.heads));
-  if (args.flags & KDA_OUTPUT_NORM)
-    hipLaunchKernelGGL(kda_short_rows_kernel<true>, grid, dim3(kSThreads), 0,
-                       stream, args);
-  else
-    hipLaunchKernelGGL(kda_short_rows_kernel<false>, grid, dim3(kSThreads), 0,
-                       stream, args);
+  const bool norm = (args.flags & KDA_OUTPUT_NORM) != 0;
+  if (args.tokens_per_row > kS) {
+    if (norm)
+      hipLaunchKernelGGL((kda_short_rows_kernel<true, true>), grid,
+                         dim3(kSThreads), 0, stream, args);
+    else
+      hipLaunchKernelGGL((kda_short_rows_kernel<false, true>), grid,
+                         dim3(kSThreads), 0, stream, args);
+  } else if (norm) {
+    hipLaunchKernelGGL((kda_short_rows_kernel<true, false>), grid,
+                       dim3(kSThreads), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((kda_short_rows_kernel<false, false>), grid,
+                       dim3(kSThreads), 0, stream, args);
+  }
   return hipGetLastError();
 }

@@ -893,17 +893,35 @@ Params base_params(const kda_dims* d, const void* qkv, const float* conv_w,
   return p;
 }
 
-// From this many tokens per row on, kda_decode_tokens runs the chunked
-// (matrix-core) kernel, which pipelines the rows of a workgroup as one
-// chunk stream: measured on MI355X with 224 live rows x 48 heads, token by
-// token / chunked, 507 / 537 us at T = 9, 548 / 544 at 10, 567 / 536 at
-// 11, 602 / 527 at 12 (a chunk is 16 tokens: up to 16 cost one).
-constexpr int32_t kChunkedMinTokens = 11;
-// Rows of kShortMinTokens .. KDA_SHORT_ROWS_MAX_TOKENS tokens run the
-// short-row kernel (the row's tokens as one chunk, one workgroup per (row,
-// head)): measured on MI355X with 224 live rows x 48 heads, token by token
-// / short rows, 296 / 320 us at T = 4, 341 / 314 at 5, 432 / 320 at 8.
+// Which form kda_decode_tokens runs for rows of T tokens, from timings on
+// MI355X (us per call):
+//   * T = 2 .. 4: token by token (224 live rows x 48 heads, token by token
+//     / short rows: 296 / 320 at T = 4);
+//   * T = 5 .. 16: the short-row kernel (341 / 314 at T = 5, 432 / 320 at
+//     T = 8; against the chunked kernel 494 / 528 at T = 12);
+//   * T = 17 .. 64 with at least 4 (row, head) units per compute unit: the
+//     short-row kernel (224 x 48: 619 / 889 at T = 24, 1360 / 1429 at 64;
+//     64 x 24: 117 / 132 at 32);  with fewer units, and from T = 65: the
+//     chunked kernel, whose prep overlaps the state chain of each
+//     (row, head) (1 x 12: 30 / 32 at T = 32, 33 / 57 at 64; 224 x 48:
+//     2199 / 2307 at 128).
 constexpr int32_t kShortMinTokens = 5;
+constexpr int32_t kShortAnyUnitsMaxTokens = 16;
+constexpr int32_t kShortMaxTokens = 64;
+constexpr int64_t kShortMinUnitsPerCU = 4;
+
+// Whether kda_decode_tokens runs the short-row kernel for these rows.
+bool use_short_rows(const kda_dims* d, int32_t tokens, int dev) {
+  if (tokens < kShortMinTokens || tokens > kShortMaxTokens) return false;
+  if (tokens <= kShortAnyUnitsMaxTokens) return true;
+  int cus = 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  return static_cast<int64_t>(d->batch) * d->num_heads >=
+         kShortMinUnitsPerCU * cus;
+}
 
 KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
                             int32_t tokens_per_row, const void* qkv,
@@ -1049,7 +1067,7 @@ kda_status kda_decode_tokens(const kda_dims* d, int32_t tokens,
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return KDA_ERR_DEVICE;
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (tokens >= kShortMinTokens && tokens <= KDA_SHORT_ROWS_MAX_TOKENS) {
+  if (use_short_rows(d, tokens, dev)) {
     const KdaChunkedArgs a =
         chunked_args(d, nullptr, tokens, qkv, conv_w, conv_state, rec_state,
                      g, beta, gate, norm_w, state_idx, out);
@@ -1057,7 +1075,7 @@ kda_status kda_decode_tokens(const kda_dims* d, int32_t tokens,
                ? KDA_OK
                : KDA_ERR_LAUNCH;
   }
-  if (tokens >= kChunkedMinTokens) {
+  if (tokens > kShortAnyUnitsMaxTokens) {
     // [B, T, ...] token-major buffers are the prefill layout with row n
     // owning tokens n*T .. n*T + T-1
     if (static_cast<int64_t>(d->batch) * tokens > INT32_MAX)

@@ -222,6 +222,40 @@ def test_tokens_5_to_8_take_the_short_row_form(name, flags, norm, T):
     print(f"[tokens short] {name}: {st}", flush=True)
 
 
+SHORT_LONG_CASES = [
+    ("nonorm", 0, False, 17), ("tap_major", O.CONV_TAP_MAJOR, True, 20),
+    ("no_conv_update", O.NO_CONV_UPDATE, True, 33),
+    ("l2_silu", O.QK_L2NORM | O.GATE_SILU, True, 64),
+]
+
+
+@pytest.mark.parametrize("name,flags,norm,T", SHORT_LONG_CASES,
+                         ids=[c[0] for c in SHORT_LONG_CASES])
+def test_tokens_17_to_64_with_many_units_take_the_short_row_form(
+        name, flags, norm, T):
+    """Rows of 17 .. 64 tokens with at least 4 (row, head) units per compute
+    unit (here 48 rows x 24 heads = 1,152) run the short-row kernel in
+    chunks of 8 (3 to 8 per row, the last one ragged at 17, 20 and 33);
+    every variant against the oracle, null and negative slots inside."""
+    H = 24
+    w = synth.small(f"tl_{name}", batch=48, heads=H, num_slots=56,
+                    seed=230 + T, null_every=6, norm=norm,
+                    conv_w_sigma=0.5 if flags & O.QK_L2NORM else 0.05)
+    inp = synth.make_tokens(w, T)
+    inp["state_idx"][3] = -1
+    if flags & O.CONV_TAP_MAJOR:
+        inp["conv_state"] = np.ascontiguousarray(
+            inp["conv_state"].transpose(0, 2, 1))
+    print(f"[tokens short long] {name} H={H} T={T}", flush=True)
+    ref = O.decode_tokens(inp, heads=H, tokens=T, norm=norm, eps=w.eps,
+                          flags=flags)
+    got = run_tokens(w, inp, T, variants=flags)
+    st = check_tokens(w, inp, got, ref, T, flags)
+    if flags & O.NO_CONV_UPDATE:
+        assert np.array_equal(got["conv_state"], inp["conv_state"])
+    print(f"[tokens short long] {name}: {st}", flush=True)
+
+
 CHUNKED_CASES = [
     ("plain", 0, True, 11), ("nonorm", 0, False, 12),
     ("tap_major", O.CONV_TAP_MAJOR, True, 16),
@@ -235,11 +269,12 @@ CHUNKED_CASES = [
 
 @pytest.mark.parametrize("name,flags,norm,T", CHUNKED_CASES,
                          ids=[c[0] for c in CHUNKED_CASES])
-def test_tokens_from_11_take_the_chunked_form(name, flags, norm, T):
-    """From 11 tokens per row the call runs the chunked matrix-core form
-    (the rows of a workgroup one chunk stream; from 17 tokens two chunks
-    per row); it must still equal T successive single-token steps (the
-    oracle)."""
+def test_tokens_multi_chunk_forms(name, flags, norm, T):
+    """Rows longer than one chunk: 11 .. 16 tokens run the short-row kernel
+    in two chunks of up to 8; from 17 tokens, with these 216 (row, head)
+    units (fewer than 4 per compute unit), the chunked kernel in chunks of
+    16 (two or three per row).  Every variant must still equal T successive
+    single-token steps (the oracle)."""
     H = 24
     w = synth.small(f"tc_{name}", batch=9, heads=H, num_slots=14,
                     seed=150 + T, null_every=4, norm=norm,
@@ -261,10 +296,9 @@ def test_tokens_from_11_take_the_chunked_form(name, flags, norm, T):
 
 def test_tokens_agree_with_single_calls_across_the_switches():
     """Either side of each switch of form (token by token up to 4, short
-    rows 5 .. 8, token by token 9 and 10, chunked from 11), against T
-    single-token kernel calls on the same inputs (and two chunks per row at
-    29)."""
-    for T in (4, 5, 8, 10, 11, 29):
+    rows 5 .. 16, and with these 576 (row, head) units the chunked kernel
+    from 17), against T single-token kernel calls on the same inputs."""
+    for T in (4, 5, 8, 9, 16, 17, 29):
         w = synth.small(f"tsw{T}", batch=12, heads=48, num_slots=20,
                         seed=170 + T, null_every=5, conv_w_sigma=0.05)
         inp = synth.make_tokens(w, T)
@@ -283,10 +317,10 @@ def test_tokens_agree_with_single_calls_across_the_switches():
 
 @pytest.mark.parametrize("T", [8, 10, 16, 29])
 def test_tokens_b256_h48_full_size(T):
-    """The batch-256, 48-head workload (32 null rows) with 8 tokens per row
-    (short rows: one chunk per (row, head)), 10 (token by token), 16 (the
-    chunked form, one chunk per row) and 29 (two chunks, the second ragged)
-    at full size, every element against the oracle.
+    """The batch-256, 48-head workload (32 null rows) with 8, 10, 16 and 29
+    tokens per row at full size (the short-row kernel: one, two and four
+    chunks of up to 8, the last ones ragged), every element against the
+    oracle.
     q/k are L2-normalised (unit keys, beta < 1: each update contracts the
     state along k).  Without it these inputs give beta |k|^2 near 40, and
     16 or more chained updates amplify fp32 rounding order by that factor
@@ -301,14 +335,14 @@ def test_tokens_b256_h48_full_size(T):
     print(f"[tokens b256 T={T}] {st}", flush=True)
 
 
-def test_tokens_rows_mode_at_the_segment_cap():
-    """Rows of 12 tokens at 200 rows x 96 heads: 19,200 (row, head)
-    segments, more than 64 per compute unit, so the chunked kernel's rows
-    mode runs workgroups of 64 segments in more than one round, with null
-    rows inside the runs; every element against the oracle (q/k
-    L2-normalised, the contractive regime: absolute state bar)."""
+def test_tokens_many_rows_with_null_rows_inside():
+    """Rows of 12 tokens at 200 rows x 96 heads: 19,200 (row, head) units,
+    the short-row kernel's two chunks each, in many rounds of workgroups
+    per compute unit, with a null row every 7; every element against the
+    oracle (q/k L2-normalised, the contractive regime: absolute state
+    bar)."""
     T, H = 12, 96
-    w = synth.small("rows_cap", batch=200, heads=H, num_slots=210, seed=410,
+    w = synth.small("rows_many", batch=200, heads=H, num_slots=210, seed=410,
                     null_every=7, conv_w_sigma=0.5)
     inp = synth.make_tokens(w, T)
     ref = O.decode_tokens(inp, heads=H, tokens=T, norm=True, eps=w.eps,
@@ -317,7 +351,7 @@ def test_tokens_rows_mode_at_the_segment_cap():
     st = check_tokens(w, inp, got, ref, T)
     null = ~((inp["state_idx"] > 0) & (inp["state_idx"] < w.num_slots))
     assert null.any() and np.all(got["out"][null] == 0)
-    print(f"[tokens rows cap] {st}", flush=True)
+    print(f"[tokens many rows] {st}", flush=True)
 
 
 def test_tokens_argument_checks():
@@ -354,11 +388,11 @@ def test_tokens_maximum_T():
     print(f"[tokens T=1024] {st}", flush=True)
 
 
-@pytest.mark.parametrize("T", [4, 8, 30])
+@pytest.mark.parametrize("T", [4, 8, 12, 30])
 def test_tokens_graph_replay_matches_eager(T):
     """kda_decode_tokens captured in a HIP graph (T = 4 token by token,
-    T = 8 short rows, T = 30 the chunked form) and replayed three times
-    with eager work and
+    T = 8 and 12 short rows in one and two chunks, T = 30 the chunked form)
+    and replayed three times with eager work and
     synchronisation in between: each replay equals the same eager call bit
     for bit (pools updated in place, so every replay advances the state)."""
     w = synth.small(f"tgraph{T}", batch=10, heads=24, num_slots=16,
@@ -402,12 +436,13 @@ def test_tokens_graph_replay_matches_eager(T):
         print(f"[tokens graph T={T}] replay {r} matches eager", flush=True)
 
 
-@pytest.mark.parametrize("T", [4, 5, 8, 10, 11, 29])
+@pytest.mark.parametrize("T", [4, 5, 8, 10, 16, 29])
 def test_tokens_decay_contract_independent_of_T(T):
     """The contract on g is the same in every form (token by token, short
-    rows from 5 tokens, chunked from 11): per element -inf (5 %, the key
-    row is forgotten), -1e30 (5 %), -100 (5 %, exp underflows), -1e-4
-    (5 %) or an ordinary decay, against the oracle (exp(-inf) = 0 there)."""
+    rows from 5 tokens in one or two chunks, with these 144 (row, head)
+    units the chunked kernel from 17): per element -inf (5 %, the key row
+    is forgotten), -1e30 (5 %), -100 (5 %, exp underflows), -1e-4 (5 %) or
+    an ordinary decay, against the oracle (exp(-inf) = 0 there)."""
     w = synth.small(f"tginf{T}", batch=6, heads=24, num_slots=10,
                     seed=310 + T, null_every=4, conv_w_sigma=0.05)
     inp = synth.make_tokens(w, T)
