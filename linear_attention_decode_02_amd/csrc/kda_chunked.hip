@@ -1114,23 +1114,25 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
     // channel-major: one channel in each of [0], [1])
     uint32_t wv[2][3][kW - 1] = {};
     if (ch == 0 || !conv_update) {
+      // the slot's window as a uniform base (this head's first channel)
+      // plus 32-bit lane offsets
+      const gptr<const char> wb = uniform_gptr(
+          p.conv_state + static_cast<int64_t>(slot) * (kW - 1) * C3 +
+          (tap_major ? col0 : col0 * (kW - 1)));
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp)
+      for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
-      for (int e = 0; e < kW - 1; ++e) {
-        const int64_t chn = static_cast<int64_t>(pp) * C + col0 + 2 * lane;
-        if (tap_major) {
-          wv[0][pp][e] = *reinterpret_cast<const uint32_t*>(
-              p.conv_state + (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 +
-              chn);
-          wv[1][pp][e] = 0u;
-        } else {
-          const uint16_t* cs =
-              p.conv_state + (static_cast<int64_t>(slot) * C3 + chn) * (kW - 1) + e;
-          wv[0][pp][e] = cs[0];
-          wv[1][pp][e] = cs[kW - 1];
+        for (int e = 0; e < kW - 1; ++e) {
+          const uint32_t chr = pp * C + 2 * lane;  // channel in the head's frame
+          if (tap_major) {
+            wv[0][pp][e] = load_at<uint32_t>(wb, 2 * (e * C3 + chr));
+            wv[1][pp][e] = 0u;
+          } else {
+            wv[0][pp][e] = load_at<uint16_t>(wb, 2 * (chr * (kW - 1) + e));
+            wv[1][pp][e] =
+                load_at<uint16_t>(wb, 2 * ((chr + 1) * (kW - 1) + e));
+          }
         }
-      }
     }
     // decays of keys 2 lane, 2 lane + 1 for every token of the row
     u2 in_g[kS];
@@ -1147,16 +1149,16 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
       const int t = 2 * wave + lane;
       bt = p.beta[(tb + (c0 + t < T ? c0 + t : T - 1)) * H + h];
     }
-    // (reloaded per chunk from the cache rather than held across chunks)
-    const float* cw = p.conv_w + col0 + 2 * lane;
-    asm volatile("" : "+v"(cw));
+    // (reloaded per chunk from the cache rather than held across chunks:
+    // load_at keeps the loads in the loop)
+    const gptr<const char> cwb = uniform_gptr(p.conv_w + col0);
     f2 cwv[3][kW];
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
       for (int tap = 0; tap < kW; ++tap)
-        cwv[pp][tap] = *reinterpret_cast<const f2*>(
-            cw + (static_cast<int64_t>(pp) * kW + tap) * C);
+        cwv[pp][tap] =
+            load_at<f2>(cwb, 4 * ((pp * kW + tap) * C + 2 * lane));
     if (ch == 0 && tid_l >= 128 && tid_l < 128 + kD)
       sm.nw[tid_l - 128] = kNorm ? p.norm_w[tid_l - 128] : 0.0f;
 
@@ -1166,14 +1168,26 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
     f2 G = {0.f, 0.f};
     f2 Gu[2] = {{0.f, 0.f}, {0.f, 0.f}};
     float gmax = 0.0f;
+    // one copy per wave, so that picking the wave's own tokens costs no
+    // selects
+    auto prefix = [&](auto W) {
+      constexpr int w = decltype(W)::value;
 #pragma unroll
-    for (int t = 0; t < kS; ++t) {
-      f2 gl = f2{__uint_as_float(in_g[t].x), __uint_as_float(in_g[t].y)} * kLog2e;
-      gl = kda_decay_floor2(gl);
-      if (t < nv) G += gl;
-      gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
-      if (t == 2 * wave) Gu[0] = G;
-      if (t == 2 * wave + 1) Gu[1] = G;
+      for (int t = 0; t < kS; ++t) {
+        f2 gl =
+            f2{__uint_as_float(in_g[t].x), __uint_as_float(in_g[t].y)} * kLog2e;
+        gl = kda_decay_floor2(gl);
+        if (t < nv) G += gl;
+        gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+        if (t == 2 * w) Gu[0] = G;
+        if (t == 2 * w + 1) Gu[1] = G;
+      }
+    };
+    switch (wave) {
+      case 0: prefix(std::integral_constant<int, 0>{}); break;
+      case 1: prefix(std::integral_constant<int, 1>{}); break;
+      case 2: prefix(std::integral_constant<int, 2>{}); break;
+      default: prefix(std::integral_constant<int, 3>{}); break;
     }
     // NaN counts as unsafe; the same verdict in every wave
     const bool unsafe = __any(!(gmax <= kSafeExp2));

@@ -41,10 +41,9 @@ __device__ __forceinline__ float kda_gate2_from_raw(float z, float a_rate,
 // unchanged for non-positive decays: a factor e^{G_t - G_s} whose span
 // holds a clamped token has exponent <= -200 either way.  It keeps the
 // cumulative sums finite, so that g = -inf (full forgetting) gives zeros
-// instead of -inf - -inf = NaN.  NaN passes through (the comparison is
-// false).
+// instead of -inf - -inf = NaN.  NaN passes through: the IEEE 754-2019
+// maximum propagates it (one v_maximum3_f32 per element on gfx950).
 typedef float kda_f2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ kda_f2 kda_decay_floor2(kda_f2 g2) {
-  return kda_f2{g2.x < -200.0f ? -200.0f : g2.x,
-                g2.y < -200.0f ? -200.0f : g2.y};
+  return __builtin_elementwise_maximum(g2, kda_f2{-200.0f, -200.0f});
 }
