@@ -460,17 +460,21 @@ def test_tokens_decay_contract_independent_of_T(T):
     print(f"[tokens decay contract T={T}] {st}", flush=True)
 
 
-def test_tokens_offsets_past_int32_products():
-    """64-bit token offsets in kda_decode_tokens: 64 rows x 1024 tokens at
-    96 heads, so row x T x 3C passes 2^31 elements from row 57 on (the
-    chunked form runs at this T).  Rows 0..59 are null (they read no input
-    and write zeros); rows 60..63 carry seeded inputs and are compared with
-    the oracle.  q/k L2-normalised (contractive)."""
-    B, T, H = 64, 1024, 96
+@pytest.mark.parametrize("B,T", [(64, 1024), (1024, 64)])
+def test_tokens_offsets_past_int32_products(B, T):
+    """64-bit token offsets in kda_decode_tokens at 96 heads, so that
+    row x T x 3C passes 2^31 elements in the last rows: 64 rows x 1024
+    tokens (the chunked kernel) and 1024 rows x 64 tokens (98,304 units:
+    the short-row kernel, eight chunks per row).  All rows but the last
+    four are null (they read no input and write zeros); the last four carry
+    seeded inputs and are compared with the oracle.  q/k L2-normalised
+    (contractive)."""
+    H = 96
     C = H * 128
     live = 4
+    assert (B - 1) * T * 3 * C > 2**31
     small = synth.small("tbig", batch=live, heads=H, num_slots=live + 1,
-                        seed=320, conv_w_sigma=0.5)
+                        seed=320 + T, conv_w_sigma=0.5)
     inp = synth.make_tokens(small, T)
     inp["state_idx"] = np.arange(1, live + 1, dtype=np.int32)
     ref = O.decode_tokens(inp, heads=H, tokens=T, norm=True, eps=small.eps,
