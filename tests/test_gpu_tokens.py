@@ -354,6 +354,24 @@ def test_tokens_many_rows_with_null_rows_inside():
     print(f"[tokens many rows] {st}", flush=True)
 
 
+@pytest.mark.parametrize("T,B", [(4, 32), (8, 32), (12, 32), (24, 32),
+                                 (24, 2)])
+def test_tokens_deterministic_bitwise(T, B):
+    """Two identical calls give identical bits in every form: token by
+    token (T = 4), short rows in one, two and three chunks (T = 8, 12, and
+    24 at 32 rows x 48 heads = 1,536 units) and the chunked kernel (T = 24
+    at 2 rows).  No form sums through atomics."""
+    w = synth.small(f"tdet{T}_{B}", batch=B, heads=48, num_slots=B + 8,
+                    seed=500 + T + B, null_every=5, conv_w_sigma=0.05)
+    inp = synth.make_tokens(w, T)
+    a = run_tokens(w, inp, T)
+    b = run_tokens(w, inp, T)
+    for key in ("out", "conv_state"):
+        assert np.array_equal(a[key], b[key])
+    assert np.array_equal(a["rec_state"].view(np.uint32),
+                          b["rec_state"].view(np.uint32))
+
+
 def test_tokens_argument_checks():
     w = synth.small("tc", batch=2, heads=12, num_slots=4, seed=60)
     inp = synth.make_tokens(w, 2)
