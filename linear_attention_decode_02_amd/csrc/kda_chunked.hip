@@ -1093,9 +1093,9 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
     const int c = lane & 15;
     const int gq = lane >> 4;
     const uint32_t st_lane = (4 * gq * kD + 2 * c) * 4;
-    // ---- inputs of tokens 2w, 2w+1, channels 2 lane, 2 lane + 1 ------------
-    // input rows 2w-3 .. 2w+1 (row indices clamped into the row; rows before
-    // it come from the stored window)
+    // ---- inputs of tokens 2w, 2w+1, channels 2 lane, 2 lane + 1 --------
+    // input rows 2w-3 .. 2w+1 of the chunk (clamped into the row; rows
+    // before the row come from the stored window)
     uint32_t raw[3][5];
     {
       const char* q0 = reinterpret_cast<const char*>(p.qkv + tb * C3 + col0);
@@ -1123,7 +1123,8 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
       for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
         for (int e = 0; e < kW - 1; ++e) {
-          const uint32_t chr = pp * C + 2 * lane;  // channel in the head's frame
+          // the channel relative to the head's first
+          const uint32_t chr = pp * C + 2 * lane;
           if (tap_major) {
             wv[0][pp][e] = load_at<uint32_t>(wb, 2 * (e * C3 + chr));
             wv[1][pp][e] = 0u;
@@ -1134,7 +1135,7 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
           }
         }
     }
-    // decays of keys 2 lane, 2 lane + 1 for every token of the row
+    // decays of keys 2 lane, 2 lane + 1 for every token of the chunk
     u2 in_g[kS];
     {
       const char* gb = reinterpret_cast<const char*>(p.g + (tb * H + h) * kD);
@@ -1162,9 +1163,9 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
     if (ch == 0 && tid_l >= 128 && tid_l < 128 + kD)
       sm.nw[tid_l - 128] = kNorm ? p.norm_w[tid_l - 128] : 0.0f;
 
-    // ---- prep ---------------------------------------------------------------
-    // cumulative decay (log2 units) over the row, its value at this wave's
-    // tokens and at the last one
+    // ---- prep -----------------------------------------------------------
+    // cumulative decay (log2 units) over the chunk, its value at this
+    // wave's tokens and at the chunk's last one
     f2 G = {0.f, 0.f};
     f2 Gu[2] = {{0.f, 0.f}, {0.f, 0.f}};
     float gmax = 0.0f;
@@ -1209,9 +1210,9 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
           float a = 0.0f;
 #pragma unroll
           for (int tap = 0; tap < kW; ++tap) {
-            // input row of this tap relative to the row start: 2w + u - 3 +
-            // tap; only waves 0 and 1 of the first chunk reach before it
-            // (compile-time indices)
+            // input row of this tap relative to the chunk start: 2w + u -
+            // 3 + tap; only waves 0 and 1 of the first chunk reach before
+            // the row (compile-time indices)
             const int r0 = u - (kW - 1) + tap;  // for wave 0
             uint32_t w2 = raw[pp][u + tap];
             if (tap < kW - 1) {
@@ -1361,15 +1362,16 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
                 p.conv_state +
                 (static_cast<int64_t>(slot) * (kW - 1) + e) * C3 + chn) = w;
           } else {
-            uint16_t* cs = p.conv_state +
-                           (static_cast<int64_t>(slot) * C3 + chn) * (kW - 1) + e;
+            uint16_t* cs =
+                p.conv_state +
+                (static_cast<int64_t>(slot) * C3 + chn) * (kW - 1) + e;
             cs[0] = static_cast<uint16_t>(w);
             cs[kW - 1] = static_cast<uint16_t>(w >> 16);
           }
         }
     }
 
-    // ---- Gram block of keys 32w .. 32w+31 ---------------------------------
+    // ---- Gram block of keys 32w .. 32w+31 -----------------------------
     if (!sm.unsafe) {
       const int off = (4 * wave + gq) * 12;
       const u4 z = {0u, 0u, 0u, 0u};
@@ -1398,7 +1400,8 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
 #pragma unroll
         for (int s_ = 0; s_ < kS; ++s_) {
           if (s_ > t) continue;
-          const f2 ks2 = *reinterpret_cast<const f2*>(&sm.u.ex.ki[s_][2 * lane]);
+          const f2 ks2 =
+              *reinterpret_cast<const f2*>(&sm.u.ex.ki[s_][2 * lane]);
           const f2 gs2 =
               *reinterpret_cast<const f2*>(&sm.u.ex.graw[s_][2 * lane]);
 #pragma unroll
@@ -1443,10 +1446,11 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
     u4 gate_raw = {0u, 0u, 0u, 0u};
     if (kNorm && tid_l < 16 * kS) {
       const int rr = c0 + ot < T - 1 ? c0 + ot : T - 1;
-      gate_raw = *reinterpret_cast<const u4*>(p.gate + (tb + rr) * C + col0 + oc);
+      gate_raw =
+          *reinterpret_cast<const u4*>(p.gate + (tb + rr) * C + col0 + oc);
     }
 
-    // ---- the chunk through the recurrence ---------------------------------
+    // ---- the chunk through the recurrence -----------------------------
     // X = [K~; Q~] S: accumulator rows 0-7 are K~ S, rows 8-15 Q~ S
     f4 X[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -1553,7 +1557,7 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
     }
     __syncthreads();  // outputs in sm.u.o
 
-    // ---- gated RMSNorm and bf16 outputs: 16 lanes per token ---------------
+    // ---- gated RMSNorm and bf16 outputs: 16 lanes per token -----------
     if (tid_l < 16 * kS) {
       const f4 v0 = ld4(&sm.u.o[ot][oc]);
       const f4 v1 = ld4(&sm.u.o[ot][oc + 4]);
