@@ -1043,12 +1043,24 @@ struct alignas(16) ShortSmem {
 };
 // four workgroups per compute unit: 160 KiB of LDS, 128 VGPRs per lane
 static_assert(4 * sizeof(ShortSmem) <= 160 * 1024, "short-row LDS");
+// Rows of several chunks keep the outputs in a buffer of their own, so that
+// the next chunk's tables can be written while they are emitted.
+struct ShortOut {
+  float o[kS][kLd];
+};
+struct ShortNoOut {};
 
 template <bool kNorm, bool kMulti>
 __global__ __launch_bounds__(kSThreads)
 __attribute__((amdgpu_waves_per_eu(kMulti ? 3 : 4)))
 void kda_short_rows_kernel(KdaChunkedArgs p) {
   __shared__ ShortSmem sm;
+  __shared__ typename std::conditional<kMulti, ShortOut, ShortNoOut>::type so;
+  float(*obuf)[kLd];
+  if constexpr (kMulti)
+    obuf = so.o;
+  else
+    obuf = sm.u.o;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.heads;
@@ -1440,14 +1452,14 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
       sm.Bm[t][s_] = s_ <= t ? b : 0.0f;
     }
     __syncthreads();  // A and B
-    // output lanes (threads 0-127): token tid_l/16, columns 8 (tid_l%16) .. +7
-    const int ot = tid_l >> 4;
-    const int oc = 8 * (tid_l & 15);
-    u4 gate_raw = {0u, 0u, 0u, 0u};
-    if (kNorm && tid_l < 16 * kS) {
+    // output lanes: token tid/32 (half a wave), columns 4 (tid%32) .. +3
+    const int ot = tid_l >> 5;
+    const int oc = 4 * (tid_l & 31);
+    u2 gate_raw = {0u, 0u};
+    if (kNorm) {
       const int rr = c0 + ot < T - 1 ? c0 + ot : T - 1;
       gate_raw =
-          *reinterpret_cast<const u4*>(p.gate + (tb + rr) * C + col0 + oc);
+          *reinterpret_cast<const u2*>(p.gate + (tb + rr) * C + col0 + oc);
     }
 
     // ---- the chunk through the recurrence -----------------------------
@@ -1513,7 +1525,7 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
       for (int j = 0; j < 4; ++j) X[cb] = mfma(ab[j], dl[cb][j], X[cb]);
       if (gq >= 2) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.u.o[4 * (gq - 2) + r][col] = X[cb][r];
+        for (int r = 0; r < 4; ++r) obuf[4 * (gq - 2) + r][col] = X[cb][r];
       }
     }
     // state update: e^{G_last} S + K^T Delta
@@ -1555,34 +1567,42 @@ void kda_short_rows_kernel(KdaChunkedArgs p) {
               reinterpret_cast<gptr<f2>>(b + lo + r * kD * 4));
       }
     }
-    __syncthreads();  // outputs in sm.u.o
+    __syncthreads();  // outputs in obuf
 
-    // ---- gated RMSNorm and bf16 outputs: 16 lanes per token -----------
-    if (tid_l < 16 * kS) {
-      const f4 v0 = ld4(&sm.u.o[ot][oc]);
-      const f4 v1 = ld4(&sm.u.o[ot][oc + 4]);
-      float yo[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    // ---- gated RMSNorm and bf16 outputs: 32 lanes per token -----------
+    // (a row of several chunks goes on to the next chunk's tables without
+    // waiting: nothing reads them after the barrier above, and its outputs
+    // have a buffer of their own)
+    {
+      const f4 ov = ld4(&obuf[ot][oc]);
+      float yo[4] = {ov.x, ov.y, ov.z, ov.w};
       if (kNorm) {
         float ss = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss += yo[j] * yo[j];
+        for (int j = 0; j < 4; ++j) ss += yo[j] * yo[j];
+        // the two tokens' sums: rows 0 + 1 in row 1, rows 2 + 3 in row 3
         ss = row_sum16(ss);
-        const float rs = rsqrtf(ss * (1.0f / kD) + p.eps);
+        ss += dpp_rows_<0x142, 0xA>(ss);
+        const float s_lo = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 31));
+        const float s_hi = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), 63));
+        const float rs =
+            rsqrtf((lane < 32 ? s_lo : s_hi) * (1.0f / kD) + p.eps);
+        const f4 nw = ld4(&sm.nw[oc]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
           const uint32_t w2 = gate_raw[j >> 1];
           const float gv = (j & 1) ? bf16_hi(w2) : bf16_lo(w2);
           const float ga = gate_silu ? gv * sigmoid_(gv) : sigmoid_(gv);
-          yo[j] = ((yo[j] * rs) * sm.nw[oc + j]) * ga;
+          yo[j] = ((yo[j] * rs) * nw[j]) * ga;
         }
       }
       if (ot < nv) {
-        const u4 pk = {pack_bf16(yo[0], yo[1]), pack_bf16(yo[2], yo[3]),
-                       pack_bf16(yo[4], yo[5]), pack_bf16(yo[6], yo[7])};
-        *reinterpret_cast<u4*>(p.out + (tb + c0 + ot) * C + col0 + oc) = pk;
+        const u2 pk = {pack_bf16(yo[0], yo[1]), pack_bf16(yo[2], yo[3])};
+        *reinterpret_cast<u2*>(p.out + (tb + c0 + ot) * C + col0 + oc) = pk;
       }
     }
-      if (!last) __syncthreads();  // the tables are free for the next chunk
   }
 }
 
