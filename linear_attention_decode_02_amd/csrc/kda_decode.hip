@@ -177,11 +177,16 @@ __device__ __forceinline__ uint32_t tile_lane_off(int rgrp, int col4) {
 struct Lds {
   f4 akq[kD];                // {exp(g_i), k_i, q_i, -} per key row i
   float v[kD];
-  float red[2 * kWaves][2][kD];  // per-half-wave partial sums of u and p
+  // per-half-wave partial sums of u and p; rows padded by 4 floats (a row
+  // pair 264 words apart, 8 banks of 32) so the quad of threads finishing
+  // one column, which read rows q, q + 4, ..., hit four different banks
+  float red[2 * kWaves][2][kD + 4];
   float qk[2 * kWaves];          // per-half-wave partial q.k
   float delta[kD];
   float p[kD];
   float qk_total;
+  f4 gate_act[kD / 4];  // output gate after its activation (norm only)
+  f4 norm_w[kD / 4];    // norm weight (norm only)
 };
 
 // Conv window of channels c, c+1 from the three state words: element t of
@@ -297,36 +302,61 @@ __device__ __forceinline__ void decay_and_partials(
   if ((lane & 31) == 0) L.qk[half] = qk;
 }
 
-// Reduce, then broadcast: threads 0..255 each finish one column of u
-// (delta_j = beta (v_j - u_j)) or of p, instead of every thread summing
-// all partials of its four columns.
+// Reduce, then broadcast: each column of u (delta_j = beta (v_j - u_j)) and
+// of p is finished by a quad of threads, each summing 8 of the 32 half-wave
+// partials (partials q, q + 4, ... for quad lane q), folded across the quad
+// by DPP; threads 0..3 finish q.k the same way.  All 1024 threads take
+// part, so the dependent chain is 8 adds deep instead of 32.
 __device__ __forceinline__ void finish_columns(Lds& L, int tid, float beta) {
-  if (tid < 2 * kD) {
-    const int which = tid / kD;
-    const int j = tid % kD;
-    float acc = L.red[0][which][j];
+  static_assert(2 * kWaves == 32 && kThreads == 8 * kD, "quad finish shape");
+  const int q = tid & 3;
+  const int col = tid >> 2;
+  const int which = col / kD;
+  const int j = col % kD;
+  float a = L.red[q][which][j], b = L.red[q + 4][which][j];
 #pragma unroll
-    for (int r = 1; r < 2 * kWaves; ++r) acc += L.red[r][which][j];
+  for (int i = 2; i < 8; i += 2) {
+    a += L.red[q + 4 * i][which][j];
+    b += L.red[q + 4 * i + 4][which][j];
+  }
+  float acc = a + b;
+  acc += dpp_mov<0xB1>(acc);  // quad_perm [1,0,3,2]
+  acc += dpp_mov<0x4E>(acc);  // quad_perm [2,3,0,1]
+  if (q == 0) {
     if (which == 0)
       L.delta[j] = beta * (L.v[j] - acc);
     else
       L.p[j] = acc;
-    if (tid == 0) {
-      float t = L.qk[0];
+  }
+  if (tid < 4) {
+    float ta = L.qk[q], tb = L.qk[q + 4];
 #pragma unroll
-      for (int r = 1; r < 2 * kWaves; ++r) t += L.qk[r];
-      L.qk_total = t;
+    for (int i = 2; i < 8; i += 2) {
+      ta += L.qk[q + 4 * i];
+      tb += L.qk[q + 4 * i + 4];
     }
+    float t = ta + tb;
+    t += dpp_mov<0xB1>(t);
+    t += dpp_mov<0x4E>(t);
+    if (tid == 0) L.qk_total = t;
   }
 }
 
+// The output gate of columns 4 col4 .. +3 after its activation (sigmoid,
+// or SiLU with KDA_GATE_SILU), from its four bf16 values.
+__device__ __forceinline__ f4 gate_activation(uint32_t flags, u2 gb) {
+  const f4 gv = {bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
+  f4 ga = {sigmoidf_(gv.x), sigmoidf_(gv.y), sigmoidf_(gv.z), sigmoidf_(gv.w)};
+  if (flags & KDA_GATE_SILU) ga *= gv;
+  return ga;
+}
+
 // Readout o = Sd^T q + (q.k) delta and the gated RMSNorm of one token, by
-// lanes 0..31 of wave 0 (four columns each); writes 4 bf16 at out4.
+// lanes 0..31 of wave 0 (four columns each, the activated gate and the norm
+// weight already in LDS); writes 4 bf16 at out4.
 template <bool kNorm>
-__device__ __forceinline__ void emit_output(const Lds& L, const float* norm_w,
-                                            uint32_t flags, float eps, int col4,
-                                            f4 delta, u2 gb,
-                                            gptr<uint16_t> out4) {
+__device__ __forceinline__ void emit_output(const Lds& L, float eps, int col4,
+                                            f4 delta, gptr<uint16_t> out4) {
   const f4 o = *reinterpret_cast<const f4*>(&L.p[4 * col4]) +
                L.qk_total * delta;
   f4 y = o;
@@ -334,12 +364,7 @@ __device__ __forceinline__ void emit_output(const Lds& L, const float* norm_w,
     const float rows = sum16(o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w);
     const float ss = lane_value(rows, 0) + lane_value(rows, 16);
     const float r = rsqrtf(ss * (1.0f / kD) + eps);
-    const f4 w = *reinterpret_cast<const f4*>(norm_w + 4 * col4);
-    const f4 gv = {bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
-    f4 ga = {sigmoidf_(gv.x), sigmoidf_(gv.y), sigmoidf_(gv.z),
-             sigmoidf_(gv.w)};
-    if (flags & KDA_GATE_SILU) ga *= gv;
-    y = o * r * w * ga;
+    y = o * r * L.norm_w[col4] * L.gate_act[col4];
   }
   u2 ob;
   ob.x = pack_bf16x2(y.x, y.y);
@@ -347,10 +372,12 @@ __device__ __forceinline__ void emit_output(const Lds& L, const float* norm_w,
   *reinterpret_cast<gptr<u2>>(out4) = ob;
 }
 
-// kNorm: gated RMSNorm epilogue; kRawGates: g and beta from raw inputs.
-// Other variants (conv-state layout and update, q/k L2 norm, SiLU gate,
-// bounded gate, conv bias) are block-uniform runtime flags.
-template <bool kNorm, bool kRawGates>
+// kNorm: gated RMSNorm epilogue; kRawGates: g and beta from raw inputs;
+// kTileFirst: the state tile is requested before the small inputs (faster
+// when some compute units hold two units, slower otherwise; the launcher
+// chooses).  Other variants (conv-state layout and update, q/k L2 norm,
+// SiLU gate, bounded gate, conv bias) are block-uniform runtime flags.
+template <bool kNorm, bool kRawGates, bool kTileFirst>
 // At most 64 VGPRs, so that two 16-wave workgroups share a CU.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void kda_decode_kernel(Params p) {
@@ -375,69 +402,92 @@ void kda_decode_kernel(Params p) {
     return;
   }
 
-  // ---- small loads first (they retire before the state loads) ----------
-  // Waves 0..2 run the conv of part `wave` (q, k, v) on channels i0, i0+1;
-  // wave 3 computes exp(g) for key rows i0, i0+1.  The loads are issued by
-  // every wave without branching (waves 3+ re-read part 2's conv inputs, an
-  // L2 hit) so that no wave has to drain them before its state loads.
-  const uint32_t flags = p.flags;
-  const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
-  const int i0 = 2 * lane;
-  const int part = wave < 3 ? wave : 2;
-  const int64_t c = part * C + h * kD + i0;
-  const uint32_t x2 = *reinterpret_cast<const uint32_t*>(p.qkv + n * 3 * C + c);
-  // conv state words of channels c, c+1 (see unpack_window)
-  uint32_t* cs_base = reinterpret_cast<uint32_t*>(
-      p.conv_state + static_cast<int64_t>(slot) * 3 * C * (kW - 1) +
-      (tap_major ? c : c * (kW - 1)));
-  const int64_t cs_step = tap_major ? (3 * C) / 2 : 1;  // in words
-  uint32_t cw0 = cs_base[0];
-  uint32_t cw1 = cs_base[cs_step];
-  uint32_t cw2 = cs_base[2 * cs_step];
-  f2 w_t[kW];
-#pragma unroll
-  for (int t = 0; t < kW; ++t)
-    w_t[t] = *reinterpret_cast<const f2*>(p.conv_w + (part * kW + t) * C +
-                                          h * kD + i0);
-  const f2 bias2 = *reinterpret_cast<const f2*>(
-      (p.conv_bias ? p.conv_bias : p.conv_w) + c);
-  f2 g2;
-  float beta;
-  if (kRawGates) {
-    const uint32_t rg = *reinterpret_cast<const uint32_t*>(
-        p.raw_g + (static_cast<int64_t>(n) * H + h) * kD + i0);
-    const f2 db = *reinterpret_cast<const f2*>(p.dt_bias + h * kD + i0);
-    const float a_rate = __expf(p.A_log[h]);
-    const float z0 = bf16_lo(rg) + db.x, z1 = bf16_hi(rg) + db.y;
-    if (flags & KDA_BOUNDED_GATE) {
-      g2.x = p.lower_bound * sigmoidf_(a_rate * z0);
-      g2.y = p.lower_bound * sigmoidf_(a_rate * z1);
-    } else {
-      g2.x = -(a_rate * softplusf_(z0));
-      g2.y = -(a_rate * softplusf_(z1));
-    }
-    const uint32_t rb = p.raw_beta[static_cast<int64_t>(n) * H + h];
-    beta = sigmoidf_(bf16_lo(rb));
-  } else {
-    g2 = *reinterpret_cast<const f2*>(
-        p.g + (static_cast<int64_t>(n) * H + h) * kD + i0);
-    beta = p.beta[static_cast<int64_t>(n) * H + h];
-  }
-
-  // ---- issue the whole state tile ----------------------------------------
-  // Keep the small loads above ahead of the state loads: the conv math
-  // then waits only for them (vmcnt retires in issue order).
-  __builtin_amdgcn_sched_barrier(0);
   const int col4 = tid & 31;
   const int rgrp = tid >> 5;
   f4* st = reinterpret_cast<f4*>(
       p.rec_state + (static_cast<int64_t>(slot) * H + h) * (kD * kD));
   const uint32_t lane_off = tile_lane_off(rgrp, col4);
   f4 s[kRowsPerThread];
+  auto issue_tile = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int m = 0; m < kRowsPerThread; ++m)
-    s[m] = __builtin_nontemporal_load(tile_at(st, lane_off, m));
-  __builtin_amdgcn_sched_barrier(0);
+    for (int m = 0; m < kRowsPerThread; ++m)
+      s[m] = __builtin_nontemporal_load(tile_at(st, lane_off, m));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (kTileFirst) issue_tile();
+
+  // ---- small loads (they retire before the state loads unless kTileFirst)
+  // Waves 0..2 run the conv of part `wave` (q, k, v) on channels i0, i0+1;
+  // wave 3 computes exp(g) for key rows i0, i0+1.  Only those waves issue
+  // these loads (wave-uniform branches): the other waves' state loads then
+  // queue behind no redundant requests in the compute unit's address path.
+  const uint32_t flags = p.flags;
+  const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
+  const int i0 = 2 * lane;
+  const int part = wave < 3 ? wave : 2;
+  const int64_t c = part * C + h * kD + i0;
+  // conv state words of channels c, c+1 (see unpack_window)
+  uint32_t* cs_base = reinterpret_cast<uint32_t*>(
+      p.conv_state + static_cast<int64_t>(slot) * 3 * C * (kW - 1) +
+      (tap_major ? c : c * (kW - 1)));
+  const int64_t cs_step = tap_major ? (3 * C) / 2 : 1;  // in words
+  uint32_t x2 = 0u, cw0 = 0u, cw1 = 0u, cw2 = 0u;
+  f2 w_t[kW] = {};
+  f2 bias2 = {0.f, 0.f};
+  if (wave < 3) {
+    x2 = *reinterpret_cast<const uint32_t*>(p.qkv + n * 3 * C + c);
+    cw0 = cs_base[0];
+    cw1 = cs_base[cs_step];
+    cw2 = cs_base[2 * cs_step];
+#pragma unroll
+    for (int t = 0; t < kW; ++t)
+      w_t[t] = *reinterpret_cast<const f2*>(p.conv_w + (part * kW + t) * C +
+                                            h * kD + i0);
+    if (p.conv_bias) bias2 = *reinterpret_cast<const f2*>(p.conv_bias + c);
+  }
+  f2 g2 = {0.f, 0.f};
+  float beta;
+  if (kRawGates) {
+    if (wave == 3) {
+      const uint32_t rg = *reinterpret_cast<const uint32_t*>(
+          p.raw_g + (static_cast<int64_t>(n) * H + h) * kD + i0);
+      const f2 db = *reinterpret_cast<const f2*>(p.dt_bias + h * kD + i0);
+      const float a_rate = __expf(p.A_log[h]);
+      const float z0 = bf16_lo(rg) + db.x, z1 = bf16_hi(rg) + db.y;
+      if (flags & KDA_BOUNDED_GATE) {
+        g2.x = p.lower_bound * sigmoidf_(a_rate * z0);
+        g2.y = p.lower_bound * sigmoidf_(a_rate * z1);
+      } else {
+        g2.x = -(a_rate * softplusf_(z0));
+        g2.y = -(a_rate * softplusf_(z1));
+      }
+    }
+    const uint32_t rb = p.raw_beta[static_cast<int64_t>(n) * H + h];
+    beta = sigmoidf_(bf16_lo(rb));
+  } else {
+    if (wave == 3)
+      g2 = *reinterpret_cast<const f2*>(
+          p.g + (static_cast<int64_t>(n) * H + h) * kD + i0);
+    beta = p.beta[static_cast<int64_t>(n) * H + h];
+  }
+  // Output gate and norm weight of columns 4 lane .. +3, by lanes 0..31 of
+  // wave 4 (idle in the conv): activated and put in LDS before the first
+  // barrier, so the readout at the end waits for no load.  (Fetched there,
+  // behind the state stores, it would also wait for their completion.)
+  const bool gate_lanes = kNorm && wave == 4 && lane < 32;
+  u2 gb = {0u, 0u};
+  f4 nw = {0.f, 0.f, 0.f, 0.f};
+  if (gate_lanes) {
+    gb = *reinterpret_cast<const u2*>(p.gate + static_cast<int64_t>(n) * C +
+                                      h * kD + 4 * lane);
+    nw = *reinterpret_cast<const f4*>(p.norm_w + 4 * lane);
+  }
+
+  // ---- the whole state tile, after (or, kTileFirst, before) the small
+  // loads: the conv math then waits only for what precedes it (vmcnt
+  // retires in issue order)
+  if (!kTileFirst) issue_tile();
 
   // ---- conv update + SiLU, decay factors ---------------------------------
   float y0, y1;
@@ -450,6 +500,10 @@ void kda_decode_kernel(Params p) {
     cs_base[2 * cs_step] = cw2;
   }
   store_token_inputs(L, wave, i0, y0, y1);
+  if (gate_lanes) {
+    L.gate_act[lane] = gate_activation(flags, gb);
+    L.norm_w[lane] = nw;
+  }
   __syncthreads();
 
   // ---- decay, column sums, delta --------------------------------------------
@@ -468,11 +522,7 @@ void kda_decode_kernel(Params p) {
 
   // ---- readout and gated RMSNorm (wave 0, lanes 0..31 own the output) -----
   if (tid >= 32) return;
-  const u2 gb = kNorm ? *reinterpret_cast<const u2*>(
-                             p.gate + static_cast<int64_t>(n) * C + h * kD +
-                             4 * col4)
-                       : u2{0u, 0u};
-  emit_output<kNorm>(L, p.norm_w, flags, p.eps, col4, delta, gb,
+  emit_output<kNorm>(L, p.eps, col4, delta,
                      at_bytes<uint16_t>(uniform_gptr(p.out + n * C + h * kD),
                                         8 * col4));
 }
@@ -830,6 +880,22 @@ bool device_is_gfx950(int dev) {
   return g_dev_ok[dev];
 }
 
+// Compute units of device `dev` (read once per device; 256 if unknown).
+std::once_flag g_cu_once[kMaxDevices];
+int g_cus[kMaxDevices];
+int cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_cu_once[dev], [dev] {
+    int cus = 0;
+    g_cus[dev] = hipDeviceGetAttribute(&cus,
+                                       hipDeviceAttributeMultiprocessorCount,
+                                       dev) == hipSuccess && cus > 0
+                     ? cus
+                     : 256;
+  });
+  return g_cus[dev];
+}
+
 bool aligned16(const void* ptr) {
   return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
 }
@@ -914,13 +980,8 @@ constexpr int64_t kShortMinUnitsPerCU = 4;
 bool use_short_rows(const kda_dims* d, int32_t tokens, int dev) {
   if (tokens < kShortMinTokens || tokens > kShortMaxTokens) return false;
   if (tokens <= kShortAnyUnitsMaxTokens) return true;
-  int cus = 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                            dev) != hipSuccess ||
-      cus < 1)
-    cus = 256;
   return static_cast<int64_t>(d->batch) * d->num_heads >=
-         kShortMinUnitsPerCU * cus;
+         kShortMinUnitsPerCU * cu_count(dev);
 }
 
 KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
@@ -950,19 +1011,39 @@ KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
   return a;
 }
 
+// Request order of the single-token kernel: the state tile first when some
+// compute units hold a second unit (CUs < units <= 2 CUs).  Graph-replay
+// latency on MI355X, us per call, tile first / small loads first: 288
+// units 8.9 / 9.7, 384 units 10.8-11.3 / 11.4-11.9; but 12 units 4.0 /
+// 3.95, 192 units 6.3 / 6.0, 768 units 21.3 / 20.8.
+bool tile_first(int64_t units, int dev) {
+  const int64_t cus = cu_count(dev);
+  return units > cus && units <= 2 * cus;
+}
+
+template <bool kNorm, bool kRaw>
+void launch_decode(bool first, dim3 grid, hipStream_t stream, const Params& p) {
+  if (first)
+    hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, true>), grid,
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, false>), grid,
+                       dim3(kThreads), 0, stream, p);
+}
+
 template <bool kRaw>
 kda_status launch(const kda_dims* d, const Params& p, void* hip_stream) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || !device_is_gfx950(dev))
     return KDA_ERR_DEVICE;
-  const dim3 grid(static_cast<unsigned>(d->batch * d->num_heads));
+  const int64_t units = static_cast<int64_t>(d->batch) * d->num_heads;
+  const dim3 grid(static_cast<unsigned>(units));
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const bool first = tile_first(units, dev);
   if (d->flags & KDA_OUTPUT_NORM)
-    hipLaunchKernelGGL((kda_decode_kernel<true, kRaw>), grid, dim3(kThreads),
-                       0, stream, p);
+    launch_decode<true, kRaw>(first, grid, stream, p);
   else
-    hipLaunchKernelGGL((kda_decode_kernel<false, kRaw>), grid, dim3(kThreads),
-                       0, stream, p);
+    launch_decode<false, kRaw>(first, grid, stream, p);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -95,8 +95,11 @@ CASES = {
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("H,B", [(48, 33), (12, 7)])
+@pytest.mark.parametrize("H,B", [(48, 33), (12, 7), (24, 16)])
 def test_variant_parity(name, H, B):
+    """Each variant against the oracle; 16 x 24 = 384 units runs the
+    single-token kernel's tile-first request order (more units than compute
+    units, at most two per unit), the others the small-loads-first order."""
     flags, raw, lb = CASES[name]
     rng = np.random.default_rng([sum(map(ord, name)), H])
     w = synth.small(f"v_{name}", batch=B, heads=H, num_slots=B + 4,
