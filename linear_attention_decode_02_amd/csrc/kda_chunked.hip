@@ -118,13 +118,23 @@ struct alignas(16) Smem {
   float ki[kC][kLd];    // exact path: raw k
   float qraw[kC][kLd];  // exact path: q_t
   float graw[kC][kLd];  // exact path: cumulative log2 decay
-  float part[4][kC][kC];  // A (keys 0-63, 64-127), B (same)
+  union {
+    float part[4][kC][kC];  // stages 2-3: A (keys 0-63, 64-127), B (same)
+    f2 gtok[kC][kD / 2];    // stage 1: token t's log2 decays of keys
+                            // 2 lane, 2 lane + 1, from the wave that owns t
+  };
   float LT[kC][kTd];    // LT[s][t] = beta_t A_ts for s < t, else 0
   float B[kC][kTd];     // B_ts for s <= t, else 0
   float o[kC][kLd];     // this chunk's outputs before the norm
   float nw[kD];         // norm weight
   int unsafe;           // exact path for the chunk being prepared
+  int gseq[4];  // per prep wave: the chunk whose decays it last put in gtok
+                // (-1: none yet)
 };
+
+// Spins of a prep wave waiting for the others' decays before it gives up
+// (then with whatever is in gtok): every wave finishes.
+constexpr int kGseqSpinMax = 1 << 20;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) {
   return __uint_as_float(w << 16);
@@ -293,6 +303,12 @@ template <bool kNorm, int kGate>
 __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     KdaChunkedArgs p) {
   constexpr bool kRaw = kGate != kGateInput;
+  // Raw gates cost a softplus (or sigmoid) per channel and token: each prep
+  // wave then converts only its own 4 tokens and the waves exchange them
+  // through LDS (raw-gate prefill 629 -> 573 us at 16 sequences x 48
+  // heads).  Plain decays are cheaper to convert than to exchange (555 ->
+  // 562 us), so there every prep wave converts all 16 itself.
+  constexpr bool kShareDecays = kRaw;
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   // wave index in a scalar register: role tests and role-derived offsets
@@ -354,6 +370,10 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   }
   if (!state_wave && tid - 256 < kD)  // norm weight, read by the state waves
     sm.nw[tid - 256] = kNorm ? p.norm_w[tid - 256] : 0.0f;
+  if (kShareDecays) {
+    if (tid < 4) sm.gseq[tid] = -1;
+    __syncthreads();  // no prep wave reads a decay flag before this
+  }
 
   // ---- prep stage 1 of chunk ci: conv, norms, decay, tables (wave-local)
   // Prep wave pw reads what it needs straight into registers, one chunk
@@ -361,12 +381,14 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
   // chunk; the first use waits for them): for channels 2 lane, 2 lane + 1
   // the input rows of tokens 4pw-3 .. 4pw+3 (chunk-relative; rows before
   // the sequence or past its end are clamped to valid rows and replaced or
-  // masked where used), the gates of all 16 tokens and (lanes 0-3) the
-  // beta of token 4pw + lane.  No LDS on this path: while the state waves
+  // masked where used), the gates of all 16 tokens (raw gates: of tokens
+  // 4pw .. 4pw+3, see kShareDecays) and (lanes 0-3) the beta of token
+  // 4pw + lane.  No LDS on this path: while the state waves
   // run their matrix products, LDS reads of the other wave on the SIMD
   // wait far longer than register loads that were issued early.
   uint32_t in_raw[3][7];
-  uint32_t in_g[kC][2];  // fp32 pair, or (raw gates) a bf16 pair in [0]
+  // fp32 pair, or (raw gates) a bf16 pair in [0]
+  uint32_t in_g[kShareDecays ? 4 : kC][2];
   uint32_t in_b = 0;     // fp32 or (raw gates) bf16 bits
   // this lane's byte offsets in an input row (parts q, k, v) and a gate row
   const uint32_t off_raw = 4 * lane;
@@ -421,15 +443,16 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
                           : reinterpret_cast<const char*>(p.g + g0);
     const int grow = H * kD * (kRaw ? 2 : 4);
 #pragma unroll
-    for (int t = 0; t < kC; ++t) {
+    for (int u = 0; u < (kShareDecays ? 4 : kC); ++u) {
+      const int t = kShareDecays ? 4 * pw + u : u;
       const int rr = t < nv - 1 ? t : nv - 1;
       const gptr<const char> row = uniform_gptr(gb + rr * grow);
       if (kRaw) {
-        in_g[t][0] = load_at<uint32_t>(row, off_g);
+        in_g[u][0] = load_at<uint32_t>(row, off_g);
       } else {
         const u2 v = load_at<u2>(row, off_g);
-        in_g[t][0] = v.x;
-        in_g[t][1] = v.y;
+        in_g[u][0] = v.x;
+        in_g[u][1] = v.y;
       }
     }
     if (lane < 4) {
@@ -517,55 +540,40 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
 #pragma unroll
       for (int e = 0; e < kW - 1; ++e)
         wc[pp][e] = wv[0][pp][e] | (wv[1][pp][e] << 16);
-    // per-token decays of keys 2 lane, 2 lane + 1 in log2 units
+    // per-token decays of keys 2 lane, 2 lane + 1 in log2 units: all 16
+    // tokens' from this wave's loads, or (kShareDecays) this wave's 4
+    // tokens', published for the other prep waves
+    constexpr int kNG = kShareDecays ? 4 : kC;
     f2 gl[kC];
     if (kRaw) {
       const float a_rate = __expf(p.rg.A_log[h]);
       const float lb2 = p.rg.lower_bound * kLog2e;
       constexpr bool kB = kGate == kGateBounded;
 #pragma unroll
-      for (int t = 0; t < kC; ++t)
-        gl[t] = f2{kda_gate2_from_raw<kB>(bf16_lo(in_g[t][0]) + dtb.x, a_rate,
+      for (int u = 0; u < kNG; ++u)
+        gl[u] = f2{kda_gate2_from_raw<kB>(bf16_lo(in_g[u][0]) + dtb.x, a_rate,
                                           lb2),
-                   kda_gate2_from_raw<kB>(bf16_hi(in_g[t][0]) + dtb.y, a_rate,
+                   kda_gate2_from_raw<kB>(bf16_hi(in_g[u][0]) + dtb.y, a_rate,
                                           lb2)};
     } else {
 #pragma unroll
-      for (int t = 0; t < kC; ++t)
-        gl[t] = f2{__uint_as_float(in_g[t][0]), __uint_as_float(in_g[t][1])} *
+      for (int u = 0; u < kNG; ++u)
+        gl[u] = f2{__uint_as_float(in_g[u][0]), __uint_as_float(in_g[u][1])} *
                 kLog2e;
     }
 #pragma unroll
-    for (int t = 0; t < kC; ++t) gl[t] = kda_decay_floor2(gl[t]);
+    for (int u = 0; u < kNG; ++u) gl[u] = kda_decay_floor2(gl[u]);
+    if (kShareDecays) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sm.gtok[4 * pw + u][lane] = gl[u];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0)
+        __hip_atomic_store(&sm.gseq[pw], ci, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     const float bt =
         lane < 4 ? (kRaw ? sigmoid_(bf16_lo(in_b)) : __uint_as_float(in_b))
                  : 0.0f;
-    // cumulative decay of keys 2 lane, 2 lane + 1 (log2 units) over the
-    // whole chunk; the values at this wave's 4 tokens and at the end
-    f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-    f2 G = {0.f, 0.f};
-    float gmax = 0.0f;
-    {
-      // in groups of the 4 tokens a wave owns: the wave keeps its own
-      // group's prefixes under a wave-uniform branch (no per-token select)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        f2 Gt[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int t = 4 * grp + u;
-          if (kPlain || t < nv) G += gl[t];
-          gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
-          Gt[u] = G;
-        }
-        if (grp == pw) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) Gu[u] = Gt[u];
-        }
-      }
-    }
-    // NaN counts as unsafe; the same verdict in every prep wave
-    const bool unsafe = __any(!(gmax <= kSafeExp2));
     const float qscale = 0.08838834764831845f;  // D^-1/2
     // conv + SiLU of the 4 tokens (weights read once), then the 8 norm
     // reductions side by side, then the tables
@@ -649,6 +657,51 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
         }
       }
     }
+    // (kShareDecays) the other waves' decays, published before their conv,
+    // so normally there by now; then the cumulative decay G over the chunk,
+    // in token order: its values at this wave's tokens and at the end
+    if (kShareDecays) {
+      for (int it = 0; it < kGseqSpinMax; ++it) {
+        bool ready = true;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          ready = ready &&
+                  __hip_atomic_load(&sm.gseq[w], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP) == ci;
+        if (ready) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    f2 Gu[4] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+    f2 G = {0.f, 0.f};
+    float gmax = 0.0f;
+    {
+      // in groups of the 4 tokens a wave owns: the wave keeps its own
+      // group's prefixes under a wave-uniform branch (no per-token select)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        f2 Gt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = 4 * grp + u;
+          if (kPlain || t < nv) {
+            if constexpr (kShareDecays)
+              G += sm.gtok[t][lane];
+            else
+              G += gl[t];
+          }
+          gmax = fmaxf(gmax, fmaxf(fabsf(G.x), fabsf(G.y)));
+          Gt[u] = G;
+        }
+        if (grp == pw) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) Gu[u] = Gt[u];
+        }
+      }
+    }
+    // NaN counts as unsafe; the same verdict in every prep wave
+    const bool unsafe = __any(!(gmax <= kSafeExp2));
     // dword of keys 2 lane, 2 lane + 1 in a split row (hi; mid at + 4, lo
     // at + 8)
     const int m = lane & 15;
