@@ -209,7 +209,8 @@ kda_status kda_prefill(const kda_dims* dims, const int32_t* cu_seqlens,
 
 /*
  * The same prefill computed in chunks of 16 tokens on the matrix cores
- * (fp32 MFMA): per chunk the deltas solve a 16 x 16 unit lower-triangular
+ * (the fp32 products as three bf16 pieces per operand, accumulated in
+ * fp32): per chunk the deltas solve a 16 x 16 unit lower-triangular
  * system (I + diag(beta) A) Delta = diag(beta) (V - K~ S), with A the
  * decayed key Gram matrix of the chunk, K~ the keys scaled by their
  * cumulative decay and S the state before the chunk; outputs and the next
