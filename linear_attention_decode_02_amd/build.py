@@ -18,6 +18,9 @@ HIPCC_FLAGS = [
     "-ffp-contract=fast",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 3 kernel-argument dwords preloaded into scalar registers
+    # (the decode kernel's slot-index pointer and head count)
+    "-mllvm", "-amdgpu-kernarg-preload-count=3",
     "-Wall",
 ]
 

@@ -380,7 +380,12 @@ __device__ __forceinline__ void emit_output(const Lds& L, float eps, int col4,
 template <bool kNorm, bool kRawGates, bool kTileFirst>
 // At most 64 VGPRs, so that two 16-wave workgroups share a CU.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void kda_decode_kernel(Params p) {
+// state_idx and heads (equal to p.state_idx, p.heads) come first as
+// arguments of their own: the library is built to preload the first
+// argument dwords into scalar registers, so the slot index, on which every
+// state and conv access waits, is requested without first reading the
+// argument block from memory.
+void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   __shared__ Lds L;
 
   const int tid = threadIdx.x;
@@ -388,12 +393,12 @@ void kda_decode_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int unit = blockIdx.x;
-  const int H = p.heads;
+  const int H = heads;
   const int n = unit / H;
   const int h = unit - n * H;
   const int64_t C = static_cast<int64_t>(H) * kD;
 
-  const int32_t slot = p.state_idx[n];
+  const int32_t slot = state_idx[n];
   if (slot <= 0 || slot >= p.num_slots) {
     // Null padding row: zero output, no state traffic.  Block-uniform.
     if (tid < kD / 8) {
@@ -1033,10 +1038,10 @@ template <bool kNorm, bool kRaw>
 void launch_decode(bool first, dim3 grid, hipStream_t stream, const Params& p) {
   if (first)
     hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, true>), grid,
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), 0, stream, p.state_idx, p.heads, p);
   else
     hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, false>), grid,
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), 0, stream, p.state_idx, p.heads, p);
 }
 
 template <bool kRaw>
