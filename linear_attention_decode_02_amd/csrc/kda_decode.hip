@@ -394,7 +394,13 @@ void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   const int lane = tid & 63;
   const int unit = blockIdx.x;
   const int H = heads;
-  const int n = unit / H;
+  // unit / H on the scalar unit: every supported head count (12, 24, 48,
+  // 96; others are rejected before launch) is 3 * 2^k, and for any 32-bit
+  // x, x / 3 = (x * 0xAAAAAAAB) >> 33
+  const uint32_t x3 = static_cast<uint32_t>(unit) >> __builtin_ctz(H);
+  const int n = static_cast<int>(__builtin_amdgcn_readfirstlane(
+                    static_cast<uint32_t>(
+                        (static_cast<uint64_t>(x3) * 0xAAAAAAABull) >> 33)));
   const int h = unit - n * H;
   const int64_t C = static_cast<int64_t>(H) * kD;
 
