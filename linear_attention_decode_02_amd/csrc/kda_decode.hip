@@ -377,14 +377,14 @@ __device__ __forceinline__ void emit_output(const Lds& L, float eps, int col4,
 // when some compute units hold two units, slower otherwise; the launcher
 // chooses).  Other variants (conv-state layout and update, q/k L2 norm,
 // SiLU gate, bounded gate, conv bias) are block-uniform runtime flags.
-template <bool kNorm, bool kRawGates, bool kTileFirst>
-// At most 64 VGPRs, so that two 16-wave workgroups share a CU.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 // state_idx and heads (equal to p.state_idx, p.heads) come first as
 // arguments of their own: the library is built to preload the first
 // argument dwords into scalar registers, so the slot index, on which every
 // state and conv access waits, is requested without first reading the
 // argument block from memory.
+template <bool kNorm, bool kRawGates, bool kTileFirst>
+// At most 64 VGPRs, so that two 16-wave workgroups share a CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   __shared__ Lds L;
 
@@ -486,8 +486,7 @@ void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   }
   // Output gate and norm weight of columns 4 lane .. +3, by lanes 0..31 of
   // wave 4 (idle in the conv): activated and put in LDS before the first
-  // barrier, so the readout at the end waits for no load.  (Fetched there,
-  // behind the state stores, it would also wait for their completion.)
+  // barrier, so the readout at the end depends on no memory access.
   const bool gate_lanes = kNorm && wave == 4 && lane < 32;
   u2 gb = {0u, 0u};
   f4 nw = {0.f, 0.f, 0.f, 0.f};
