@@ -372,21 +372,33 @@ __device__ __forceinline__ void emit_output(const Lds& L, float eps, int col4,
   *reinterpret_cast<gptr<u2>>(out4) = ob;
 }
 
+// Request order of the single-token kernel, chosen by the launcher from the
+// units per compute unit (see load_mode):
+//   kLoadLean      the small inputs, then the state tile; only the waves
+//                  that use a small input load it (calls up to one unit per
+//                  compute unit, and large ones up to 32 per compute unit);
+//   kLoadTileFirst the state tile, then the small inputs (some compute units
+//                  hold two units);
+//   kLoadAllWaves  the small inputs, then the tile, every wave loading the
+//                  conv and decay inputs (larger calls, where that stream
+//                  order keeps HBM busier).
+enum LoadMode { kLoadLean = 0, kLoadTileFirst = 1, kLoadAllWaves = 2 };
+
 // kNorm: gated RMSNorm epilogue; kRawGates: g and beta from raw inputs;
-// kTileFirst: the state tile is requested before the small inputs (faster
-// when some compute units hold two units, slower otherwise; the launcher
-// chooses).  Other variants (conv-state layout and update, q/k L2 norm,
-// SiLU gate, bounded gate, conv bias) are block-uniform runtime flags.
+// kMode: a LoadMode.  Other variants (conv-state layout and update, q/k L2
+// norm, SiLU gate, bounded gate, conv bias) are block-uniform runtime flags.
 // state_idx and heads (equal to p.state_idx, p.heads) come first as
 // arguments of their own: the library is built to preload the first
 // argument dwords into scalar registers, so the slot index, on which every
 // state and conv access waits, is requested without first reading the
 // argument block from memory.
-template <bool kNorm, bool kRawGates, bool kTileFirst>
+template <bool kNorm, bool kRawGates, int kMode>
 // At most 64 VGPRs, so that two 16-wave workgroups share a CU.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   __shared__ Lds L;
+  constexpr bool kTileFirst = kMode == kLoadTileFirst;
+  constexpr bool kAllWaves = kMode == kLoadAllWaves;
 
   const int tid = threadIdx.x;
   // scalar: the branches on the wave below are uniform and cost no masks
@@ -431,9 +443,11 @@ void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
 
   // ---- small loads (they retire before the state loads unless kTileFirst)
   // Waves 0..2 run the conv of part `wave` (q, k, v) on channels i0, i0+1;
-  // wave 3 computes exp(g) for key rows i0, i0+1.  Only those waves issue
-  // these loads (wave-uniform branches): the other waves' state loads then
-  // queue behind no redundant requests in the compute unit's address path.
+  // wave 3 computes exp(g) for key rows i0, i0+1.  Unless kAllWaves, only
+  // those waves issue these loads (wave-uniform branches), so the other
+  // waves' state loads queue behind no redundant requests in the compute
+  // unit's address path; with kAllWaves waves 3+ re-read part 2's conv
+  // inputs (cache hits) and every wave reads its decays.
   const uint32_t flags = p.flags;
   const bool tap_major = (flags & KDA_CONV_TAP_MAJOR) != 0;
   const int i0 = 2 * lane;
@@ -442,8 +456,8 @@ void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   uint32_t x2 = 0u, cw0 = 0u, cw1 = 0u, cw2 = 0u;
   f2 w_t[kW] = {};
   f2 bias2 = {0.f, 0.f};
-  if (wave < 3) {
-    const int part = wave;
+  if (kAllWaves || wave < 3) {
+    const int part = wave < 3 ? wave : 2;
     const int64_t c = part * C + h * kD + i0;
     // conv state words of channels c, c+1 (see unpack_window)
     cs_base = reinterpret_cast<uint32_t*>(
@@ -462,7 +476,7 @@ void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   f2 g2 = {0.f, 0.f};
   float beta;
   if (kRawGates) {
-    if (wave == 3) {
+    if (kAllWaves || wave == 3) {
       const uint32_t rg = *reinterpret_cast<const uint32_t*>(
           p.raw_g + (static_cast<int64_t>(n) * H + h) * kD + i0);
       const f2 db = *reinterpret_cast<const f2*>(p.dt_bias + h * kD + i0);
@@ -479,7 +493,7 @@ void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
     const uint32_t rb = p.raw_beta[static_cast<int64_t>(n) * H + h];
     beta = sigmoidf_(bf16_lo(rb));
   } else {
-    if (wave == 3)
+    if (kAllWaves || wave == 3)
       g2 = *reinterpret_cast<const f2*>(
           p.g + (static_cast<int64_t>(n) * H + h) * kD + i0);
     beta = p.beta[static_cast<int64_t>(n) * H + h];
@@ -502,11 +516,10 @@ void kda_decode_kernel(const int32_t* state_idx, int32_t heads, Params p) {
   if (!kTileFirst) issue_tile();
 
   // ---- conv update + SiLU, decay factors (waves 0..3) ---------------------
-  // Waves 4..15 skip this, except in the tile-first variant, where their
-  // discarded copy of the conv math measured faster (288 units, 12 heads:
-  // 9.0 against 9.5 us; skipping it saves 16 % of the vector instructions
-  // and 0.3 us at one row, where the small-loads-first variant runs).
-  if (kTileFirst || wave < 4) {
+  // In kLoadLean waves 4..15 skip this (16 % of the vector instructions,
+  // 0.3 us at one row); in the other modes they run a discarded copy, which
+  // measured faster there (288 units, 12 heads: 9.0 against 9.5 us).
+  if (kMode != kLoadLean || wave < 4) {
     float y0, y1;
     token_inputs(flags, wave, cw0, cw1, cw2, x2, w_t, bias2,
                  p.conv_bias != nullptr, g2, y0, y1);
@@ -1029,23 +1042,35 @@ KdaChunkedArgs chunked_args(const kda_dims* d, const int32_t* cu_seqlens,
   return a;
 }
 
-// Request order of the single-token kernel: the state tile first when some
-// compute units hold a second unit (CUs < units <= 2 CUs).  Graph-replay
-// latency on MI355X, us per call, tile first / small loads first: 288
-// units 8.9 / 9.7, 384 units 10.8-11.3 / 11.4-11.9; but 12 units 4.0 /
-// 3.95, 192 units 6.3 / 6.0, 768 units 21.3 / 20.8.
-bool tile_first(int64_t units, int dev) {
+// Load mode of the single-token kernel from the units per compute unit.
+// Measured on MI355X (us per call; graph replay for small calls):
+//   * tile first when some compute units hold a second unit (CUs < units
+//     <= 2 CUs): 288 units 8.9 against 9.7 (lean), 384 units 10.8-11.3
+//     against 11.4-11.9; but 12 units 4.0 against 3.95, 192 units 6.3
+//     against 6.0, 768 units 21.3 against 20.8;
+//   * every wave loading the small inputs from 32 units per compute unit:
+//     49,152 units (96 heads, norm off) 1027 against 1072 (lean), 12,288
+//     units (48 heads) 265 against 270; lean is faster up to ~24 units per
+//     compute unit (3,072 units 72.3 against 73.3, 6,144 units 140.6
+//     against 141.6).
+constexpr int64_t kAllWavesMinUnitsPerCU = 32;
+int load_mode(int64_t units, int dev) {
   const int64_t cus = cu_count(dev);
-  return units > cus && units <= 2 * cus;
+  if (units > cus && units <= 2 * cus) return kLoadTileFirst;
+  if (units >= kAllWavesMinUnitsPerCU * cus) return kLoadAllWaves;
+  return kLoadLean;
 }
 
 template <bool kNorm, bool kRaw>
-void launch_decode(bool first, dim3 grid, hipStream_t stream, const Params& p) {
-  if (first)
-    hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, true>), grid,
+void launch_decode(int mode, dim3 grid, hipStream_t stream, const Params& p) {
+  if (mode == kLoadTileFirst)
+    hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, kLoadTileFirst>), grid,
+                       dim3(kThreads), 0, stream, p.state_idx, p.heads, p);
+  else if (mode == kLoadAllWaves)
+    hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, kLoadAllWaves>), grid,
                        dim3(kThreads), 0, stream, p.state_idx, p.heads, p);
   else
-    hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, false>), grid,
+    hipLaunchKernelGGL((kda_decode_kernel<kNorm, kRaw, kLoadLean>), grid,
                        dim3(kThreads), 0, stream, p.state_idx, p.heads, p);
 }
 
@@ -1057,11 +1082,11 @@ kda_status launch(const kda_dims* d, const Params& p, void* hip_stream) {
   const int64_t units = static_cast<int64_t>(d->batch) * d->num_heads;
   const dim3 grid(static_cast<unsigned>(units));
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const bool first = tile_first(units, dev);
+  const int mode = load_mode(units, dev);
   if (d->flags & KDA_OUTPUT_NORM)
-    launch_decode<true, kRaw>(first, grid, stream, p);
+    launch_decode<true, kRaw>(mode, grid, stream, p);
   else
-    launch_decode<false, kRaw>(first, grid, stream, p);
+    launch_decode<false, kRaw>(mode, grid, stream, p);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
