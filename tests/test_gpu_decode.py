@@ -92,13 +92,15 @@ def test_shape_grid_with_null_and_invalid_slots(H, B):
 
 
 @pytest.mark.parametrize("H,B", [(12, 21), (12, 22), (12, 42), (12, 43),
-                                 (48, 5), (48, 6), (48, 10), (48, 11)])
+                                 (48, 5), (48, 6), (48, 10), (48, 11),
+                                 (48, 170), (48, 171)])
 @pytest.mark.parametrize("norm", [True, False])
 def test_request_order_switch(H, B, norm):
-    """Unit counts on both sides of the two switches of the single-token
-    kernel's request order on a 256-CU part (tile first for 257 .. 512
-    units): 252 / 264, 504 / 516 units at 12 heads and 240 / 288, 480 / 528
-    at 48, with a null row and an out-of-range slot in each."""
+    """Unit counts on both sides of the three switches of the single-token
+    kernel's load mode on a 256-CU part (tile first for 257 .. 512 units,
+    every wave loading the small inputs from 8192): 252 / 264, 504 / 516
+    units at 12 heads and 240 / 288, 480 / 528, 8160 / 8208 at 48, with a
+    null row and an out-of-range slot in each."""
     w = synth.small(f"order_h{H}_b{B}", batch=B, heads=H, num_slots=B + 3,
                     seed=300 + H + B, null_every=4, norm=norm)
     inp = synth.make_inputs(w)

@@ -123,6 +123,14 @@ def test_variant_parity(name, H, B):
     print(f"[variant] {name}: {st}", flush=True)
 
 
+@pytest.mark.parametrize("name", ["raw_gates", "raw_bounded_l2_tap_nonorm"])
+def test_variant_parity_all_wave_loads(name):
+    """Raw gates at 48 x 176 = 8448 units, past the size (32 units per
+    compute unit of a 256-CU part) from which every wave of the
+    single-token kernel issues the small loads."""
+    test_variant_parity(name, 48, 176)
+
+
 def test_raw_gate_l2norm_chain_is_contractive():
     """Eight chained calls in the L2-normalised, raw-gate configuration
     (unit keys, beta < 1: the update never amplifies the state), compared
