@@ -550,8 +550,20 @@ def bench_prefill(args, np, torch, kda, synth):
             rg["dt_bias"], t["gate"], t["norm_w"], t["state_idx"], out,
             eps=w.eps, variants=flags, stream=stream)
 
+    # the same sequences shortest first (the longest last in the batch):
+    # the launch order a caller's batch may come in
+    cu_asc = torch.from_numpy(np.concatenate(
+        [[0], np.cumsum(np.sort(lens))]).astype(np.int32)).to(dev)
+
+    def ascending():
+        kda.kda_prefill(cu_asc, t["qkv"], t["conv_w"], t["conv_state"],
+                        t["rec_state"], t["g"], t["beta"], t["gate"],
+                        t["norm_w"], t["state_idx"], out, eps=w.eps,
+                        variants=flags, chunked=True, stream=stream)
+
     kern_two = event_time(two_pass, max(K // 2, 1))
     kern_raw = event_time(raw_gates, max(K // 2, 1))
+    kern_asc = event_time(ascending, max(K // 2, 1))
     updates = total * H
     # matrix-core work of the chunked form per (16-token chunk, head): K~S,
     # Q~S and the state update (3 x 2*16*128*128), the A and B products and
@@ -633,6 +645,7 @@ def bench_prefill(args, np, torch, kda, synth):
                   "speedup_vs_sequential": round(kern_seq / kern, 2),
                   "two_pass_us": round(kern_two * 1e6, 2),
                   "raw_gates_us": round(kern_raw * 1e6, 2),
+                  "ascending_order_us": round(kern_asc * 1e6, 2),
                   "chunk_metadata_us": round(meta_us, 2)},
     }
     print(json.dumps(line), flush=True)

@@ -362,7 +362,36 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
       o32[((g.tb + t) * C + col0) / 2 + idx % (kD / 2)] = 0u;
     }
   };
-  const Seg seg = seg_at(static_cast<int>(blockIdx.x));
+  // Longest sequences first.  A workgroup takes a whole compute unit (LDS),
+  // so the workgroups of a large batch run in rounds, in index order, and a
+  // long sequence late in the batch would start its chunk chain only after
+  // others end.  With cu_seqlens and at most kThreads sequences, workgroup
+  // b takes head b % H of the (b / H)-th sequence by descending length
+  // (ties by index): the rank of each sequence is counted over the lengths
+  // staged in sm.o, which no wave uses before the second barrier below.
+  int sg = static_cast<int>(blockIdx.x);
+  const int nseq = static_cast<int>(gridDim.x) / H;
+  if (p.cu_seqlens != nullptr && nseq > 1 && nseq <= kThreads) {
+    __shared__ int picked;
+    int* lens = reinterpret_cast<int*>(&sm.o[0][0]);
+    const int want = sg / H;
+    if (tid < nseq)
+      lens[tid] = max(p.cu_seqlens[tid + 1] - p.cu_seqlens[tid], 0);
+    if (tid == 0) picked = want;
+    __syncthreads();
+    if (tid < nseq) {
+      const int mine = lens[tid];
+      int rank = 0;
+      for (int j = 0; j < nseq; ++j) {
+        const int other = lens[j];
+        rank += (other > mine || (other == mine && j < tid)) ? 1 : 0;
+      }
+      if (rank == want) picked = tid;
+    }
+    __syncthreads();
+    sg = picked * H + (sg - want * H);
+  }
+  const Seg seg = seg_at(sg);
   if (seg.len == 0) return;
   if (!live(seg)) {
     zero_outputs(seg, tid, kThreads);

@@ -163,6 +163,44 @@ def test_chunked_matches_sequential_kernel():
     assert d <= 1e-4
 
 
+def permute_batch(inp, cu, perm):
+    """The same sequences in the order ``perm`` (new sequence i is old
+    sequence perm[i], with its tokens and its slot)."""
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in perm]
+                          ).astype(np.int64)
+    out = dict(inp, state_idx=inp["state_idx"][perm].copy())
+    for k in ("qkv", "g", "beta", "gate"):
+        out[k] = np.ascontiguousarray(inp[k][rows])
+    lens = np.diff(cu)[perm]
+    return out, np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), rows
+
+
+@pytest.mark.parametrize("lens,H", [
+    ([5, 40, 0, 17, 40, 1, 33, 16, 2, 70], 24),
+    (list(np.random.default_rng(41).integers(0, 24, 600)), 12),
+])
+def test_fused_result_independent_of_batch_order(lens, H):
+    """The fused kernel takes the sequences longest first (up to 512
+    sequences; beyond that in index order): each (sequence, head) is still
+    computed alone by one workgroup, so reversing the batch gives every
+    sequence bit-identical outputs and states.  The 600-sequence case runs
+    the index order and is also checked against the oracle."""
+    w, inp, cu = prefill_case(230 + H, lens, H, S=len(lens) + 2,
+                              null=(2,))
+    a = run_prefill(w, inp, cu, chunked=True)
+    if len(lens) > 512:
+        ref = O.prefill(inp, cu, heads=H, norm=w.norm, eps=w.eps)
+        print(f"[order] 600 sequences {check_prefill(w, inp, cu, a, ref)}",
+              flush=True)
+    perm = np.arange(len(lens))[::-1].copy()
+    pin, pcu, rows = permute_batch(inp, cu, perm)
+    b = run_prefill(w, pin, pcu, chunked=True)
+    assert np.array_equal(a["rec_state"].view(np.uint32),
+                          b["rec_state"].view(np.uint32))
+    assert np.array_equal(a["conv_state"], b["conv_state"])
+    assert np.array_equal(a["out"][rows], b["out"])
+
+
 def test_two_pass_matches_fused():
     """The two chunked paths compute the same chunk form: they agree far
     inside the oracle bars."""
