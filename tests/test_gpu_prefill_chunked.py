@@ -179,22 +179,23 @@ def permute_batch(inp, cu, perm):
     ([5, 40, 0, 17, 40, 1, 33, 16, 2, 70], 24),
     (list(np.random.default_rng(41).integers(0, 24, 600)), 12),
 ])
-def test_fused_result_independent_of_batch_order(lens, H):
+def test_result_independent_of_batch_order(lens, H, path):
     """The fused kernel takes the sequences longest first (up to 512
-    sequences; beyond that in index order): each (sequence, head) is still
-    computed alone by one workgroup, so reversing the batch gives every
-    sequence bit-identical outputs and states.  The 600-sequence case runs
-    the index order and is also checked against the oracle."""
+    sequences; beyond that in index order), the two-pass state pass in
+    index order: each (sequence, head) is still computed alone, so
+    reversing the batch gives every sequence bit-identical outputs and
+    states on both paths.  The 600-sequence case runs the fused kernel's
+    index order and is also checked against the oracle."""
     w, inp, cu = prefill_case(230 + H, lens, H, S=len(lens) + 2,
                               null=(2,))
-    a = run_prefill(w, inp, cu, chunked=True)
+    a = run_path(path, w, inp, cu)
     if len(lens) > 512:
         ref = O.prefill(inp, cu, heads=H, norm=w.norm, eps=w.eps)
         print(f"[order] 600 sequences {check_prefill(w, inp, cu, a, ref)}",
               flush=True)
     perm = np.arange(len(lens))[::-1].copy()
     pin, pcu, rows = permute_batch(inp, cu, perm)
-    b = run_prefill(w, pin, pcu, chunked=True)
+    b = run_path(path, w, pin, pcu)
     assert np.array_equal(a["rec_state"].view(np.uint32),
                           b["rec_state"].view(np.uint32))
     assert np.array_equal(a["conv_state"], b["conv_state"])
