@@ -550,7 +550,8 @@ def bench_prefill(args, np, torch, kda, synth):
             rg["dt_bias"], t["gate"], t["norm_w"], t["state_idx"], out,
             eps=w.eps, variants=flags, stream=stream)
 
-    # the same sequences shortest first (the longest last in the batch):
+    # the same lengths shortest first (the longest last in the batch; the
+    # token rows are reused in place, so each sequence reads other rows):
     # the launch order a caller's batch may come in
     cu_asc = torch.from_numpy(np.concatenate(
         [[0], np.cumsum(np.sort(lens))]).astype(np.int32)).to(dev)
