@@ -375,8 +375,12 @@ __global__ __launch_bounds__(kThreads) void kda_chunked_prefill_kernel(
     __shared__ int picked;
     int* lens = reinterpret_cast<int*>(&sm.o[0][0]);
     const int want = sg / H;
-    if (tid < nseq)
-      lens[tid] = max(p.cu_seqlens[tid + 1] - p.cu_seqlens[tid], 0);
+    if (tid < nseq) {
+      // in 64 bits, as seg_at: any two int32 offsets, a decreasing pair 0
+      const int64_t d = static_cast<int64_t>(p.cu_seqlens[tid + 1]) -
+                        p.cu_seqlens[tid];
+      lens[tid] = d > 0 ? static_cast<int>(d < INT32_MAX ? d : INT32_MAX) : 0;
+    }
     if (tid == 0) picked = want;
     __syncthreads();
     if (tid < nseq) {
